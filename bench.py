@@ -1,0 +1,211 @@
+"""Benchmark of the Veda block-sparse attention layer on one MI355X.
+
+One step = one attention layer through the whole hot path on one batch of
+resident synthetic input: permute Q, K (rows) and V (tile-transposed), score
+tiles (pool + projection + pair scores), select blocks, block-sparse
+attention, inverse permutation of O (plus, for the packed workload, the
+all-blocks forward for the dense LSE and the block heat).  Four seeded input
+sets rotate across steps, so each call sees a new block pattern.
+
+Prints one JSON line.  value = attention FLOP over computed blocks / layer
+time (TFLOP/s); ms_per_step = ms per layer; roofline = the attention kernel
+alone, timed with HIP events on the stream it runs on.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import veda_workloads as wl
+
+METRIC = "block-sparse attn TFLOP/s over computed blocks + ms/layer at 90% sparsity"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload index 1..5 (default: the 16:9 clip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="rough budget of the oracle sample")
+    ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "profiles", "traffic.json"))
+    return ap.parse_args()
+
+
+class Layer:
+    """Device buffers and the calls of one attention layer."""
+
+    def __init__(self, w, inputs, vb):
+        self.w, self.vb = w, vb
+        self.plan = vb.Plan.from_workload(w)
+        p = self.plan
+        dev = "cuda"
+        self.sets = [{k: t.to(dev) for k, t in inp.items()} for inp in inputs]
+        self.qp, self.kp, self.vt = p.empty_perm(), p.empty_perm(), p.empty_vt()
+        self.scores = torch.empty(p.info["total_pairs"], dtype=torch.float32, device=dev)
+        self.ws = p.empty_workspace()
+        self.row_ptr = torch.empty(p.T + 1, dtype=torch.int32, device=dev)
+        self.col = torch.empty(p.info["nnz"], dtype=torch.int32, device=dev)
+        self.o = p.empty_perm()
+        self.lse = torch.empty(p.R, dtype=torch.float32, device=dev)
+        self.o_nat = torch.empty((w.num_tokens, w.num_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+        self.dense = None
+        if w.with_heat:
+            self.dense = vb.Plan.from_workload(w, budget_mode=wl.ALL_BLOCKS)
+            self.d_row_ptr = torch.empty(p.T + 1, dtype=torch.int32, device=dev)
+            self.d_col = torch.empty(self.dense.info["nnz"], dtype=torch.int32, device=dev)
+            self.d_o = p.empty_perm()
+            self.d_lse = torch.empty(p.R, dtype=torch.float32, device=dev)
+            self.heat = torch.empty(p.info["total_pairs"], dtype=torch.float32, device=dev)
+        self.attn_events = []
+
+    def step(self, s, time_attn=False):
+        vb, p, w = self.vb, self.plan, self.w
+        x = self.sets[s % len(self.sets)]
+        p.permute(x["q"], self.qp, vb.VEDA_PERMUTE_FORWARD)
+        p.permute(x["k"], self.kp, vb.VEDA_PERMUTE_FORWARD)
+        p.permute(x["v"], self.vt, vb.VEDA_PERMUTE_FORWARD_TRANSPOSED)
+        p.score(self.qp, self.kp, x["w_q"], x["w_k"], self.scores, self.ws)
+        p.select(self.scores, self.row_ptr, self.col)
+        if time_attn:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        p.attention(self.qp, self.kp, self.vt, self.row_ptr, self.col, w.softmax_scale, self.o, self.lse)
+        if time_attn:
+            e1.record()
+            self.attn_events.append((e0, e1))
+        p.permute(self.o, self.o_nat, vb.VEDA_PERMUTE_INVERSE)
+        if self.dense is not None:
+            d = self.dense
+            d.select(self.scores, self.d_row_ptr, self.d_col)
+            d.attention(self.qp, self.kp, self.vt, self.d_row_ptr, self.d_col, w.softmax_scale, self.d_o,
+                        self.d_lse)
+            d.heat(self.qp, self.kp, self.d_lse, w.softmax_scale, self.heat)
+
+
+def cpu_baseline(w, inp, budget_s):
+    """The oracle on a bounded sample: the whole path for the first heads of
+    the same workload, timed on the host; reported in the metric's unit."""
+    from oracle import veda_oracle as vo
+    threads = torch.get_num_threads()
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max(blas) if blas else threads
+    except Exception:
+        pass
+    heads_done, flops, elapsed = 0, 0.0, 0.0
+    per_block = 4.0 * 128 * 128 * w.head_dim
+    qn = inp["q"].to(torch.float64).numpy()
+    kn = inp["k"].to(torch.float64).numpy()
+    vn = inp["v"].to(torch.float64).numpy()
+    for h in range(w.num_heads):
+        sub = vo.Plan(w.segments, 1, w.head_dim, [w.tile_shapes[h]], w.budget_mode, w.keep_num, w.keep_den,
+                      w.fixed_k)
+        t0 = time.perf_counter()
+        res = vo.run_path(sub, qn[:, h:h + 1], kn[:, h:h + 1], vn[:, h:h + 1], inp["w_q"].numpy()[h:h + 1],
+                          inp["w_k"].numpy()[h:h + 1], w.softmax_scale)
+        vo.permute_inverse(sub, np.nan_to_num(res["o_perm"]))
+        elapsed += time.perf_counter() - t0
+        flops += per_block * sum(len(r) for r in res["selection"][0])
+        heads_done += 1
+        if elapsed >= budget_s:
+            break
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "whole path (permute, pool, project, score, select, attention, unpermute) of heads "
+                      "0..%d of %d, %.1f s on the host, fp64 numpy" % (heads_done - 1, w.num_heads, elapsed),
+            "ms_per_layer_extrapolated": 1e3 * elapsed * w.num_heads / heads_done,
+            "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the Veda path shards by heads with no exchange, and multi-GPU "
+              "runs are not part of this build (got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    from block_sparse_attention_10_amd import binding as vb
+    ok, why = vb.veda_available(0)
+    if not ok:
+        print("libveda unavailable: " + why, file=sys.stderr)
+        sys.exit(1)
+    w = wl.workload(args.config)
+    print("bench: generating inputs for %s" % w.describe(), file=sys.stderr, flush=True)
+    inputs = [wl.make_inputs(w, seed=s) for s in wl.rotation_seeds(w)]
+    layer = Layer(w, inputs, vb)
+    p = layer.plan
+    nnz = p.info["nnz"]
+    flops_attn = 4.0 * 128 * 128 * w.head_dim * nnz
+    print("bench: warmup %d, steps %d, nnz %d" % (args.warmup, args.steps, nnz), file=sys.stderr, flush=True)
+    for s in range(args.warmup):
+        layer.step(s)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s in range(args.steps):
+        layer.step(args.warmup + s, time_attn=True)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in layer.attn_events]
+    attn_avg = float(np.mean(attn_ms))
+    attn_tflops = flops_attn / (attn_avg * 1e-3) / 1e12
+    value = flops_attn / (ms_step * 1e-3) / 1e12
+    traffic = None
+    try:
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        key = "attn_fwd_config%d" % args.config
+        if key in tj and tj[key].get("kernel_source_sha") == _kernel_sha():
+            traffic = tj[key]["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, 4 rotating input sets)",
+        "config": {"workload": "config %d %s" % (args.config, w.describe()), "tokens": w.num_tokens,
+                   "heads": w.num_heads, "head_dim": w.head_dim, "nnz_blocks": nnz,
+                   "block_density": round(nnz / p.info["total_pairs"], 4), "parallelism": "single GPU"},
+        "attn_kernel_ms": round(attn_avg, 4), "attn_kernel_tflops": round(attn_tflops, 2),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: oracle CPU baseline (~%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, inputs[0], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def _kernel_sha():
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_sparse_attention_10_amd", "csrc",
+                        "veda_kernels.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

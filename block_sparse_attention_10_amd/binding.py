@@ -1,0 +1,376 @@
+"""Thin ctypes binding of libveda (include/veda.h), same names as the C ABI.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Torch tensors provide device memory and the current stream; sizes
+and dtypes are checked against the plan before a pointer crosses the ABI, so a
+wrong tensor raises here instead of reaching a kernel.  There is no fallback:
+if libveda.so is missing or the device is not gfx950, calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libveda.so")
+
+VEDA_OK = 0
+VEDA_SEG_VIDEO3D = 0
+VEDA_SEG_DENSE1D = 1
+VEDA_BUDGET_KEEP_RATIO = 0
+VEDA_BUDGET_FIXED_K = 1
+VEDA_BUDGET_ALL = 2
+VEDA_PERMUTE_FORWARD = 0
+VEDA_PERMUTE_INVERSE = 1
+VEDA_PERMUTE_FORWARD_TRANSPOSED = 2
+
+STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "SHAPE", 3: "UNSUPPORTED", 4: "WORKSPACE",
+                5: "LAUNCH", 6: "STATE"}
+
+
+class VedaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("veda %s (%d): %s" % (STATUS_NAMES.get(status, "?"), status, message))
+        self.status = status
+
+
+class Segment(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("t", ctypes.c_int32), ("h", ctypes.c_int32),
+                ("w", ctypes.c_int32), ("token_offset", ctypes.c_int64)]
+
+
+class PlanDesc(ctypes.Structure):
+    _fields_ = [("num_segments", ctypes.c_int32), ("segments", ctypes.POINTER(Segment)),
+                ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("tile_shape", ctypes.POINTER(ctypes.c_int32)), ("budget_mode", ctypes.c_int32),
+                ("keep_num", ctypes.c_int32), ("keep_den", ctypes.c_int32), ("fixed_k", ctypes.c_int32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int64), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("num_segments", ctypes.c_int32),
+                ("num_shapes", ctypes.c_int32), ("total_rows", ctypes.c_int64),
+                ("total_tiles", ctypes.c_int64), ("total_pairs", ctypes.c_int64),
+                ("nnz", ctypes.c_int64), ("max_row_blocks", ctypes.c_int64),
+                ("device_table_bytes", ctypes.c_int64), ("score_workspace_bytes", ctypes.c_int64),
+                ("max_tiles_per_head", ctypes.c_int32), ("uploaded", ctypes.c_int32)]
+
+
+# name -> (restype, argtypes)
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SIGS = {
+    "veda_abi_version": (ctypes.c_int, []),
+    "veda_available": (_I32, [ctypes.c_int, ctypes.c_char_p, ctypes.c_size_t]),
+    "veda_last_error": (ctypes.c_char_p, []),
+    "veda_plan_create": (_I32, [ctypes.POINTER(PlanDesc), ctypes.POINTER(_P)]),
+    "veda_plan_destroy": (None, [_P]),
+    "veda_plan_query": (_I32, [_P, ctypes.POINTER(PlanInfo)]),
+    "veda_plan_head": (_I32, [_P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I64),
+                              ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "veda_plan_copy_perm": (_I32, [_P, _I32, _P, _I64]),
+    "veda_plan_copy_valid": (_I32, [_P, _I32, _P, _I64]),
+    "veda_plan_copy_budgets": (_I32, [_P, _I32, _P, _I64]),
+    "veda_plan_copy_row_ptr": (_I32, [_P, _P, _I64]),
+    "veda_plan_upload": (_I32, [_P, _P, ctypes.c_size_t, _P]),
+    "veda_permute_tiles": (_I32, [_P, _P, _P, _I32, _P]),
+    "veda_score_tiles": (_I32, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "veda_select_blocks": (_I32, [_P, _P, _P, _P, _P, _P]),
+    "veda_block_sparse_attn_fwd": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P]),
+    "veda_block_heat": (_I32, [_P, _P, _P, _P, ctypes.c_float, _P, _P]),
+}
+EXPORTED = tuple(_SIGS)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libveda.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libveda.so is not built (%s); run "
+                              "python -m block_sparse_attention_10_amd.build" % LIB_PATH)
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != VEDA_OK:
+        raise VedaError(status, lib().veda_last_error().decode())
+
+
+# ---------------------------------------------------------------------------
+# direct wrappers (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def veda_abi_version() -> int:
+    return lib().veda_abi_version()
+
+
+def veda_available(device: int = 0) -> Tuple[bool, str]:
+    buf = ctypes.create_string_buffer(256)
+    st = lib().veda_available(device, buf, 256)
+    return st == VEDA_OK, buf.value.decode()
+
+
+def veda_last_error() -> str:
+    return lib().veda_last_error().decode()
+
+
+def veda_plan_create(segments: Sequence, num_heads: int, head_dim: int,
+                     tile_shapes: Sequence[Tuple[int, int, int]], budget_mode: int,
+                     keep_num: int = 1, keep_den: int = 10, fixed_k: int = 0) -> int:
+    """segments: objects with .kind, .grid (t, h, w) and .offset, or tuples
+    (kind, (t, h, w), offset).  Returns the plan handle."""
+    segs = (Segment * len(segments))()
+    for i, s in enumerate(segments):
+        kind, grid, off = (s.kind, s.grid, s.offset) if hasattr(s, "kind") else s
+        segs[i] = Segment(kind, grid[0], grid[1], grid[2], off)
+    shapes = (ctypes.c_int32 * (3 * len(tile_shapes)))(*[x for t in tile_shapes for x in t])
+    desc = PlanDesc(len(segments), segs, num_heads, head_dim, shapes, budget_mode,
+                    keep_num, keep_den, fixed_k)
+    out = _P()
+    _check(lib().veda_plan_create(ctypes.byref(desc), ctypes.byref(out)))
+    return out.value
+
+
+def veda_plan_destroy(plan: int) -> None:
+    lib().veda_plan_destroy(plan)
+
+
+def veda_plan_query(plan: int) -> Dict[str, int]:
+    info = PlanInfo()
+    _check(lib().veda_plan_query(plan, ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in PlanInfo._fields_}
+
+
+def veda_plan_head(plan: int, head: int) -> Tuple[int, int, int, int]:
+    n, r, t, p = _I32(), _I64(), _I64(), _I64()
+    _check(lib().veda_plan_head(plan, head, ctypes.byref(n), ctypes.byref(r), ctypes.byref(t),
+                                ctypes.byref(p)))
+    return n.value, r.value, t.value, p.value
+
+
+def _copy(fn, plan, n, *head):
+    out = np.zeros(n, dtype=np.int32)
+    _check(fn(plan, *head, out.ctypes.data, n))
+    return out
+
+
+def veda_plan_copy_perm(plan: int, head: int) -> np.ndarray:
+    n = veda_plan_head(plan, head)[0]
+    return _copy(lib().veda_plan_copy_perm, plan, 128 * n, head)
+
+
+def veda_plan_copy_valid(plan: int, head: int) -> np.ndarray:
+    n = veda_plan_head(plan, head)[0]
+    return _copy(lib().veda_plan_copy_valid, plan, n, head)
+
+
+def veda_plan_copy_budgets(plan: int, head: int) -> np.ndarray:
+    n = veda_plan_head(plan, head)[0]
+    S = veda_plan_query(plan)["num_segments"]
+    return _copy(lib().veda_plan_copy_budgets, plan, n * S, head).reshape(n, S)
+
+
+def veda_plan_copy_row_ptr(plan: int) -> np.ndarray:
+    T = veda_plan_query(plan)["total_tiles"]
+    out = np.zeros(T + 1, dtype=np.int32)
+    _check(lib().veda_plan_copy_row_ptr(plan, out.ctypes.data, T + 1))
+    return out
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def veda_plan_upload(plan: int, dev_tables, stream=None) -> None:
+    _check(lib().veda_plan_upload(plan, dev_tables.data_ptr(), dev_tables.numel() * dev_tables.element_size(),
+                                  _stream(stream)))
+
+
+def veda_permute_tiles(plan: int, src, dst, direction: int, stream=None) -> None:
+    _check(lib().veda_permute_tiles(plan, _ptr(src), _ptr(dst), direction, _stream(stream)))
+
+
+def veda_score_tiles(plan: int, q_perm, k_perm, w_q, w_k, scores, workspace, stream=None) -> None:
+    _check(lib().veda_score_tiles(plan, _ptr(q_perm), _ptr(k_perm), _ptr(w_q), _ptr(w_k), _ptr(scores),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)))
+
+
+def veda_select_blocks(plan: int, scores, row_ptr, col_idx, dense_mask=None, stream=None) -> None:
+    _check(lib().veda_select_blocks(plan, _ptr(scores), _ptr(row_ptr), _ptr(col_idx), _ptr(dense_mask),
+                                    _stream(stream)))
+
+
+def veda_block_sparse_attn_fwd(plan: int, q, k, v_t, row_ptr, col_idx, softmax_scale: float, o,
+                               lse=None, blocks_visited=None, stream=None) -> None:
+    _check(lib().veda_block_sparse_attn_fwd(plan, _ptr(q), _ptr(k), _ptr(v_t), _ptr(row_ptr), _ptr(col_idx),
+                                            float(softmax_scale), _ptr(o), _ptr(lse), _ptr(blocks_visited),
+                                            _stream(stream)))
+
+
+def veda_block_heat(plan: int, q, k, lse, softmax_scale: float, heat, stream=None) -> None:
+    _check(lib().veda_block_heat(plan, _ptr(q), _ptr(k), _ptr(lse), float(softmax_scale), _ptr(heat),
+                                 _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Plan: owns the handle and the device tables; checks tensor sizes
+# ---------------------------------------------------------------------------
+
+class Plan:
+    """A host plan plus its uploaded device tables on the current GPU."""
+
+    def __init__(self, segments, num_heads, head_dim, tile_shapes, budget_mode,
+                 keep_num=1, keep_den=10, fixed_k=0, upload=True):
+        self.handle = veda_plan_create(segments, num_heads, head_dim, tile_shapes, budget_mode,
+                                       keep_num, keep_den, fixed_k)
+        self.info = veda_plan_query(self.handle)
+        self.tables = None
+        if upload:
+            self.upload()
+
+    @classmethod
+    def from_workload(cls, w, budget_mode=None, upload=True):
+        mode = w.budget_mode if budget_mode is None else budget_mode
+        return cls(w.segments, w.num_heads, w.head_dim, w.tile_shapes, mode, w.keep_num, w.keep_den,
+                   w.fixed_k, upload=upload)
+
+    def upload(self):
+        import torch
+        self.tables = torch.empty(self.info["device_table_bytes"], dtype=torch.uint8, device="cuda")
+        veda_plan_upload(self.handle, self.tables)
+        self.info = veda_plan_query(self.handle)
+
+    def close(self):
+        if self.handle:
+            veda_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # sizes
+    @property
+    def N(self):
+        return self.info["num_tokens"]
+
+    @property
+    def H(self):
+        return self.info["num_heads"]
+
+    @property
+    def D(self):
+        return self.info["head_dim"]
+
+    @property
+    def R(self):
+        return self.info["total_rows"]
+
+    @property
+    def T(self):
+        return self.info["total_tiles"]
+
+    def _expect(self, t, shape, dtype, name):
+        import torch
+        if t is None:
+            raise ValueError("%s is None" % name)
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous CUDA tensor" % name)
+        if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+            raise ValueError("%s: expected %s %s, got %s %s" % (name, dtype, tuple(shape), t.dtype,
+                                                               tuple(t.shape)))
+
+    # calls
+    def permute(self, src, dst, direction, stream=None):
+        import torch
+        bf = torch.bfloat16
+        nat = (self.N, self.H, self.D)
+        if direction == VEDA_PERMUTE_INVERSE:
+            self._expect(src, (self.R, self.D), bf, "src")
+            self._expect(dst, nat, bf, "dst")
+        elif direction == VEDA_PERMUTE_FORWARD:
+            self._expect(src, nat, bf, "src")
+            self._expect(dst, (self.R, self.D), bf, "dst")
+        else:
+            self._expect(src, nat, bf, "src")
+            self._expect(dst, (self.T, self.D, 128), bf, "dst")
+        veda_permute_tiles(self.handle, src, dst, direction, stream)
+
+    def score(self, q_perm, k_perm, w_q, w_k, scores, workspace, stream=None):
+        import torch
+        self._expect(q_perm, (self.R, self.D), torch.bfloat16, "q_perm")
+        self._expect(k_perm, (self.R, self.D), torch.bfloat16, "k_perm")
+        self._expect(w_q, (self.H, self.D, 3 * self.D), torch.float32, "w_q")
+        self._expect(w_k, (self.H, self.D, 3 * self.D), torch.float32, "w_k")
+        self._expect(scores, (self.info["total_pairs"],), torch.float32, "scores")
+        veda_score_tiles(self.handle, q_perm, k_perm, w_q, w_k, scores, workspace, stream)
+
+    def select(self, scores, row_ptr, col_idx, dense_mask=None, stream=None):
+        import torch
+        self._expect(scores, (self.info["total_pairs"],), torch.float32, "scores")
+        self._expect(row_ptr, (self.T + 1,), torch.int32, "row_ptr")
+        self._expect(col_idx, (self.info["nnz"],), torch.int32, "col_idx")
+        if dense_mask is not None:
+            self._expect(dense_mask, (self.info["total_pairs"],), torch.uint8, "dense_mask")
+        veda_select_blocks(self.handle, scores, row_ptr, col_idx, dense_mask, stream)
+
+    def attention(self, q, k, v_t, row_ptr, col_idx, scale, o, lse=None, visited=None, stream=None,
+                  nnz=None):
+        import torch
+        bf = torch.bfloat16
+        self._expect(q, (self.R, self.D), bf, "q")
+        self._expect(k, (self.R, self.D), bf, "k")
+        self._expect(v_t, (self.T, self.D, 128), bf, "v_t")
+        self._expect(row_ptr, (self.T + 1,), torch.int32, "row_ptr")
+        if col_idx is None or col_idx.dtype != torch.int32 or not col_idx.is_cuda:
+            raise ValueError("col_idx must be an int32 CUDA tensor")
+        self._expect(o, (self.R, self.D), bf, "o")
+        if lse is not None:
+            self._expect(lse, (self.R,), torch.float32, "lse")
+        if visited is not None:
+            self._expect(visited, (1,), torch.int32, "blocks_visited")
+        veda_block_sparse_attn_fwd(self.handle, q, k, v_t, row_ptr, col_idx, scale, o, lse, visited, stream)
+
+    def heat(self, q, k, lse, scale, heat, stream=None):
+        import torch
+        self._expect(q, (self.R, self.D), torch.bfloat16, "q")
+        self._expect(k, (self.R, self.D), torch.bfloat16, "k")
+        self._expect(lse, (self.R,), torch.float32, "lse")
+        self._expect(heat, (self.info["total_pairs"],), torch.float32, "heat")
+        veda_block_heat(self.handle, q, k, lse, scale, heat, stream)
+
+    # allocation helpers (torch: device memory only)
+    def empty_perm(self):
+        import torch
+        return torch.empty((self.R, self.D), dtype=torch.bfloat16, device="cuda")
+
+    def empty_vt(self):
+        import torch
+        return torch.empty((self.T, self.D, 128), dtype=torch.bfloat16, device="cuda")
+
+    def empty_workspace(self):
+        import torch
+        return torch.empty(self.info["score_workspace_bytes"] // 4, dtype=torch.float32, device="cuda")

@@ -1,0 +1,70 @@
+// Internal declarations shared by the host side of libveda (plan, checks,
+// C ABI) and its HIP kernels.  Not installed, not part of the ABI.
+#pragma once
+
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+#include "veda.h"
+
+namespace veda {
+
+constexpr int kTile = 128;          // tokens per tile, rows per query tile
+constexpr int kMaxSegments = 8;
+constexpr int kMaxShapes = 2;       // at most two tile shapes per layer
+constexpr int kMaxTilesPerHead = 16384;
+constexpr int kMaxHeatTiles = 4096;
+
+// Device view of the tables of one distinct tile shape.  Heads that share a
+// shape share these tables (tiling, valid counts, budgets, local CSR offsets).
+struct DevShape {
+  const int32_t* perm;           // [n * 128] slot -> token, -1 = padding
+  const int32_t* valid;          // [n] valid tokens per tile
+  const int32_t* tile_seg;       // [n] segment of each tile
+  const int32_t* budget;         // [n * S] blocks kept per key segment
+  const int32_t* local_row_ptr;  // [n + 1] CSR offsets inside one head
+  int32_t num_tiles;
+  int32_t seg_first[kMaxSegments];
+  int32_t seg_count[kMaxSegments];
+};
+
+// Device view of a whole plan, passed to kernels by value.
+struct DevPlan {
+  int32_t num_heads, head_dim, num_segments, num_shapes;
+  int64_t num_tokens, total_rows, total_tiles, total_pairs, nnz;
+  int32_t seg_dense[kMaxSegments];   // 1 if every pair with this segment is dense
+  int32_t all_dense;                 // budget mode ALL
+  DevShape shape[kMaxShapes];
+  const int32_t* head_shape;     // [H]
+  const int64_t* head_row_off;   // [H] first permuted row
+  const int32_t* head_tile_off;  // [H] first global tile / CSR row
+  const int64_t* head_pair_off;  // [H] first score
+  const int64_t* head_nnz_off;   // [H] first col_idx entry
+  const int32_t* row_head;       // [T] head of every global tile
+  const int32_t* row_ptr;        // [T + 1] global CSR row pointers
+  const int32_t* attn_order;     // [attn_grid] global tile per workgroup, -1 idle
+  int32_t attn_grid;
+};
+
+// Kernel launchers (veda_kernels.hip).  Shapes are validated by the caller;
+// each returns the launch status.
+hipError_t launch_permute(const DevPlan& p, const void* src, void* dst, int direction,
+                          hipStream_t s);
+hipError_t launch_score(const DevPlan& p, const void* q, const void* k, const float* wq,
+                        const float* wk, float* scores, void* ws, hipStream_t s);
+hipError_t launch_select(const DevPlan& p, const float* scores, int32_t* row_ptr,
+                         int32_t* col_idx, uint8_t* dense_mask, hipStream_t s);
+hipError_t launch_attn_fwd(const DevPlan& p, const void* q, const void* k, const void* vt,
+                           const int32_t* row_ptr, const int32_t* col_idx, float scale,
+                           void* o, float* lse, uint32_t* visited, hipStream_t s);
+hipError_t launch_heat(const DevPlan& p, const void* q, const void* k, const float* lse,
+                       float scale, float* heat, hipStream_t s);
+
+// Scratch the score call needs: pooled features of Q and K (fp32 [T, 3D]
+// each) and their projections (fp32 [T, D] each).
+inline int64_t score_workspace_bytes(int64_t total_tiles, int32_t head_dim) {
+  return total_tiles * (int64_t)head_dim * 4 * (3 + 3 + 1 + 1);
+}
+
+}  // namespace veda

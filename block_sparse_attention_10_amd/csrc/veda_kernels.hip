@@ -1,0 +1,769 @@
+// HIP kernels of libveda for CDNA4 (gfx950, MI355X).
+//
+//   permute   gather natural [N,H,D] rows into per-head tile order (and back);
+//             V can be written per tile transposed, [D][128], the layout the
+//             attention kernel streams it in.                    HBM-bound
+//   pool      mean (fp64 sum) / max / min of every tile's valid slots
+//   project   per-head residual projection, fp64 sequential sums
+//   score     pair scores q_hat . k_hat, fp64 sequential sums
+//   select    per-row radix top-k on order-preserving 32-bit keys, ties to the
+//             lowest key tile, ascending CSR by wavefront ballot compaction
+//   attn_fwd  block-sparse flash attention over the CSR, bf16 MFMA
+//             (32x32x16), fp32 online softmax in the log2 domain
+//   heat      block heat from the dense LSE, same QK^T machinery, no PV
+//
+// The method is the Veda sparse attention of the Miowtion project page
+// ("Sparse acceleration (Veda)"; Key Features > "Veda sparse attention") and
+// the 128x128 block tiling of "Deploying this checkpoint", section 2.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "veda_internal.h"
+
+namespace veda {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// permute
+// ---------------------------------------------------------------------------
+
+// Row-wise gather/scatter: one thread moves 16 bytes (8 channels) of one row.
+template <int D>
+__global__ void __launch_bounds__(kThreads) permute_rows_kernel(DevPlan p, const uint16_t* __restrict__ src,
+                                                               uint16_t* __restrict__ dst, int inverse) {
+  constexpr int CH = D / 8;  // 16-byte chunks per row
+  const int64_t g = (int64_t)blockIdx.x * (kThreads / CH) + threadIdx.x / CH;
+  const int c = threadIdx.x % CH;
+  if (g >= p.total_rows) return;
+  const int64_t tile = g / kTile;
+  const int h = p.row_head[tile];
+  const DevShape& sh = p.shape[p.head_shape[h]];
+  const int64_t s = g - p.head_row_off[h];
+  const int32_t tok = sh.perm[s];
+  const int64_t nat = ((int64_t)tok * p.num_heads + h) * D + 8 * c;
+  if (!inverse) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (tok >= 0) v = ld16(src + nat);
+    st16(dst + g * D + 8 * c, v);
+  } else if (tok >= 0) {
+    st16(dst + nat, ld16(src + g * D + 8 * c));
+  }
+}
+
+// Forward permutation into the tile-transposed layout [T][D][128]: one
+// workgroup per tile gathers 128 rows into LDS and writes D rows of 128 slots.
+template <int D>
+__global__ void __launch_bounds__(kThreads) permute_vt_kernel(DevPlan p, const uint16_t* __restrict__ src,
+                                                             uint16_t* __restrict__ dst) {
+  constexpr int CH = D / 8;
+  constexpr int LD = D + 8;  // padded LDS row (bf16 elements)
+  __shared__ __attribute__((aligned(16))) uint16_t tileb[kTile * LD];
+  const int64_t t = blockIdx.x;
+  const int h = p.row_head[t];
+  const DevShape& sh = p.shape[p.head_shape[h]];
+  const int64_t s0 = t * kTile - p.head_row_off[h];  // first slot of the tile (head-local)
+  for (int q = threadIdx.x; q < kTile * CH; q += kThreads) {
+    const int r = q / CH, c = q % CH;
+    const int32_t tok = sh.perm[s0 + r];
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (tok >= 0) v = ld16(src + ((int64_t)tok * p.num_heads + h) * D + 8 * c);
+    *reinterpret_cast<u32x4*>(&tileb[r * LD + 8 * c]) = v;
+  }
+  __syncthreads();
+  // output row d holds 128 slots = 16 chunks of 8
+  uint16_t* out = dst + t * (int64_t)D * kTile;
+  for (int q = threadIdx.x; q < D * 16; q += kThreads) {
+    const int d = q / 16, c = q % 16;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = tileb[(8 * c + 2 * e) * LD + d];
+      const uint32_t hi = tileb[(8 * c + 2 * e + 1) * LD + d];
+      w[e] = lo | (hi << 16);
+    }
+    u32x4 v = {w[0], w[1], w[2], w[3]};
+    st16(out + (int64_t)d * kTile + 8 * c, v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// predictor: pool, project, score
+// ---------------------------------------------------------------------------
+
+// One workgroup per (tile, tensor).  Thread (row group g, chunk c) sums 8
+// channels over rows g, g+RG, ... < valid; partials meet in LDS and are
+// combined in a fixed order.  The fp64 sum of bf16 inputs is exact for the
+// inputs the method sees, so any order gives the same mean.
+template <int D>
+__global__ void __launch_bounds__(kThreads) pool_kernel(DevPlan p, const uint16_t* __restrict__ q,
+                                                       const uint16_t* __restrict__ k, float* __restrict__ feat_q,
+                                                       float* __restrict__ feat_k) {
+  constexpr int CH = D / 8;
+  constexpr int RG = kThreads / CH;
+  __shared__ double s_sum[RG][D];
+  __shared__ float s_max[RG][D];
+  __shared__ float s_min[RG][D];
+  const int64_t t = blockIdx.x;
+  const uint16_t* x = blockIdx.y ? k : q;
+  float* feat = blockIdx.y ? feat_k : feat_q;
+  const int h = p.row_head[t];
+  const DevShape& sh = p.shape[p.head_shape[h]];
+  const int i = (int)(t - p.head_tile_off[h]);
+  const int nv = sh.valid[i];
+  const int g = threadIdx.x / CH, c = threadIdx.x % CH;
+  double sum[8];
+  float mx[8], mn[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    sum[e] = 0.0;
+    mx[e] = -INFINITY;
+    mn[e] = INFINITY;
+  }
+  const uint16_t* base = x + t * (int64_t)kTile * D + 8 * c;
+  for (int r = g; r < nv; r += RG) {
+    u32x4 v = ld16(base + (int64_t)r * D);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = __uint_as_float(v[e] << 16);
+      const float hi = __uint_as_float(v[e] & 0xffff0000u);
+      sum[2 * e] += (double)lo;
+      sum[2 * e + 1] += (double)hi;
+      mx[2 * e] = fmaxf(mx[2 * e], lo);
+      mx[2 * e + 1] = fmaxf(mx[2 * e + 1], hi);
+      mn[2 * e] = fminf(mn[2 * e], lo);
+      mn[2 * e + 1] = fminf(mn[2 * e + 1], hi);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    s_sum[g][8 * c + e] = sum[e];
+    s_max[g][8 * c + e] = mx[e];
+    s_min[g][8 * c + e] = mn[e];
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    double tot = 0.0;
+    float a = -INFINITY, b = INFINITY;
+    for (int r = 0; r < RG; ++r) {
+      tot += s_sum[r][d];
+      a = fmaxf(a, s_max[r][d]);
+      b = fminf(b, s_min[r][d]);
+    }
+    float* out = feat + t * (int64_t)(3 * D);
+    out[d] = (float)(tot / (double)nv);
+    out[D + d] = a;
+    out[2 * D + d] = b;
+  }
+}
+
+// x_hat[t][d] = fp32(mean[d] + sum_e W[h][d][e] f[t][e]), e ascending, fp64.
+// Workgroup = (16-tile chunk of one head, head, tensor); W[h][d][:] is read
+// once per chunk.
+constexpr int kProjTiles = 16;
+
+template <int D>
+__global__ void __launch_bounds__(kThreads) project_kernel(DevPlan p, const float* __restrict__ wq,
+                                                          const float* __restrict__ wk,
+                                                          const float* __restrict__ feat_q,
+                                                          const float* __restrict__ feat_k, float* __restrict__ hat_q,
+                                                          float* __restrict__ hat_k) {
+  constexpr int E = 3 * D;
+  constexpr int G = kThreads / D;           // tile groups
+  constexpr int TPT = kProjTiles / G;       // tiles per thread
+  __shared__ float f[kProjTiles][E];
+  const int h = blockIdx.y;
+  const DevShape& sh = p.shape[p.head_shape[h]];
+  const int n = sh.num_tiles;
+  const int i0 = blockIdx.x * kProjTiles;
+  if (i0 >= n) return;
+  const int cnt = min(kProjTiles, n - i0);
+  const float* W = (blockIdx.z ? wk : wq) + (int64_t)h * D * E;
+  const float* feat = blockIdx.z ? feat_k : feat_q;
+  float* hat = blockIdx.z ? hat_k : hat_q;
+  const int64_t t0 = p.head_tile_off[h] + i0;
+  for (int q = threadIdx.x; q < kProjTiles * E; q += kThreads) {
+    const int r = q / E;
+    f[r][q % E] = r < cnt ? feat[(t0 + r) * E + q % E] : 0.0f;
+  }
+  __syncthreads();
+  const int d = threadIdx.x % D, grp = threadIdx.x / D;
+  double acc[TPT];
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) acc[u] = (double)f[grp * TPT + u][d];
+  const float* wr = W + (int64_t)d * E;
+  for (int e = 0; e < E; ++e) {
+    const double w = (double)wr[e];
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) acc[u] = fma(w, (double)f[grp * TPT + u][e], acc[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+    const int r = grp * TPT + u;
+    if (r < cnt) hat[(t0 + r) * D + d] = (float)acc[u];
+  }
+}
+
+// s[i][j] = fp32(sum_d q_hat_i[d] k_hat_j[d]), d ascending in fp64; 64x64
+// output tile per workgroup, 4x4 per thread.
+template <int D>
+__global__ void __launch_bounds__(kThreads) score_kernel(DevPlan p, const float* __restrict__ hat_q,
+                                                        const float* __restrict__ hat_k, float* __restrict__ scores) {
+  __shared__ float qs[D][64];
+  __shared__ float ks[D][64];
+  const int h = blockIdx.z;
+  const DevShape& sh = p.shape[p.head_shape[h]];
+  const int n = sh.num_tiles;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  if (i0 >= n || j0 >= n) return;
+  const int64_t t0 = p.head_tile_off[h];
+  for (int q = threadIdx.x; q < 64 * D; q += kThreads) {
+    const int r = q / D, d = q % D;
+    qs[d][r] = (i0 + r < n) ? hat_q[(t0 + i0 + r) * D + d] : 0.0f;
+    ks[d][r] = (j0 + r < n) ? hat_k[(t0 + j0 + r) * D + d] : 0.0f;
+  }
+  __syncthreads();
+  const int ti = threadIdx.x / 16, tj = threadIdx.x % 16;
+  double acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  for (int d = 0; d < D; ++d) {
+    const float4 qa = *reinterpret_cast<const float4*>(&qs[d][4 * ti]);
+    const float4 kb = *reinterpret_cast<const float4*>(&ks[d][4 * tj]);
+    const double qv[4] = {(double)qa.x, (double)qa.y, (double)qa.z, (double)qa.w};
+    const double kv[4] = {(double)kb.x, (double)kb.y, (double)kb.z, (double)kb.w};
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = fma(qv[a], kv[b], acc[a][b]);
+  }
+  float* out = scores + p.head_pair_off[h];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int i = i0 + 4 * ti + a;
+    if (i >= n) continue;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int j = j0 + 4 * tj + b;
+      if (j >= n) continue;
+      uint32_t u = __float_as_uint((float)acc[a][b]);
+      if ((u & 0x7fffffffu) == 0u) u = 0u;  // -0 -> +0
+      out[(int64_t)i * n + j] = __uint_as_float(u);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// select: budgeted top-k per row
+// ---------------------------------------------------------------------------
+
+// Order-preserving key: larger score <=> larger unsigned key; -0 == +0.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t lanes_below() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// One 64-lane workgroup per CSR row.  Per budgeted key segment a 4-pass,
+// 8-bit radix select finds the k-th largest key T and how many keys equal to
+// T to take; the final pass walks the row's columns in ascending 64-wide
+// chunks, decides each column and compacts with ballots, so col_idx comes out
+// ascending.
+__global__ void __launch_bounds__(64) select_kernel(DevPlan p, const float* __restrict__ scores,
+                                                   int32_t* __restrict__ row_ptr_out, int32_t* __restrict__ col_idx,
+                                                   uint8_t* __restrict__ dense_mask) {
+  __shared__ uint32_t hist[256];
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int h = p.row_head[t];
+  const DevShape& sh = p.shape[p.head_shape[h]];
+  const int n = sh.num_tiles;
+  const int i = (int)(t - p.head_tile_off[h]);
+  const int S = p.num_segments;
+  const int A = sh.tile_seg[i];
+  const float* srow = scores + p.head_pair_off[h] + (int64_t)i * n;
+  const int32_t rp0 = p.row_ptr[t];
+  const int32_t row_len = p.row_ptr[t + 1] - rp0;
+  if (lane == 0) {
+    row_ptr_out[t] = rp0;
+    if (t == p.total_tiles - 1) row_ptr_out[t + 1] = p.row_ptr[t + 1];
+  }
+  // per segment: mode 0 = all, 1 = diagonal only / nothing, 2 = radix threshold
+  uint32_t thr[kMaxSegments];
+  int32_t rem[kMaxSegments], mode[kMaxSegments];
+#pragma unroll
+  for (int B = 0; B < kMaxSegments; ++B) {
+    thr[B] = 0u;
+    rem[B] = 0;
+    mode[B] = 1;
+    if (B >= S) continue;
+    const int first = sh.seg_first[B], count = sh.seg_count[B];
+    const int kb = sh.budget[(int64_t)i * S + B];
+    if (kb >= count) {
+      mode[B] = 0;
+      continue;
+    }
+    const int diag = (A == B) ? i : -1;
+    int need = kb - (diag >= 0 ? 1 : 0);
+    if (need <= 0) continue;
+    mode[B] = 2;
+    uint32_t prefix = 0u, pmask = 0u;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int b = lane; b < 256; b += 64) hist[b] = 0u;
+      __syncthreads();
+      for (int j = first + lane; j < first + count; j += 64) {
+        if (j == diag) continue;
+        const uint32_t key = order_key(srow[j]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
+                     c3 = hist[4 * lane + 3];
+      const uint32_t mine = c0 + c1 + c2 + c3;
+      // inclusive suffix sum over lanes: sum of bins of this lane and above
+      uint32_t suf = mine;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_down(suf, off, 64);
+        if (lane + off < 64) suf += y;
+      }
+      uint32_t above = suf - mine;
+      int found = 0, digit = 0, need_left = 0;
+      if (above < (uint32_t)need && (uint32_t)need <= suf) {
+        const uint32_t cs[4] = {c0, c1, c2, c3};
+        for (int b = 3; b >= 0; --b) {
+          if (above + cs[b] >= (uint32_t)need) {
+            digit = 4 * lane + b;
+            need_left = need - (int)above;
+            found = 1;
+            break;
+          }
+          above += cs[b];
+        }
+      }
+      const uint64_t fm = __ballot(found);
+      const int src = fm ? __ffsll((unsigned long long)fm) - 1 : 0;
+      digit = __shfl(digit, src, 64);
+      need = __shfl(need_left, src, 64);
+      prefix |= (uint32_t)digit << shift;
+      pmask |= 255u << shift;
+      __syncthreads();
+    }
+    thr[B] = prefix;
+    rem[B] = need;
+  }
+  // final pass over the columns in ascending order
+  int32_t eq_seen[kMaxSegments];
+#pragma unroll
+  for (int B = 0; B < kMaxSegments; ++B) eq_seen[B] = 0;
+  int32_t pos = 0;
+  const uint64_t below = lanes_below();
+  uint8_t* mrow = dense_mask ? dense_mask + p.head_pair_off[h] + (int64_t)i * n : nullptr;
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int j = c0 + lane;
+    const bool in = j < n;
+    const int Bj = in ? sh.tile_seg[j] : -1;
+    const uint32_t key = in ? order_key(srow[j]) : 0u;
+    bool sel = false;
+#pragma unroll
+    for (int B = 0; B < kMaxSegments; ++B) {
+      if (B >= S) continue;
+      const bool mine = (Bj == B);
+      if (mode[B] == 0) {
+        sel = sel || mine;
+        continue;
+      }
+      const bool isdiag = mine && (A == B) && (j == i);
+      if (mode[B] == 1) {
+        sel = sel || isdiag;
+        continue;
+      }
+      const bool eq = mine && !isdiag && key == thr[B];
+      const uint64_t em = __ballot(eq);
+      const int rank = eq_seen[B] + __popcll(em & below);
+      if (mine) sel = isdiag || (key > thr[B] && !isdiag) || (eq && rank < rem[B]);
+      eq_seen[B] += __popcll(em);
+    }
+    const uint64_t sm = __ballot(sel);
+    const int32_t at = pos + __popcll(sm & below);
+    if (sel && at < row_len) col_idx[rp0 + at] = j;  // a row never exceeds its budget
+    pos += __popcll(sm);
+    if (mrow && in) mrow[j] = sel ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// block-sparse attention forward
+// ---------------------------------------------------------------------------
+//
+// One workgroup (4 waves) per (head, 128-row query tile); wave w owns query
+// rows 32w .. 32w+31.  Per key block the wave computes S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T from registers), so
+// each lane holds one query column and the softmax reductions over keys stay
+// inside the lane plus one exchange with the lane 32 away.  Then
+// O^T += V^T P^T with A = V^T from LDS and B = P^T straight from the S^T
+// registers: the K rows of each 32-key group are stored in LDS in the order
+// pi(m) (bits 2 and 3 of m swapped) so that the eight S^T values a lane holds
+// for one 16-key MFMA step are eight consecutive keys, i.e. one 16-byte
+// V^T read.  LDS rows are XOR-swizzled by 16-byte chunk (chunk ^ (row & 15))
+// so the 16-byte operand reads of consecutive lanes hit distinct banks.
+
+__device__ __forceinline__ int pi_row(int m) {  // swap bits 2 and 3
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+template <int D>
+struct AttnTiles {
+  static constexpr int CH = D / 8;           // 16-byte chunks per K row
+  static constexpr int KB = kTile * D;       // bf16 elements of one K / V^T tile
+};
+
+// Stage a K tile (rows in pi order, swizzled) and a V^T tile into LDS.
+template <int D>
+__device__ __forceinline__ void load_kv_tile(uint16_t* __restrict__ ks, uint16_t* __restrict__ vs,
+                                             const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg) {
+  constexpr int CH = D / 8;
+  constexpr int KCH = kTile * CH;  // chunks per K tile
+  constexpr int PER = KCH / kThreads;
+  {
+    u32x4 kr[PER];
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int q = it * kThreads + threadIdx.x;
+      const int m = q / CH, pc = q % CH;
+      const int c = pc ^ (m & (CH - 1));
+      const int key = (m & ~31) | pi_row(m & 31);
+      kr[it] = ld16(kg + (int64_t)key * D + 8 * c);
+    }
+#pragma unroll
+    for (int it = 0; it < PER; ++it) st16(ks + 8 * (it * kThreads + threadIdx.x), kr[it]);
+  }
+  if (vs) {
+    u32x4 vr[PER];
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int q = it * kThreads + threadIdx.x;
+      const int d = q / 16, pc = q % 16;
+      const int c = pc ^ (d & 15);
+      vr[it] = ld16(vg + (int64_t)d * kTile + 8 * c);
+    }
+#pragma unroll
+    for (int it = 0; it < PER; ++it) st16(vs + 8 * (it * kThreads + threadIdx.x), vr[it]);
+  }
+}
+
+// S^T for one 128-key block: sacc[kt] covers keys 32kt.. in MFMA row order.
+template <int D>
+__device__ __forceinline__ void qk_block(const uint16_t* __restrict__ ks, const bf16x8 (&qf)[D / 16],
+                                         f32x16 (&sacc)[4]) {
+  constexpr int CH = D / 8;
+  const int lane = lane_id();
+  const int ln = lane & 31, hl = lane >> 5;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    f32x16 acc = {};
+    const int m = 32 * kt + ln;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const int c = 2 * s + hl;
+      const u32x4 raw = ld16(ks + m * D + 8 * (c ^ (m & (CH - 1))));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, raw);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc, 0, 0, 0);
+    }
+    sacc[kt] = acc;
+  }
+}
+
+// Key index (0..127 inside the block) held by S^T register r of key group kt.
+__device__ __forceinline__ int sacc_key(int kt, int r, int hl) {
+  return 32 * kt + 16 * (r >> 3) + 8 * hl + (r & 7);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ k,
+                                                              const uint16_t* __restrict__ vt,
+                                                              const int32_t* __restrict__ row_ptr,
+                                                              const int32_t* __restrict__ col_idx, float scale_log2,
+                                                              uint16_t* __restrict__ o, float* __restrict__ lse,
+                                                              uint32_t* __restrict__ visited) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kTile * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[D * kTile];
+  const int t = p.attn_order[blockIdx.x];
+  if (t < 0) return;
+  const int h = p.row_head[t];
+  const DevShape& sh = p.shape[p.head_shape[h]];
+  const int i = t - p.head_tile_off[h];
+  const int64_t hrow = p.head_row_off[h];
+  const int64_t row0 = hrow + (int64_t)kTile * i;
+  const int64_t tile0 = p.head_tile_off[h];
+  const int beg = row_ptr[t], end = row_ptr[t + 1];
+  const int w = threadIdx.x >> 6, lane = lane_id(), ln = lane & 31, hl = lane >> 5;
+
+  // Q^T operand: query row 32w + ln, channels 16s + 8hl .. +7
+  bf16x8 qf[D / 16];
+  const uint16_t* qrow = q + (row0 + 32 * w + ln) * D + 8 * hl;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld16(qrow + 16 * s));
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  for (int b = beg; b < end; ++b) {
+    const int j = min(max(col_idx[b], 0), sh.num_tiles - 1);  // stay inside the head
+    const int nj = sh.valid[j];
+    __syncthreads();
+    load_kv_tile<D>(ks, vs, k + (hrow + (int64_t)kTile * j) * D, vt + (tile0 + j) * (int64_t)D * kTile);
+    __syncthreads();
+    f32x16 sacc[4];
+    qk_block<D>(ks, qf, sacc);
+    if (nj < kTile) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (sacc_key(kt, r, hl) >= nj) sacc[kt][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    // per 32-key group: P = exp2(s*c - m), then O^T[d][q] += V^T[d][keys] P^T[keys][q]
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      bf16x8 pb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], scale_log2, -m_new));
+        l_run += pv;
+        pb[r >> 3][r & 7] = (__bf16)pv;
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int c = 4 * kt + 2 * s2 + hl;  // 16-byte chunk of keys in a V^T row
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int d = 32 * db + ln;
+          const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(vs + d * kTile + 8 * (c ^ (d & 15))));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s2], oacc[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // epilogue: combine the two lane halves' partial sums, normalise, store
+  const float l_all = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / l_all;
+  uint16_t* orow = o + (row0 + 32 * w + ln) * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      bf16x2 lo, hi;
+      lo[0] = (__bf16)(oacc[db][4 * jj + 0] * inv);
+      lo[1] = (__bf16)(oacc[db][4 * jj + 1] * inv);
+      hi[0] = (__bf16)(oacc[db][4 * jj + 2] * inv);
+      hi[1] = (__bf16)(oacc[db][4 * jj + 3] * inv);
+      uint2 v;
+      v.x = __builtin_bit_cast(uint32_t, lo);
+      v.y = __builtin_bit_cast(uint32_t, hi);
+      *reinterpret_cast<uint2*>(orow + 32 * db + 8 * jj + 4 * hl) = v;
+    }
+  if (lse && hl == 0) lse[row0 + 32 * w + ln] = m_run * 0.69314718055994531f + logf(l_all);
+  if (visited && threadIdx.x == 0) atomicAdd(visited, (uint32_t)(end - beg));
+}
+
+// ---------------------------------------------------------------------------
+// block heat from the dense LSE
+// ---------------------------------------------------------------------------
+//
+// One workgroup per (head, query tile); it walks every key tile of the head,
+// computes S^T as the attention kernel does, and sums
+// exp2(s * scale*log2e - lse*log2e) over valid (query, key) pairs.  Each
+// wave reduces its partial across lanes; the four wave partials are added in
+// a fixed order by thread 0 of the next iteration.
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2) heat_kernel(DevPlan p, const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ k,
+                                                          const float* __restrict__ lse, float scale_log2,
+                                                          float* __restrict__ heat) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kTile * D];
+  __shared__ float red[2][4];
+  const int t = blockIdx.x;
+  const int h = p.row_head[t];
+  const DevShape& sh = p.shape[p.head_shape[h]];
+  const int n = sh.num_tiles;
+  const int i = t - p.head_tile_off[h];
+  const int ni = sh.valid[i];
+  const int64_t hrow = p.head_row_off[h];
+  const int64_t row0 = hrow + (int64_t)kTile * i;
+  const int w = threadIdx.x >> 6, lane = lane_id(), ln = lane & 31, hl = lane >> 5;
+  const int qr = 32 * w + ln;
+  const bool qvalid = qr < ni;
+  bf16x8 qf[D / 16];
+  const uint16_t* qrow = q + (row0 + qr) * D + 8 * hl;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld16(qrow + 16 * s));
+  const float l2 = qvalid ? lse[row0 + qr] * 1.4426950408889634f : 0.0f;
+  float* hrow_out = heat + p.head_pair_off[h] + (int64_t)i * n;
+  const float inv_ni = 1.0f / (float)ni;
+  for (int j = 0; j <= n; ++j) {
+    __syncthreads();
+    if (j > 0 && threadIdx.x == 0) {
+      const float* rr = red[(j - 1) & 1];
+      hrow_out[j - 1] = (((rr[0] + rr[1]) + rr[2]) + rr[3]) * inv_ni;
+    }
+    if (j == n) break;
+    const int nj = sh.valid[j];
+    load_kv_tile<D>(ks, nullptr, k + (hrow + (int64_t)kTile * j) * D, nullptr);
+    __syncthreads();
+    f32x16 sacc[4];
+    qk_block<D>(ks, qf, sacc);
+    float part = 0.0f;
+    if (qvalid) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], scale_log2, -l2));
+          part += (sacc_key(kt, r, hl) < nj) ? pv : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+    if (lane == 0) red[j & 1][w] = part;
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_permute(const DevPlan& p, const void* src, void* dst, int direction, hipStream_t s) {
+  const uint16_t* in = static_cast<const uint16_t*>(src);
+  uint16_t* out = static_cast<uint16_t*>(dst);
+  if (direction == VEDA_PERMUTE_FORWARD_TRANSPOSED) {
+    const dim3 grid((unsigned)p.total_tiles);
+    if (p.head_dim == 128)
+      hipLaunchKernelGGL(permute_vt_kernel<128>, grid, dim3(kThreads), 0, s, p, in, out);
+    else
+      hipLaunchKernelGGL(permute_vt_kernel<64>, grid, dim3(kThreads), 0, s, p, in, out);
+    return hipGetLastError();
+  }
+  const int inverse = direction == VEDA_PERMUTE_INVERSE;
+  const int rows_per_block = kThreads / (p.head_dim / 8);
+  const dim3 grid((unsigned)((p.total_rows + rows_per_block - 1) / rows_per_block));
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL(permute_rows_kernel<128>, grid, dim3(kThreads), 0, s, p, in, out, inverse);
+  else
+    hipLaunchKernelGGL(permute_rows_kernel<64>, grid, dim3(kThreads), 0, s, p, in, out, inverse);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const DevPlan& p, const void* q, const void* k, const float* wq, const float* wk,
+                        float* scores, void* ws, hipStream_t s) {
+  const int D = p.head_dim;
+  const int64_t T = p.total_tiles;
+  float* feat_q = static_cast<float*>(ws);
+  float* feat_k = feat_q + T * 3 * D;
+  float* hat_q = feat_k + T * 3 * D;
+  float* hat_k = hat_q + T * D;
+  int maxn = 0;
+  for (int g = 0; g < p.num_shapes; ++g) maxn = maxn > p.shape[g].num_tiles ? maxn : p.shape[g].num_tiles;
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const dim3 gpool((unsigned)T, 2);
+  const dim3 gproj((unsigned)((maxn + kProjTiles - 1) / kProjTiles), (unsigned)p.num_heads, 2);
+  const dim3 gscore((unsigned)((maxn + 63) / 64), (unsigned)((maxn + 63) / 64), (unsigned)p.num_heads);
+  if (D == 128) {
+    hipLaunchKernelGGL(pool_kernel<128>, gpool, dim3(kThreads), 0, s, p, qq, kk, feat_q, feat_k);
+    hipLaunchKernelGGL(project_kernel<128>, gproj, dim3(kThreads), 0, s, p, wq, wk, feat_q, feat_k, hat_q, hat_k);
+    hipLaunchKernelGGL(score_kernel<128>, gscore, dim3(kThreads), 0, s, p, hat_q, hat_k, scores);
+  } else {
+    hipLaunchKernelGGL(pool_kernel<64>, gpool, dim3(kThreads), 0, s, p, qq, kk, feat_q, feat_k);
+    hipLaunchKernelGGL(project_kernel<64>, gproj, dim3(kThreads), 0, s, p, wq, wk, feat_q, feat_k, hat_q, hat_k);
+    hipLaunchKernelGGL(score_kernel<64>, gscore, dim3(kThreads), 0, s, p, hat_q, hat_k, scores);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const DevPlan& p, const float* scores, int32_t* row_ptr, int32_t* col_idx,
+                         uint8_t* dense_mask, hipStream_t s) {
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)p.total_tiles), dim3(64), 0, s, p, scores, row_ptr, col_idx,
+                     dense_mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd(const DevPlan& p, const void* q, const void* k, const void* vt, const int32_t* row_ptr,
+                           const int32_t* col_idx, float scale, void* o, float* lse, uint32_t* visited,
+                           hipStream_t s) {
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const dim3 grid((unsigned)p.attn_grid);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(vt);
+  uint16_t* oo = static_cast<uint16_t*>(o);
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
+                       scale_log2, oo, lse, visited);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
+                       scale_log2, oo, lse, visited);
+  return hipGetLastError();
+}
+
+hipError_t launch_heat(const DevPlan& p, const void* q, const void* k, const float* lse, float scale, float* heat,
+                       hipStream_t s) {
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const dim3 grid((unsigned)p.total_tiles);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL(heat_kernel<128>, grid, dim3(kThreads), 0, s, p, qq, kk, lse, scale_log2, heat);
+  else
+    hipLaunchKernelGGL(heat_kernel<64>, grid, dim3(kThreads), 0, s, p, qq, kk, lse, scale_log2, heat);
+  return hipGetLastError();
+}
+
+}  // namespace veda

@@ -1,0 +1,245 @@
+/*
+ * veda.h -- C ABI of the Veda block-sparse attention library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method (Miowtion project page, intro bullet "Sparse acceleration (Veda)"
+ * and Key Features > "Veda sparse attention"): the video tokens of each head
+ * are permuted into 3D (t, h, w) tiles of 128 tokens; a small per-head
+ * predictor pools every tile (mean, max, min), projects it and scores every
+ * (query tile, key tile) pair; a block mask keeps the top-scoring pairs under
+ * equal-kernel-cost budgets with Bresenham rounding and a forced diagonal; and
+ * flash attention computes only the kept 128x128 blocks.  "Deploying this
+ * checkpoint", section 2 (SM90): the block mask reaches the kernel packed into
+ * index lists, and query tiles are 128 rows.
+ *
+ * Conventions shared by every call:
+ *  - Every pointer named "device" is caller-owned GPU memory (e.g. from torch),
+ *    contiguous and 16-byte aligned.  The library never allocates GPU memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every compute call only enqueues work on it and returns; it never
+ *    synchronises the host.
+ *  - Every argument, shape and plan check happens on the host before any
+ *    launch.  A failed check returns a non-zero veda_status, launches nothing,
+ *    and leaves a message for veda_last_error() on the calling thread.
+ *  - Nothing is ever silently computed another way: an unsupported device,
+ *    dtype, head dim or plan returns VEDA_ERR_UNSUPPORTED (the pages' rule of
+ *    an explicit error instead of a silent dense fallback, "Deploying this
+ *    checkpoint", sections 2 and 5).
+ *  - Tensors are bf16 (stored as uint16 bit patterns) unless stated otherwise.
+ *
+ * Layouts (N = tokens of the packed sequence, H = heads, D = head dim):
+ *  - natural:   bf16 [N, H, D], token-major, as a fused QKV projection emits.
+ *  - permuted:  bf16 [R, D] with R = sum_h L_h, head-major; head h owns rows
+ *               [row_offset(h), row_offset(h) + L_h), L_h = 128 * n_h, and
+ *               row row_offset(h) + 128*i + s is slot s of tile i.  The valid
+ *               tokens of a tile occupy its first valid(i) slots; padding
+ *               slots hold +0.
+ *  - tile-transposed (V only): bf16 [T, D, 128] with T = sum_h n_h; block t
+ *               holds tile t (head-major, like the rows above) with element
+ *               [t][d][s] = V_perm[128 t + s][d].  This is the layout the
+ *               attention kernel streams V in.
+ *  - scores:    fp32, head h's n_h x n_h matrix (row = query tile, column =
+ *               key tile) at offset pair_offset(h).
+ *  - CSR mask:  row_ptr int32 [T + 1] over the global rows t = tile_offset(h)
+ *               + i; col_idx int32 [nnz] holds head-local key tile indices,
+ *               ascending within a row.
+ */
+#ifndef VEDA_H
+#define VEDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VEDA_ABI_VERSION 1
+
+typedef int32_t veda_status;
+enum {
+  VEDA_OK = 0,
+  VEDA_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad enum value     */
+  VEDA_ERR_SHAPE = 2,       /* sizes inconsistent with the plan              */
+  VEDA_ERR_UNSUPPORTED = 3, /* device, head dim, plan form not supported     */
+  VEDA_ERR_WORKSPACE = 4,   /* workspace missing or too small                */
+  VEDA_ERR_LAUNCH = 5,      /* the HIP runtime rejected a copy or a launch   */
+  VEDA_ERR_STATE = 6        /* plan used before veda_plan_upload             */
+};
+
+/* Segment kinds of the packed sequence (Miowtion project page, Key Features >
+ * "H3 DiT for training": packed t2va / fl2va / ref2va layouts). */
+enum { VEDA_SEG_VIDEO3D = 0, VEDA_SEG_DENSE1D = 1 };
+
+/* Budget modes.  KEEP_RATIO: equal-kernel-cost budgets, keep_num/keep_den of
+ * the blocks a dense kernel over the valid tokens of each (query segment, key
+ * segment) video pair would compute, spread over query tiles by midpoint
+ * Bresenham rounding (Key Features > "Veda sparse attention").  FIXED_K:
+ * fixed_k key tiles per query tile and key segment.  ALL: every block (dense
+ * attention through the same kernel; used for the dense LSE). */
+enum { VEDA_BUDGET_KEEP_RATIO = 0, VEDA_BUDGET_FIXED_K = 1, VEDA_BUDGET_ALL = 2 };
+
+/* Directions of veda_permute_tiles. */
+enum {
+  VEDA_PERMUTE_FORWARD = 0,            /* natural  -> permuted              */
+  VEDA_PERMUTE_INVERSE = 1,            /* permuted -> natural (valid slots) */
+  VEDA_PERMUTE_FORWARD_TRANSPOSED = 2  /* natural  -> tile-transposed (V)   */
+};
+
+typedef struct veda_segment {
+  int32_t kind;         /* VEDA_SEG_VIDEO3D or VEDA_SEG_DENSE1D              */
+  int32_t t, h, w;      /* grid; a DENSE1D segment of length n is (1, 1, n)  */
+  int64_t token_offset; /* first token of the segment in the packed sequence */
+} veda_segment;
+
+typedef struct veda_plan_desc {
+  int32_t num_segments;          /* 1 .. 8, in packed order, contiguous from 0 */
+  const veda_segment* segments;  /* host array [num_segments]                 */
+  int32_t num_heads;             /* 1 .. 1024                                 */
+  int32_t head_dim;              /* 64 or 128                                 */
+  const int32_t* tile_shape;     /* host array [num_heads][3]: (a, b, c) per
+                                    head, a*b*c == 128, at most 2 distinct     */
+  int32_t budget_mode;           /* VEDA_BUDGET_*                             */
+  int32_t keep_num, keep_den;    /* KEEP_RATIO: 0 <= keep_num <= keep_den     */
+  int32_t fixed_k;               /* FIXED_K: >= 0 (the diagonal is always kept)*/
+} veda_plan_desc;
+
+typedef struct veda_plan veda_plan; /* opaque, host memory */
+
+typedef struct veda_plan_info {
+  int64_t num_tokens;         /* N                                            */
+  int32_t num_heads, head_dim, num_segments, num_shapes;
+  int64_t total_rows;         /* R = sum_h 128 n_h                            */
+  int64_t total_tiles;        /* T = sum_h n_h                                */
+  int64_t total_pairs;        /* sum_h n_h^2 (length of the score array)      */
+  int64_t nnz;                /* kept blocks over all heads (exact, from the
+                                 budgets; known before any launch)            */
+  int64_t max_row_blocks;     /* longest CSR row                              */
+  int64_t device_table_bytes; /* bytes veda_plan_upload needs                 */
+  int64_t score_workspace_bytes; /* bytes veda_score_tiles needs              */
+  int32_t max_tiles_per_head;
+  int32_t uploaded;           /* 1 after a successful veda_plan_upload        */
+} veda_plan_info;
+
+/* ABI version of the loaded library (VEDA_ABI_VERSION it was built with). */
+int veda_abi_version(void);
+
+/* VEDA_OK iff `device` is a gfx950 GPU the library was built for; otherwise
+ * VEDA_ERR_UNSUPPORTED and a reason in `reason` (may be NULL, truncated to n).
+ * Every compute call re-checks the current device the same way. */
+veda_status veda_available(int device, char* reason, size_t n);
+
+/* Message of the last non-OK status on the calling thread ("" if none). */
+const char* veda_last_error(void);
+
+/* Build a plan on the host (no GPU call).  Validates the description and
+ * computes the tiles of every head (readings of the Veda tiling: tiles
+ * row-major over the padded tile grid, tokens row-major inside each tile's
+ * valid box, valid prefix then padding), the slot->token tables, the per-row
+ * budgets per key segment and the CSR row pointers.  *out receives a plan the
+ * caller frees with veda_plan_destroy. */
+veda_status veda_plan_create(const veda_plan_desc* desc, veda_plan** out);
+void veda_plan_destroy(veda_plan* plan);
+
+veda_status veda_plan_query(const veda_plan* plan, veda_plan_info* info);
+
+/* Per-head geometry: tiles n_h, first row, first global tile, first score. */
+veda_status veda_plan_head(const veda_plan* plan, int32_t head, int32_t* num_tiles,
+                           int64_t* row_offset, int64_t* tile_offset,
+                           int64_t* pair_offset);
+
+/* Host copies of plan tables (for tests and tools).  Each takes the element
+ * count of `out` and fails with VEDA_ERR_SHAPE if it differs from:
+ *   perm:    L_h     int32 slot -> token, -1 for padding
+ *   valid:   n_h     int32 valid tokens per tile
+ *   budgets: n_h * S int32 blocks row i keeps from key segment s
+ *   row_ptr: T + 1   int32 global CSR row pointers */
+veda_status veda_plan_copy_perm(const veda_plan* plan, int32_t head, int32_t* out, int64_t n);
+veda_status veda_plan_copy_valid(const veda_plan* plan, int32_t head, int32_t* out, int64_t n);
+veda_status veda_plan_copy_budgets(const veda_plan* plan, int32_t head, int32_t* out, int64_t n);
+veda_status veda_plan_copy_row_ptr(const veda_plan* plan, int32_t* out, int64_t n);
+
+/* Copy the plan's tables into caller-owned device memory `dev_tables`
+ * (device_table_bytes bytes, 256-byte aligned) with an async copy on `stream`.
+ * The host plan keeps the device address; `dev_tables` must stay alive and
+ * unmodified while the plan is used.  Upload once, before any compute call;
+ * the plan is then immutable and may be used from several threads. */
+veda_status veda_plan_upload(veda_plan* plan, void* dev_tables, size_t bytes, void* stream);
+
+/* Tile permutation (Miowtion project page, "Sparse acceleration (Veda)" and
+ * Key Features > "Veda sparse attention": per-head 3D tiles of 128 tokens,
+ * padded grids with valid-prefix tiles).
+ *   FORWARD:            src natural [N,H,D] -> dst permuted [R,D]
+ *   FORWARD_TRANSPOSED: src natural [N,H,D] -> dst tile-transposed [T,D,128]
+ *   INVERSE:            src permuted [R,D]  -> dst natural [N,H,D]; only
+ *                       valid slots are written (padding rows are dropped).
+ * Padding slots of the forward outputs are written as +0.  Bit copies. */
+veda_status veda_permute_tiles(const veda_plan* plan, const void* src, void* dst,
+                               int32_t direction, void* stream);
+
+/* The predictor (Key Features > "Veda sparse attention": mean/max/min pooling
+ * plus a per-head residual projection; "Sparse acceleration (Veda)": scores
+ * of (query tile, key tile) pairs).  For every tile, over its valid slots only:
+ * f = [mean | max | min] (fp32; the mean from an fp64 sum), then
+ * x_hat[d] = fp32(mean[d] + sum_e W[h][d][e] * f[e]) summed in fp64 over
+ * e = 0..3D-1 ascending, and s[i][j] = fp32(sum_d q_hat_i[d] * k_hat_j[d]) in
+ * fp64 over d ascending, with -0 written as +0.
+ *   q_perm, k_perm: device permuted bf16 [R, D]
+ *   w_q, w_k:       device fp32 [H, D, 3D]
+ *   scores:         device fp32 [sum_h n_h^2]
+ *   workspace:      device scratch of score_workspace_bytes (16-byte aligned) */
+veda_status veda_score_tiles(const veda_plan* plan, const void* q_perm, const void* k_perm,
+                             const float* w_q, const float* w_k, float* scores,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Budgeted top-k block mask (Key Features > "Veda sparse attention":
+ * equal-kernel-cost budgets, Bresenham rounding, forced diagonal, segmented
+ * reference/target budgets).  Row i of head h keeps, per key segment B, the
+ * plan's budget k[i][B]: the diagonal tile first when i lies in B, then B's
+ * highest-scoring tiles, ties to the lowest key tile index; pairs with a
+ * DENSE1D segment keep every tile.  Outputs (device): row_ptr int32 [T+1],
+ * col_idx int32 [nnz] ascending per row, and, if dense_mask is not NULL,
+ * uint8 [sum_h n_h^2] with 1 for kept blocks.  Scores must be finite. */
+veda_status veda_select_blocks(const veda_plan* plan, const float* scores, int32_t* row_ptr,
+                               int32_t* col_idx, uint8_t* dense_mask, void* stream);
+
+/* Block-sparse flash attention forward (Miowtion project page, "Sparse
+ * acceleration (Veda)": only the kept blocks are computed; Key Features >
+ * "Veda sparse attention": singleton mask_mod with full/partial block lists;
+ * "Deploying this checkpoint", section 2 (SM90): 128x128 tiles).
+ * For every query tile (head h, tile i) the kernel walks col_idx[row_ptr[t] ..
+ * row_ptr[t+1]) and computes, for each query slot r,
+ *   O[r] = softmax_c(scale * q_r . k_c) v_c,  LSE[r] = log sum_c exp(scale q_r.k_c)
+ * over the valid slots c of the listed key tiles (slots >= valid(j) are
+ * masked: the only mask rule).  bf16 MFMA products, fp32 online softmax.
+ *   q, k:   device permuted bf16 [R, D]
+ *   v_t:    device tile-transposed bf16 [T, D, 128]
+ *   row_ptr, col_idx: device CSR as written by veda_select_blocks (or any CSR
+ *           of this plan's shape with ascending, in-range, non-empty rows)
+ *   o:      device permuted bf16 [R, D]; rows of padding slots are
+ *           unspecified (they are finite)
+ *   lse:    device fp32 [R] natural log, or NULL
+ *   blocks_visited: device uint32 counter the kernel adds the number of
+ *           blocks it computed to (caller zeroes it), or NULL.
+ * softmax_scale must be finite and > 0 (1/sqrt(D) for the usual scale). */
+veda_status veda_block_sparse_attn_fwd(const veda_plan* plan, const void* q, const void* k,
+                                       const void* v_t, const int32_t* row_ptr,
+                                       const int32_t* col_idx, float softmax_scale, void* o,
+                                       float* lse, uint32_t* blocks_visited, void* stream);
+
+/* Teacher block heat from the dense LSE (Key Features > "Veda sparse
+ * attention": teacher block heat from the dense LSE, fused kernel).
+ * heat[i][j] = (1/valid(i)) * sum over valid query slots r of tile i and valid
+ * key slots c of tile j of exp(scale * q_r . k_c - lse[r]), for every pair of
+ * tiles of every head; with the dense LSE each row sums to 1.
+ *   q, k:  device permuted bf16 [R, D];  lse: device fp32 [R]
+ *   heat:  device fp32 [sum_h n_h^2], layout of the scores.
+ * A head may have at most 4096 tiles. */
+veda_status veda_block_heat(const veda_plan* plan, const void* q, const void* k,
+                            const float* lse, float softmax_scale, float* heat, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VEDA_H */
