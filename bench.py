@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload index 1..5 (default: the 16:9 clip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (known bytes) to scale HBM counters")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="rough budget of the oracle sample")
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                            "profiles", "traffic.json"))
@@ -160,6 +162,13 @@ def main():
     for s in range(args.warmup):
         layer.step(s)
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)     # 1 GiB read + 1 GiB written per launch
+        torch.cuda.synchronize()
+        del a, b
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()

@@ -499,6 +499,7 @@ __device__ __forceinline__ void qk_block(const uint16_t* __restrict__ ks, const 
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc, 0, 0, 0);
     }
     sacc[kt] = acc;
+    __builtin_amdgcn_sched_barrier(0);   // keep operand reads of one group together
   }
 }
 
@@ -507,6 +508,68 @@ __device__ __forceinline__ int sacc_key(int kt, int r, int hl) {
   return 32 * kt + 16 * (r >> 3) + 8 * hl + (r & 7);
 }
 
+// LDS synchronisation without the compiler's implicit full memory fences: a
+// wave first waits for its own LDS reads (lgkmcnt) and, where asked, for all
+// but its `pending` newest vector-memory operations (the asynchronous tile
+// copies into LDS), then meets the other waves at s_barrier.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+template <int PENDING>
+__device__ __forceinline__ void dma_sync() {
+  static_assert(PENDING >= 0 && PENDING < 16, "vmcnt field");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070 | PENDING);  // vmcnt(PENDING) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Asynchronous copy of one K tile (rows in pi order, 16-byte chunks
+// XOR-swizzled) straight into LDS: every lane moves 16 bytes per instruction,
+// the wave's 64 chunks land contiguously at a wave-uniform LDS base, so the
+// swizzle is applied on the global side.  Chunk q = it*256 + tid sits in LDS
+// row m = q / CH; with 256 threads that row is it*(256/CH) + tid/CH and its
+// swizzled column does not depend on `it`, so every instruction of a thread
+// reads at one per-thread offset plus a uniform step of 256/CH rows.
+template <int D>
+__device__ __forceinline__ int k_lane_offset() {
+  constexpr int CH = D / 8;
+  const int r = threadIdx.x / CH, pc = threadIdx.x % CH;      // row inside a 256/CH-row step
+  const int c = pc ^ (r & (CH - 1));
+  const int key = (r & ~31) | pi_row(r & 31);
+  return key * D + 8 * c;
+}
+template <int D>
+__device__ __forceinline__ void dma_k_tile(uint16_t* ks, const uint16_t* __restrict__ kg, int lane_off) {
+  constexpr int CH = D / 8;
+  constexpr int STEP = kThreads / CH;           // rows per instruction
+  constexpr int PER = kTile / STEP;
+  static_assert(STEP % 32 == 0 || 32 % STEP == 0, "pi order stays inside one step");
+  const int wbase = threadIdx.x & ~63;
+#pragma unroll
+  for (int it = 0; it < PER; ++it)
+    __builtin_amdgcn_global_load_lds(kg + it * STEP * D + lane_off, ks + 8 * (it * kThreads + wbase), 16, 0, 0);
+}
+__device__ __forceinline__ int vt_lane_offset() {
+  const int r = threadIdx.x / 16, pc = threadIdx.x % 16;
+  return r * kTile + 8 * (pc ^ (r & 15));
+}
+template <int D>
+__device__ __forceinline__ void dma_vt_tile(uint16_t* vs, const uint16_t* __restrict__ vg, int lane_off) {
+  constexpr int PER = D * 16 / kThreads;        // 16 rows of 128 keys per instruction
+  const int wbase = threadIdx.x & ~63;
+#pragma unroll
+  for (int it = 0; it < PER; ++it)
+    __builtin_amdgcn_global_load_lds(vg + it * 16 * kTile + lane_off, vs + 8 * (it * kThreads + wbase), 16, 0, 0);
+}
+
+// Pipelining over a row's key blocks with one K and one V^T buffer: the copy
+// of K(b+1) runs during softmax(b) and PV(b); the copy of V^T(b+1) runs
+// during QK^T(b+1) and softmax(b+1).  Two workgroups share a CU (64 KB of
+// LDS each), so one's waits are covered by the other's MFMA work.
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
@@ -515,18 +578,24 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
                                                               const int32_t* __restrict__ col_idx, float scale_log2,
                                                               uint16_t* __restrict__ o, float* __restrict__ lse,
                                                               uint32_t* __restrict__ visited) {
+  constexpr int PER = kTile * D / 8 / kThreads;  // copy instructions per tile and thread
+  constexpr int kRowList = 2048;
   __shared__ __attribute__((aligned(16))) uint16_t ks[kTile * D];
   __shared__ __attribute__((aligned(16))) uint16_t vs[D * kTile];
+  __shared__ int32_t rowlist[kRowList];
   const int t = p.attn_order[blockIdx.x];
   if (t < 0) return;
   const int h = p.row_head[t];
   const DevShape& sh = p.shape[p.head_shape[h]];
+  const int nt = sh.num_tiles;
   const int i = t - p.head_tile_off[h];
   const int64_t hrow = p.head_row_off[h];
   const int64_t row0 = hrow + (int64_t)kTile * i;
-  const int64_t tile0 = p.head_tile_off[h];
+  const uint16_t* kbase = k + hrow * D;
+  const uint16_t* vbase = vt + (int64_t)p.head_tile_off[h] * D * kTile;
   const int beg = row_ptr[t], end = row_ptr[t + 1];
   const int w = threadIdx.x >> 6, lane = lane_id(), ln = lane & 31, hl = lane >> 5;
+  const int koff = k_lane_offset<D>(), voff = vt_lane_offset();
 
   // Q^T operand: query row 32w + ln, channels 16s + 8hl .. +7
   bf16x8 qf[D / 16];
@@ -539,14 +608,42 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
 
+  // The row's key tiles and their valid counts, staged in LDS as
+  // (tile << 8 | valid) so the loop issues no vector loads besides the tile
+  // copies; rows longer than kRowList refill it at that boundary.
+  auto fill_list = [&](int base) {
+    for (int e = threadIdx.x; e < kRowList && base + e < end; e += kThreads) {
+      const int jj = min(max(col_idx[base + e], 0), nt - 1);   // stay inside the head
+      rowlist[e] = (jj << 8) | sh.valid[jj];
+    }
+  };
+  fill_list(beg);
+  dma_sync<0>();
+  int ent = beg < end ? rowlist[0] : kTile;
+  int j = ent >> 8, nj = ent & 0xff;
+  if (beg < end) {
+    dma_k_tile<D>(ks, kbase + (int64_t)kTile * j * D, koff);
+    dma_vt_tile<D>(vs, vbase + (int64_t)j * D * kTile, voff);
+  }
+  dma_sync<0>();
   for (int b = beg; b < end; ++b) {
-    const int j = min(max(col_idx[b], 0), sh.num_tiles - 1);  // stay inside the head
-    const int nj = sh.valid[j];
-    __syncthreads();
-    load_kv_tile<D>(ks, vs, k + (hrow + (int64_t)kTile * j) * D, vt + (tile0 + j) * (int64_t)D * kTile);
-    __syncthreads();
+    const bool more = b + 1 < end;
+    int jn = 0, njn = kTile;
+    if (more) {
+      const int slot = (b + 1 - beg) % kRowList;
+      if (slot == 0) {   // only rows longer than kRowList blocks get here
+        lds_sync();
+        fill_list(b + 1);
+        dma_sync<0>();
+      }
+      const int en = rowlist[slot];
+      jn = en >> 8;
+      njn = en & 0xff;
+    }
     f32x16 sacc[4];
     qk_block<D>(ks, qf, sacc);
+    lds_sync();                       // every wave is done with K(b)
+    if (more) dma_k_tile<D>(ks, kbase + (int64_t)kTile * jn * D, koff);
     if (nj < kTile) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -564,20 +661,25 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
     m_run = m_new;
+    if (__any(alpha != 1.0f)) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    // per 32-key group: P = exp2(s*c - m), then O^T[d][q] += V^T[d][keys] P^T[keys][q]
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    bf16x8 pb[4][2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      bf16x8 pb[2];
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], scale_log2, -m_new));
         l_run += pv;
-        pb[r >> 3][r & 7] = (__bf16)pv;
+        pb[kt][r >> 3][r & 7] = (__bf16)pv;
       }
+    if (more) dma_sync<PER>(); else dma_sync<0>();   // V^T(b) has landed
+    // O^T[d][q] += V^T[d][keys] P^T[keys][q]
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int c = 4 * kt + 2 * s2 + hl;  // 16-byte chunk of keys in a V^T row
@@ -585,10 +687,17 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
         for (int db = 0; db < D / 32; ++db) {
           const int d = 32 * db + ln;
           const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(vs + d * kTile + 8 * (c ^ (d & 15))));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s2], oacc[db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][s2], oacc[db], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
+    if (more) {
+      lds_sync();                     // every wave is done with V^T(b)
+      dma_vt_tile<D>(vs, vbase + (int64_t)jn * D * kTile, voff);
+      dma_sync<PER>();                // K(b+1) has landed
     }
+    j = jn;
+    nj = njn;
   }
   // epilogue: combine the two lane halves' partial sums, normalise, store
   const float l_all = l_run + __shfl_xor(l_run, 32, 64);
