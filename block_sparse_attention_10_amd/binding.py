@@ -16,7 +16,9 @@ from typing import Dict, Optional, Sequence, Tuple
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libveda.so")
+# VEDA_LIB may point at another build of the same library (e.g. a variant
+# being compared); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("VEDA_LIB") or os.path.join(_PKG, "libveda.so")
 
 VEDA_OK = 0
 VEDA_SEG_VIDEO3D = 0

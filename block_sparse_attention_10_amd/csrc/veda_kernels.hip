@@ -34,6 +34,15 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Values every lane of a workgroup agrees on, moved to scalar registers so
+// address arithmetic and buffer resources built from them stay scalar.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -528,42 +537,58 @@ __device__ __forceinline__ void dma_sync() {
 }
 
 // Asynchronous copy of one K tile (rows in pi order, 16-byte chunks
-// XOR-swizzled) straight into LDS: every lane moves 16 bytes per instruction,
-// the wave's 64 chunks land contiguously at a wave-uniform LDS base, so the
-// swizzle is applied on the global side.  Chunk q = it*256 + tid sits in LDS
-// row m = q / CH; with 256 threads that row is it*(256/CH) + tid/CH and its
-// swizzled column does not depend on `it`, so every instruction of a thread
-// reads at one per-thread offset plus a uniform step of 256/CH rows.
+// XOR-swizzled) straight into LDS through a buffer resource: every lane moves
+// 16 bytes per instruction and the wave's 64 chunks land contiguously at a
+// wave-uniform LDS base (M0), so the swizzle is applied on the global side.
+// Chunk q = it*256 + tid sits in LDS row m = q / CH; with 256 threads that row
+// is it*(256/CH) + tid/CH and its swizzled column does not depend on `it`, so
+// all of a thread's instructions use one byte offset (VGPR) plus a uniform
+// step (SGPR).  The resource covers one head's rows, so the hardware range
+// check keeps every copy inside that head.
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer, dword data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, int64_t bytes) {
+  const int records = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;   // integer compare, stays scalar
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, records, kBufferWord3);
+}
+
 template <int D>
-__device__ __forceinline__ int k_lane_offset() {
+__device__ __forceinline__ int k_lane_offset() {   // bytes
   constexpr int CH = D / 8;
   const int r = threadIdx.x / CH, pc = threadIdx.x % CH;      // row inside a 256/CH-row step
   const int c = pc ^ (r & (CH - 1));
   const int key = (r & ~31) | pi_row(r & 31);
-  return key * D + 8 * c;
+  return 2 * (key * D + 8 * c);
 }
 template <int D>
-__device__ __forceinline__ void dma_k_tile(uint16_t* ks, const uint16_t* __restrict__ kg, int lane_off) {
+__device__ __forceinline__ void dma_k_tile(uint16_t* ks, __amdgpu_buffer_rsrc_t rk, int tile_byte, int lane_off,
+                                           int wave) {
   constexpr int CH = D / 8;
   constexpr int STEP = kThreads / CH;           // rows per instruction
   constexpr int PER = kTile / STEP;
   static_assert(STEP % 32 == 0 || 32 % STEP == 0, "pi order stays inside one step");
-  const int wbase = threadIdx.x & ~63;
 #pragma unroll
   for (int it = 0; it < PER; ++it)
-    __builtin_amdgcn_global_load_lds(kg + it * STEP * D + lane_off, ks + 8 * (it * kThreads + wbase), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, ks + 8 * (it * kThreads + 64 * wave), 16, lane_off,
+                                             tile_byte + it * STEP * D * 2, 0, 0);
 }
-__device__ __forceinline__ int vt_lane_offset() {
+__device__ __forceinline__ int vt_lane_offset() {   // bytes
   const int r = threadIdx.x / 16, pc = threadIdx.x % 16;
-  return r * kTile + 8 * (pc ^ (r & 15));
+  return 2 * (r * kTile + 8 * (pc ^ (r & 15)));
 }
 template <int D>
-__device__ __forceinline__ void dma_vt_tile(uint16_t* vs, const uint16_t* __restrict__ vg, int lane_off) {
+__device__ __forceinline__ void dma_vt_tile(uint16_t* vs, __amdgpu_buffer_rsrc_t rv, int tile_byte, int lane_off,
+                                            int wave) {
   constexpr int PER = D * 16 / kThreads;        // 16 rows of 128 keys per instruction
-  const int wbase = threadIdx.x & ~63;
 #pragma unroll
   for (int it = 0; it < PER; ++it)
-    __builtin_amdgcn_global_load_lds(vg + it * 16 * kTile + lane_off, vs + 8 * (it * kThreads + wbase), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vs + 8 * (it * kThreads + 64 * wave), 16, lane_off,
+                                             tile_byte + it * 16 * kTile * 2, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // Pipelining over a row's key blocks with one K and one V^T buffer: the copy
@@ -583,17 +608,19 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
   __shared__ __attribute__((aligned(16))) uint16_t ks[kTile * D];
   __shared__ __attribute__((aligned(16))) uint16_t vs[D * kTile];
   __shared__ int32_t rowlist[kRowList];
-  const int t = p.attn_order[blockIdx.x];
+  const int t = uni(p.attn_order[blockIdx.x]);
   if (t < 0) return;
-  const int h = p.row_head[t];
-  const DevShape& sh = p.shape[p.head_shape[h]];
+  const int h = uni(p.row_head[t]);
+  const DevShape& sh = p.shape[uni(p.head_shape[h])];
   const int nt = sh.num_tiles;
-  const int i = t - p.head_tile_off[h];
-  const int64_t hrow = p.head_row_off[h];
+  const int i = t - uni(p.head_tile_off[h]);
+  const int64_t hrow = uni64(p.head_row_off[h]);
   const int64_t row0 = hrow + (int64_t)kTile * i;
-  const uint16_t* kbase = k + hrow * D;
-  const uint16_t* vbase = vt + (int64_t)p.head_tile_off[h] * D * kTile;
-  const int beg = row_ptr[t], end = row_ptr[t + 1];
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + hrow * D, (int64_t)nt * kTile * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(vt + (int64_t)uni(p.head_tile_off[h]) * D * kTile,
+                                              (int64_t)nt * kTile * D * 2);
+  const int wave = uni(threadIdx.x >> 6);
+  const int beg = uni(row_ptr[t]), end = uni(row_ptr[t + 1]);
   const int w = threadIdx.x >> 6, lane = lane_id(), ln = lane & 31, hl = lane >> 5;
   const int koff = k_lane_offset<D>(), voff = vt_lane_offset();
 
@@ -619,11 +646,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
   };
   fill_list(beg);
   dma_sync<0>();
-  int ent = beg < end ? rowlist[0] : kTile;
+  int ent = uni(beg < end ? rowlist[0] : kTile);
   int j = ent >> 8, nj = ent & 0xff;
   if (beg < end) {
-    dma_k_tile<D>(ks, kbase + (int64_t)kTile * j * D, koff);
-    dma_vt_tile<D>(vs, vbase + (int64_t)j * D * kTile, voff);
+    dma_k_tile<D>(ks, rk, j * kTile * D * 2, koff, wave);
+    dma_vt_tile<D>(vs, rv, j * kTile * D * 2, voff, wave);
   }
   dma_sync<0>();
   for (int b = beg; b < end; ++b) {
@@ -636,20 +663,27 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
         fill_list(b + 1);
         dma_sync<0>();
       }
-      const int en = rowlist[slot];
+      const int en = uni(rowlist[slot]);
       jn = en >> 8;
       njn = en & 0xff;
     }
     f32x16 sacc[4];
     qk_block<D>(ks, qf, sacc);
     lds_sync();                       // every wave is done with K(b)
-    if (more) dma_k_tile<D>(ks, kbase + (int64_t)kTile * jn * D, koff);
-    if (nj < kTile) {
+    if (more) dma_k_tile<D>(ks, rk, jn * kTile * D * 2, koff, wave);
+    if (nj < kTile) {   // singleton mask rule: key slots >= valid(j) are padding
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 4; ++kt) {
+        if (32 * kt + 32 <= nj) continue;              // group fully valid
+        if (32 * kt >= nj) {                           // group fully padding
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kt][r] = -INFINITY;
+          continue;
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (sacc_key(kt, r, hl) >= nj) sacc[kt][r] = -INFINITY;
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -657,24 +691,35 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
+    // The reference point m only moves up when the block max exceeds it by
+    // more than 2^8 (softmax does not depend on it; p stays <= 256), so the
+    // O rescale is rare.  The first block always sets it.
+    const float mx_s = mx * scale_log2;
+    const float m_new = (mx_s > m_run + 8.0f) ? mx_s : m_run;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
     m_run = m_new;
-    if (__any(alpha != 1.0f)) {
+    if (b > beg && __any(alpha != 1.0f)) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
+    // P = exp2(s*c - m), summed in fp32 and packed to bf16 pairs.
     bf16x8 pb[4][2];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], scale_log2, -m_new));
-        l_run += pv;
-        pb[kt][r >> 3][r & 7] = (__bf16)pv;
+      for (int s2 = 0; s2 < 2; ++s2) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * s2 + 2 * e], scale_log2, -m_new));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * s2 + 2 * e + 1], scale_log2, -m_new));
+          pk[e] = pack_bf16x2(p0, p1);
+          l_run += p0 + p1;
+        }
+        pb[kt][s2] = __builtin_bit_cast(bf16x8, pk);
       }
     if (more) dma_sync<PER>(); else dma_sync<0>();   // V^T(b) has landed
     // O^T[d][q] += V^T[d][keys] P^T[keys][q]
@@ -693,7 +738,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
       }
     if (more) {
       lds_sync();                     // every wave is done with V^T(b)
-      dma_vt_tile<D>(vs, vbase + (int64_t)jn * D * kTile, voff);
+      dma_vt_tile<D>(vs, rv, jn * kTile * D * 2, voff, wave);
       dma_sync<PER>();                // K(b+1) has landed
     }
     j = jn;
