@@ -1,10 +1,11 @@
 """Benchmark of the Veda block-sparse attention layer on one MI355X.
 
 One step = one attention layer through the whole hot path on one batch of
-resident synthetic input: permute Q, K (rows) and V (tile-transposed), score
-tiles (pool + projection + pair scores), select blocks, block-sparse
-attention, inverse permutation of O (plus, for the packed workload, the
-all-blocks forward for the dense LSE and the block heat).  Four seeded input
+resident synthetic input: permute Q, K (rows) and V (tile-transposed) with the
+tile pooling fused in, project and score tile pairs, select blocks, and run
+block-sparse attention whose epilogue writes O back in natural token order
+(plus, for the packed workload, the all-blocks forward for the dense LSE and
+the block heat).  Four seeded input
 sets rotate across steps, so each call sees a new block pattern.
 
 Prints one JSON line.  value = attention FLOP over computed blocks / layer
@@ -57,7 +58,6 @@ class Layer:
         self.ws = p.empty_workspace()
         self.row_ptr = torch.empty(p.T + 1, dtype=torch.int32, device=dev)
         self.col = torch.empty(p.info["nnz"], dtype=torch.int32, device=dev)
-        self.o = p.empty_perm()
         self.lse = torch.empty(p.R, dtype=torch.float32, device=dev)
         self.o_nat = torch.empty((w.num_tokens, w.num_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
         self.dense = None
@@ -73,19 +73,17 @@ class Layer:
     def step(self, s, time_attn=False):
         vb, p, w = self.vb, self.plan, self.w
         x = self.sets[s % len(self.sets)]
-        p.permute(x["q"], self.qp, vb.VEDA_PERMUTE_FORWARD)
-        p.permute(x["k"], self.kp, vb.VEDA_PERMUTE_FORWARD)
-        p.permute(x["v"], self.vt, vb.VEDA_PERMUTE_FORWARD_TRANSPOSED)
-        p.score(self.qp, self.kp, x["w_q"], x["w_k"], self.scores, self.ws)
+        p.permute_qkv(x["q"], x["k"], x["v"], self.qp, self.kp, self.vt, self.ws)
+        p.score_pooled(x["w_q"], x["w_k"], self.scores, self.ws)
         p.select(self.scores, self.row_ptr, self.col)
         if time_attn:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-        p.attention(self.qp, self.kp, self.vt, self.row_ptr, self.col, w.softmax_scale, self.o, self.lse)
+        p.attention(self.qp, self.kp, self.vt, self.row_ptr, self.col, w.softmax_scale, self.o_nat, self.lse,
+                    o_layout=vb.VEDA_LAYOUT_NATURAL)
         if time_attn:
             e1.record()
             self.attn_events.append((e0, e1))
-        p.permute(self.o, self.o_nat, vb.VEDA_PERMUTE_INVERSE)
         if self.dense is not None:
             d = self.dense
             d.select(self.scores, self.d_row_ptr, self.d_col)

@@ -29,6 +29,8 @@ VEDA_BUDGET_ALL = 2
 VEDA_PERMUTE_FORWARD = 0
 VEDA_PERMUTE_INVERSE = 1
 VEDA_PERMUTE_FORWARD_TRANSPOSED = 2
+VEDA_LAYOUT_PERMUTED = 0
+VEDA_LAYOUT_NATURAL = 1
 
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "SHAPE", 3: "UNSUPPORTED", 4: "WORKSPACE",
                 5: "LAUNCH", 6: "STATE"}
@@ -82,8 +84,10 @@ _SIGS = {
     "veda_plan_upload": (_I32, [_P, _P, ctypes.c_size_t, _P]),
     "veda_permute_tiles": (_I32, [_P, _P, _P, _I32, _P]),
     "veda_score_tiles": (_I32, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "veda_permute_qkv": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "veda_score_pooled": (_I32, [_P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "veda_select_blocks": (_I32, [_P, _P, _P, _P, _P, _P]),
-    "veda_block_sparse_attn_fwd": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P]),
+    "veda_block_sparse_attn_fwd": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _P, _P, _P]),
     "veda_block_heat": (_I32, [_P, _P, _P, _P, ctypes.c_float, _P, _P]),
 }
 EXPORTED = tuple(_SIGS)
@@ -218,16 +222,31 @@ def veda_score_tiles(plan: int, q_perm, k_perm, w_q, w_k, scores, workspace, str
                                   _stream(stream)))
 
 
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def veda_permute_qkv(plan: int, q, k, v, q_perm, k_perm, v_t, workspace=None, stream=None) -> None:
+    _check(lib().veda_permute_qkv(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(q_perm), _ptr(k_perm), _ptr(v_t),
+                                  _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def veda_score_pooled(plan: int, w_q, w_k, scores, workspace, stream=None) -> None:
+    _check(lib().veda_score_pooled(plan, _ptr(w_q), _ptr(w_k), _ptr(scores), _ptr(workspace),
+                                   _nbytes(workspace), _stream(stream)))
+
+
 def veda_select_blocks(plan: int, scores, row_ptr, col_idx, dense_mask=None, stream=None) -> None:
     _check(lib().veda_select_blocks(plan, _ptr(scores), _ptr(row_ptr), _ptr(col_idx), _ptr(dense_mask),
                                     _stream(stream)))
 
 
 def veda_block_sparse_attn_fwd(plan: int, q, k, v_t, row_ptr, col_idx, softmax_scale: float, o,
-                               lse=None, blocks_visited=None, stream=None) -> None:
+                               o_layout: int = VEDA_LAYOUT_PERMUTED, lse=None, blocks_visited=None,
+                               stream=None) -> None:
     _check(lib().veda_block_sparse_attn_fwd(plan, _ptr(q), _ptr(k), _ptr(v_t), _ptr(row_ptr), _ptr(col_idx),
-                                            float(softmax_scale), _ptr(o), _ptr(lse), _ptr(blocks_visited),
-                                            _stream(stream)))
+                                            float(softmax_scale), _ptr(o), int(o_layout), _ptr(lse),
+                                            _ptr(blocks_visited), _stream(stream)))
 
 
 def veda_block_heat(plan: int, q, k, lse, softmax_scale: float, heat, stream=None) -> None:
@@ -321,6 +340,32 @@ class Plan:
             self._expect(dst, (self.T, self.D, 128), bf, "dst")
         veda_permute_tiles(self.handle, src, dst, direction, stream)
 
+    def permute_qkv(self, q, k, v, q_perm, k_perm, v_t, workspace=None, stream=None):
+        import torch
+        bf = torch.bfloat16
+        nat = (self.N, self.H, self.D)
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            self._expect(t, nat, bf, n)
+        self._expect(q_perm, (self.R, self.D), bf, "q_perm")
+        self._expect(k_perm, (self.R, self.D), bf, "k_perm")
+        self._expect(v_t, (self.T, self.D, 128), bf, "v_t")
+        if workspace is not None:
+            self._check_workspace(workspace)
+        veda_permute_qkv(self.handle, q, k, v, q_perm, k_perm, v_t, workspace, stream)
+
+    def score_pooled(self, w_q, w_k, scores, workspace, stream=None):
+        import torch
+        self._expect(w_q, (self.H, self.D, 3 * self.D), torch.float32, "w_q")
+        self._expect(w_k, (self.H, self.D, 3 * self.D), torch.float32, "w_k")
+        self._expect(scores, (self.info["total_pairs"],), torch.float32, "scores")
+        self._check_workspace(workspace)
+        veda_score_pooled(self.handle, w_q, w_k, scores, workspace, stream)
+
+    def _check_workspace(self, ws):
+        if ws is None or not ws.is_cuda or not ws.is_contiguous() or _nbytes(ws) < self.info["score_workspace_bytes"]:
+            raise ValueError("workspace must be a contiguous CUDA tensor of >= %d bytes"
+                             % self.info["score_workspace_bytes"])
+
     def score(self, q_perm, k_perm, w_q, w_k, scores, workspace, stream=None):
         import torch
         self._expect(q_perm, (self.R, self.D), torch.bfloat16, "q_perm")
@@ -328,6 +373,7 @@ class Plan:
         self._expect(w_q, (self.H, self.D, 3 * self.D), torch.float32, "w_q")
         self._expect(w_k, (self.H, self.D, 3 * self.D), torch.float32, "w_k")
         self._expect(scores, (self.info["total_pairs"],), torch.float32, "scores")
+        self._check_workspace(workspace)
         veda_score_tiles(self.handle, q_perm, k_perm, w_q, w_k, scores, workspace, stream)
 
     def select(self, scores, row_ptr, col_idx, dense_mask=None, stream=None):
@@ -340,7 +386,7 @@ class Plan:
         veda_select_blocks(self.handle, scores, row_ptr, col_idx, dense_mask, stream)
 
     def attention(self, q, k, v_t, row_ptr, col_idx, scale, o, lse=None, visited=None, stream=None,
-                  nnz=None):
+                  o_layout=VEDA_LAYOUT_PERMUTED):
         import torch
         bf = torch.bfloat16
         self._expect(q, (self.R, self.D), bf, "q")
@@ -349,12 +395,16 @@ class Plan:
         self._expect(row_ptr, (self.T + 1,), torch.int32, "row_ptr")
         if col_idx is None or col_idx.dtype != torch.int32 or not col_idx.is_cuda:
             raise ValueError("col_idx must be an int32 CUDA tensor")
-        self._expect(o, (self.R, self.D), bf, "o")
+        if o_layout == VEDA_LAYOUT_NATURAL:
+            self._expect(o, (self.N, self.H, self.D), bf, "o")
+        else:
+            self._expect(o, (self.R, self.D), bf, "o")
         if lse is not None:
             self._expect(lse, (self.R,), torch.float32, "lse")
         if visited is not None:
             self._expect(visited, (1,), torch.int32, "blocks_visited")
-        veda_block_sparse_attn_fwd(self.handle, q, k, v_t, row_ptr, col_idx, scale, o, lse, visited, stream)
+        veda_block_sparse_attn_fwd(self.handle, q, k, v_t, row_ptr, col_idx, scale, o, o_layout, lse, visited,
+                                   stream)
 
     def heat(self, q, k, lse, scale, heat, stream=None):
         import torch

@@ -601,6 +601,42 @@ veda_status veda_score_tiles(const veda_plan* p, const void* q_perm, const void*
                   "score");
 }
 
+veda_status veda_permute_qkv(const veda_plan* p, const void* q, const void* k, const void* v, void* q_perm,
+                             void* k_perm, void* v_t, void* workspace, size_t workspace_bytes, void* stream) {
+  veda_status st = check_plan_ready(p);
+  if (st) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(q_perm, "q_perm")) || (st = check_ptr(k_perm, "k_perm")) || (st = check_ptr(v_t, "v_t")))
+    return st;
+  const void* ins[3] = {q, k, v};
+  void* outs[3] = {q_perm, k_perm, v_t};
+  for (int a = 0; a < 3; ++a)
+    for (int b = 0; b < 3; ++b)
+      if (ins[a] == outs[b]) return fail(VEDA_ERR_INVALID_ARG, "an input aliases an output");
+  if (workspace) {
+    if ((st = check_ptr(workspace, "workspace"))) return st;
+    if ((int64_t)workspace_bytes < p->info.score_workspace_bytes)
+      return fail(VEDA_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
+                  (long long)p->info.score_workspace_bytes);
+  }
+  return launched(launch_permute_qkv(p->dev, q, k, v, q_perm, k_perm, v_t, workspace, (hipStream_t)stream),
+                  "permute qkv");
+}
+
+veda_status veda_score_pooled(const veda_plan* p, const float* w_q, const float* w_k, float* scores,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  veda_status st = check_plan_ready(p);
+  if (st) return st;
+  if ((st = check_ptr(w_q, "w_q")) || (st = check_ptr(w_k, "w_k")) || (st = check_ptr(scores, "scores")))
+    return st;
+  if (!workspace) return fail(VEDA_ERR_WORKSPACE, "workspace is NULL");
+  if ((st = check_ptr(workspace, "workspace"))) return st;
+  if ((int64_t)workspace_bytes < p->info.score_workspace_bytes)
+    return fail(VEDA_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
+                (long long)p->info.score_workspace_bytes);
+  return launched(launch_score_pooled(p->dev, w_q, w_k, scores, workspace, (hipStream_t)stream), "score pooled");
+}
+
 veda_status veda_select_blocks(const veda_plan* p, const float* scores, int32_t* row_ptr, int32_t* col_idx,
                                uint8_t* dense_mask, void* stream) {
   veda_status st = check_plan_ready(p);
@@ -614,7 +650,8 @@ veda_status veda_select_blocks(const veda_plan* p, const float* scores, int32_t*
 
 veda_status veda_block_sparse_attn_fwd(const veda_plan* p, const void* q, const void* k, const void* v_t,
                                        const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
-                                       void* o, float* lse, uint32_t* blocks_visited, void* stream) {
+                                       void* o, int32_t o_layout, float* lse, uint32_t* blocks_visited,
+                                       void* stream) {
   veda_status st = check_plan_ready(p);
   if (st) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v_t, "v_t")) ||
@@ -625,8 +662,11 @@ veda_status veda_block_sparse_attn_fwd(const veda_plan* p, const void* q, const 
     return fail(VEDA_ERR_INVALID_ARG, "blocks_visited is not 4-byte aligned");
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
     return fail(VEDA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
-  return launched(launch_attn_fwd(p->dev, q, k, v_t, row_ptr, col_idx, softmax_scale, o, lse, blocks_visited,
-                                  (hipStream_t)stream),
+  if (o_layout != VEDA_LAYOUT_PERMUTED && o_layout != VEDA_LAYOUT_NATURAL)
+    return fail(VEDA_ERR_INVALID_ARG, "unknown o_layout %d", o_layout);
+  if (o == q || o == k || o == v_t) return fail(VEDA_ERR_INVALID_ARG, "o aliases an input");
+  return launched(launch_attn_fwd(p->dev, q, k, v_t, row_ptr, col_idx, softmax_scale, o,
+                                  o_layout == VEDA_LAYOUT_NATURAL, lse, blocks_visited, (hipStream_t)stream),
                   "block-sparse attention");
 }
 

@@ -53,11 +53,15 @@ hipError_t launch_permute(const DevPlan& p, const void* src, void* dst, int dire
                           hipStream_t s);
 hipError_t launch_score(const DevPlan& p, const void* q, const void* k, const float* wq,
                         const float* wk, float* scores, void* ws, hipStream_t s);
+hipError_t launch_permute_qkv(const DevPlan& p, const void* q, const void* k, const void* v, void* qp,
+                              void* kp, void* vt, void* ws, hipStream_t s);
+hipError_t launch_score_pooled(const DevPlan& p, const float* wq, const float* wk, float* scores,
+                               void* ws, hipStream_t s);
 hipError_t launch_select(const DevPlan& p, const float* scores, int32_t* row_ptr,
                          int32_t* col_idx, uint8_t* dense_mask, hipStream_t s);
 hipError_t launch_attn_fwd(const DevPlan& p, const void* q, const void* k, const void* vt,
                            const int32_t* row_ptr, const int32_t* col_idx, float scale,
-                           void* o, float* lse, uint32_t* visited, hipStream_t s);
+                           void* o, int o_natural, float* lse, uint32_t* visited, hipStream_t s);
 hipError_t launch_heat(const DevPlan& p, const void* q, const void* k, const float* lse,
                        float scale, float* heat, hipStream_t s);
 

@@ -115,6 +115,111 @@ __global__ void __launch_bounds__(kThreads) permute_vt_kernel(DevPlan p, const u
   }
 }
 
+// Forward permutation of Q, K and V in one launch, with the pooling of Q and
+// K fused in.  Workgroup (tile t, tensor y); thread (cb, sb) owns channels
+// 8cb..8cb+7 of slots 8sb..8sb+7: it gathers those eight 16-byte pieces of
+// natural rows (the 16 threads sharing sb read whole 256-byte rows), then
+//  - Q, K: writes them as permuted rows and keeps fp64 sums / max / min of
+//    the valid ones, combined over sb through LDS in a fixed order;
+//  - V:    transposes the 8x8 block in registers and writes 8 rows of the
+//    tile-transposed layout.
+template <int D>
+__global__ void __launch_bounds__(D * 2) permute_qkv_kernel(DevPlan p, const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ v, uint16_t* __restrict__ qp,
+                                                           uint16_t* __restrict__ kp, uint16_t* __restrict__ vt,
+                                                           float* __restrict__ feat_q, float* __restrict__ feat_k) {
+  constexpr int CB = D / 8;     // channel chunks
+  constexpr int SB = 16;        // slot chunks of 8
+  __shared__ double s_sum[SB][D];
+  __shared__ float s_max[SB][D];
+  __shared__ float s_min[SB][D];
+  const int64_t t = blockIdx.x;
+  const int y = blockIdx.y;
+  const int cb = threadIdx.x % CB, sb = threadIdx.x / CB;
+  const int h = uni(p.row_head[t]);
+  const DevShape& sh = p.shape[uni(p.head_shape[h])];
+  const int i = (int)(t - uni(p.head_tile_off[h]));
+  const int nv = sh.valid[i];
+  const int H = p.num_heads;
+  const uint16_t* src = y == 0 ? q : (y == 1 ? k : v);
+  // the eight slot -> token entries of this thread (two 16-byte reads), then
+  // eight independent gathers; padding slots read token 0 and are zeroed
+  const u32x4 pa = ld16(sh.perm + (int64_t)kTile * i + 8 * sb);
+  const u32x4 pb = ld16(sh.perm + (int64_t)kTile * i + 8 * sb + 4);
+  const int32_t toks[8] = {(int32_t)pa[0], (int32_t)pa[1], (int32_t)pa[2], (int32_t)pa[3],
+                           (int32_t)pb[0], (int32_t)pb[1], (int32_t)pb[2], (int32_t)pb[3]};
+  u32x4 blk[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int32_t tk = toks[e] >= 0 ? toks[e] : 0;
+    blk[e] = ld16(src + ((int64_t)tk * H + h) * D + 8 * cb);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (toks[e] < 0) blk[e] = u32x4{0u, 0u, 0u, 0u};
+  if (y == 2) {
+    uint16_t* out = vt + t * (int64_t)D * kTile;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {           // channel 8cb + c
+      uint32_t wv[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t a = blk[2 * m][c >> 1], b = blk[2 * m + 1][c >> 1];
+        wv[m] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+      }
+      st16(out + (int64_t)(8 * cb + c) * kTile + 8 * sb, u32x4{wv[0], wv[1], wv[2], wv[3]});
+    }
+    return;
+  }
+  uint16_t* dst = y == 0 ? qp : kp;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) st16(dst + (t * kTile + 8 * sb + e) * D + 8 * cb, blk[e]);
+  float* feat = y == 0 ? feat_q : feat_k;
+  if (!feat) return;
+  double sum[8];
+  float mx[8], mn[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    sum[c] = 0.0;
+    mx[c] = -INFINITY;
+    mn[c] = INFINITY;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (8 * sb + e >= nv) continue;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t wd = blk[e][c >> 1];
+      const float x = __uint_as_float((c & 1) ? (wd & 0xffff0000u) : (wd << 16));
+      sum[c] += (double)x;
+      mx[c] = fmaxf(mx[c], x);
+      mn[c] = fminf(mn[c], x);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    s_sum[sb][8 * cb + c] = sum[c];
+    s_max[sb][8 * cb + c] = mx[c];
+    s_min[sb][8 * cb + c] = mn[c];
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    double tot = 0.0;
+    float a = -INFINITY, b = INFINITY;
+    for (int r = 0; r < SB; ++r) {
+      tot += s_sum[r][d];
+      a = fmaxf(a, s_max[r][d]);
+      b = fminf(b, s_min[r][d]);
+    }
+    float* out = feat + t * (int64_t)(3 * D);
+    out[d] = (float)(tot / (double)nv);
+    out[D + d] = a;
+    out[2 * D + d] = b;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // predictor: pool, project, score
 // ---------------------------------------------------------------------------
@@ -200,7 +305,7 @@ __global__ void __launch_bounds__(kThreads) project_kernel(DevPlan p, const floa
   constexpr int E = 3 * D;
   constexpr int G = kThreads / D;           // tile groups
   constexpr int TPT = kProjTiles / G;       // tiles per thread
-  __shared__ float f[kProjTiles][E];
+  __shared__ __attribute__((aligned(16))) float f[kProjTiles][E];
   const int h = blockIdx.y;
   const DevShape& sh = p.shape[p.head_shape[h]];
   const int n = sh.num_tiles;
@@ -211,20 +316,51 @@ __global__ void __launch_bounds__(kThreads) project_kernel(DevPlan p, const floa
   const float* feat = blockIdx.z ? feat_k : feat_q;
   float* hat = blockIdx.z ? hat_k : hat_q;
   const int64_t t0 = p.head_tile_off[h] + i0;
-  for (int q = threadIdx.x; q < kProjTiles * E; q += kThreads) {
-    const int r = q / E;
-    f[r][q % E] = r < cnt ? feat[(t0 + r) * E + q % E] : 0.0f;
+  {   // features of the chunk's tiles, 16-byte loads all in flight together
+    constexpr int V4 = kProjTiles * E / 4 / kThreads;
+    float4 buf[V4];
+#pragma unroll
+    for (int u = 0; u < V4; ++u) {
+      const int q4 = u * kThreads + threadIdx.x;
+      const int r = (4 * q4) / E;
+      buf[u] = r < cnt ? *reinterpret_cast<const float4*>(feat + (t0 + r) * E + (4 * q4) % E)
+                       : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < V4; ++u) {
+      const int q4 = u * kThreads + threadIdx.x;
+      *reinterpret_cast<float4*>(&f[(4 * q4) / E][(4 * q4) % E]) = buf[u];
+    }
   }
   __syncthreads();
   const int d = threadIdx.x % D, grp = threadIdx.x / D;
   double acc[TPT];
 #pragma unroll
   for (int u = 0; u < TPT; ++u) acc[u] = (double)f[grp * TPT + u][d];
-  const float* wr = W + (int64_t)d * E;
-  for (int e = 0; e < E; ++e) {
-    const double w = (double)wr[e];
+  // W[h][d][:] streamed in 16-float chunks, the next chunk in flight while
+  // the current one is used; the sum order stays e = 0, 1, ..., 3D-1.
+  const float4* wr = reinterpret_cast<const float4*>(W + (int64_t)d * E);
+  float4 cur[4], nxt[4];
 #pragma unroll
-    for (int u = 0; u < TPT; ++u) acc[u] = fma(w, (double)f[grp * TPT + u][e], acc[u]);
+  for (int u = 0; u < 4; ++u) cur[u] = wr[u];
+  for (int e0 = 0; e0 < E; e0 += 16) {
+    if (e0 + 16 < E) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) nxt[u] = wr[(e0 + 16) / 4 + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wv[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = e0 + 4 * u + c;
+        const double wd = (double)wv[c];
+#pragma unroll
+        for (int tt = 0; tt < TPT; ++tt) acc[tt] = fma(wd, (double)f[grp * TPT + tt][e], acc[tt]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
   }
 #pragma unroll
   for (int u = 0; u < TPT; ++u) {
@@ -601,8 +737,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
                                                               const uint16_t* __restrict__ vt,
                                                               const int32_t* __restrict__ row_ptr,
                                                               const int32_t* __restrict__ col_idx, float scale_log2,
-                                                              uint16_t* __restrict__ o, float* __restrict__ lse,
-                                                              uint32_t* __restrict__ visited) {
+                                                              uint16_t* __restrict__ o, int o_natural,
+                                                              float* __restrict__ lse, uint32_t* __restrict__ visited) {
   constexpr int PER = kTile * D / 8 / kThreads;  // copy instructions per tile and thread
   constexpr int kRowList = 2048;
   __shared__ __attribute__((aligned(16))) uint16_t ks[kTile * D];
@@ -747,7 +883,15 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
   // epilogue: combine the two lane halves' partial sums, normalise, store
   const float l_all = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_all;
+  // permuted: row row0 + slot; natural: the slot's token, padding dropped
   uint16_t* orow = o + (row0 + 32 * w + ln) * D;
+  bool store = true;
+  if (o_natural) {
+    const int slot = 32 * w + ln;
+    const int32_t tok = sh.perm[(int64_t)kTile * i + slot];
+    store = tok >= 0;
+    orow = o + ((int64_t)(store ? tok : 0) * p.num_heads + h) * D;
+  }
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -760,7 +904,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
       uint2 v;
       v.x = __builtin_bit_cast(uint32_t, lo);
       v.y = __builtin_bit_cast(uint32_t, hi);
-      *reinterpret_cast<uint2*>(orow + 32 * db + 8 * jj + 4 * hl) = v;
+      if (store) *reinterpret_cast<uint2*>(orow + 32 * db + 8 * jj + 4 * hl) = v;
     }
   if (lse && hl == 0) lse[row0 + 32 * w + ln] = m_run * 0.69314718055994531f + logf(l_all);
   if (visited && threadIdx.x == 0) atomicAdd(visited, (uint32_t)(end - beg));
@@ -855,8 +999,28 @@ hipError_t launch_permute(const DevPlan& p, const void* src, void* dst, int dire
   return hipGetLastError();
 }
 
-hipError_t launch_score(const DevPlan& p, const void* q, const void* k, const float* wq, const float* wk,
-                        float* scores, void* ws, hipStream_t s) {
+hipError_t launch_permute_qkv(const DevPlan& p, const void* q, const void* k, const void* v, void* qp, void* kp,
+                              void* vt, void* ws, hipStream_t s) {
+  const int D = p.head_dim;
+  const int64_t T = p.total_tiles;
+  float* feat_q = ws ? static_cast<float*>(ws) : nullptr;
+  float* feat_k = ws ? feat_q + T * 3 * D : nullptr;
+  const dim3 grid((unsigned)T, 3);
+  auto cq = static_cast<const uint16_t*>(q);
+  auto ck = static_cast<const uint16_t*>(k);
+  auto cv = static_cast<const uint16_t*>(v);
+  auto oq = static_cast<uint16_t*>(qp);
+  auto ok = static_cast<uint16_t*>(kp);
+  auto ov = static_cast<uint16_t*>(vt);
+  if (D == 128)
+    hipLaunchKernelGGL(permute_qkv_kernel<128>, grid, dim3(256), 0, s, p, cq, ck, cv, oq, ok, ov, feat_q, feat_k);
+  else
+    hipLaunchKernelGGL(permute_qkv_kernel<64>, grid, dim3(128), 0, s, p, cq, ck, cv, oq, ok, ov, feat_q, feat_k);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_pooled(const DevPlan& p, const float* wq, const float* wk, float* scores, void* ws,
+                               hipStream_t s) {
   const int D = p.head_dim;
   const int64_t T = p.total_tiles;
   float* feat_q = static_cast<float*>(ws);
@@ -865,21 +1029,34 @@ hipError_t launch_score(const DevPlan& p, const void* q, const void* k, const fl
   float* hat_k = hat_q + T * D;
   int maxn = 0;
   for (int g = 0; g < p.num_shapes; ++g) maxn = maxn > p.shape[g].num_tiles ? maxn : p.shape[g].num_tiles;
-  const uint16_t* qq = static_cast<const uint16_t*>(q);
-  const uint16_t* kk = static_cast<const uint16_t*>(k);
-  const dim3 gpool((unsigned)T, 2);
   const dim3 gproj((unsigned)((maxn + kProjTiles - 1) / kProjTiles), (unsigned)p.num_heads, 2);
   const dim3 gscore((unsigned)((maxn + 63) / 64), (unsigned)((maxn + 63) / 64), (unsigned)p.num_heads);
   if (D == 128) {
-    hipLaunchKernelGGL(pool_kernel<128>, gpool, dim3(kThreads), 0, s, p, qq, kk, feat_q, feat_k);
     hipLaunchKernelGGL(project_kernel<128>, gproj, dim3(kThreads), 0, s, p, wq, wk, feat_q, feat_k, hat_q, hat_k);
     hipLaunchKernelGGL(score_kernel<128>, gscore, dim3(kThreads), 0, s, p, hat_q, hat_k, scores);
   } else {
-    hipLaunchKernelGGL(pool_kernel<64>, gpool, dim3(kThreads), 0, s, p, qq, kk, feat_q, feat_k);
     hipLaunchKernelGGL(project_kernel<64>, gproj, dim3(kThreads), 0, s, p, wq, wk, feat_q, feat_k, hat_q, hat_k);
     hipLaunchKernelGGL(score_kernel<64>, gscore, dim3(kThreads), 0, s, p, hat_q, hat_k, scores);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_score(const DevPlan& p, const void* q, const void* k, const float* wq, const float* wk,
+                        float* scores, void* ws, hipStream_t s) {
+  const int D = p.head_dim;
+  const int64_t T = p.total_tiles;
+  float* feat_q = static_cast<float*>(ws);
+  float* feat_k = feat_q + T * 3 * D;
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const dim3 gpool((unsigned)T, 2);
+  if (D == 128)
+    hipLaunchKernelGGL(pool_kernel<128>, gpool, dim3(kThreads), 0, s, p, qq, kk, feat_q, feat_k);
+  else
+    hipLaunchKernelGGL(pool_kernel<64>, gpool, dim3(kThreads), 0, s, p, qq, kk, feat_q, feat_k);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_score_pooled(p, wq, wk, scores, ws, s);
 }
 
 hipError_t launch_select(const DevPlan& p, const float* scores, int32_t* row_ptr, int32_t* col_idx,
@@ -890,8 +1067,8 @@ hipError_t launch_select(const DevPlan& p, const float* scores, int32_t* row_ptr
 }
 
 hipError_t launch_attn_fwd(const DevPlan& p, const void* q, const void* k, const void* vt, const int32_t* row_ptr,
-                           const int32_t* col_idx, float scale, void* o, float* lse, uint32_t* visited,
-                           hipStream_t s) {
+                           const int32_t* col_idx, float scale, void* o, int o_natural, float* lse,
+                           uint32_t* visited, hipStream_t s) {
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid((unsigned)p.attn_grid);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
@@ -900,10 +1077,10 @@ hipError_t launch_attn_fwd(const DevPlan& p, const void* q, const void* k, const
   uint16_t* oo = static_cast<uint16_t*>(o);
   if (p.head_dim == 128)
     hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
-                       scale_log2, oo, lse, visited);
+                       scale_log2, oo, o_natural, lse, visited);
   else
     hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
-                       scale_log2, oo, lse, visited);
+                       scale_log2, oo, o_natural, lse, visited);
   return hipGetLastError();
 }
 

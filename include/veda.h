@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define VEDA_ABI_VERSION 1
+#define VEDA_ABI_VERSION 2
 
 typedef int32_t veda_status;
 enum {
@@ -78,6 +78,9 @@ enum { VEDA_SEG_VIDEO3D = 0, VEDA_SEG_DENSE1D = 1 };
  * fixed_k key tiles per query tile and key segment.  ALL: every block (dense
  * attention through the same kernel; used for the dense LSE). */
 enum { VEDA_BUDGET_KEEP_RATIO = 0, VEDA_BUDGET_FIXED_K = 1, VEDA_BUDGET_ALL = 2 };
+
+/* Layouts of the attention output O. */
+enum { VEDA_LAYOUT_PERMUTED = 0, VEDA_LAYOUT_NATURAL = 1 };
 
 /* Directions of veda_permute_tiles. */
 enum {
@@ -177,6 +180,23 @@ veda_status veda_plan_upload(veda_plan* plan, void* dev_tables, size_t bytes, vo
 veda_status veda_permute_tiles(const veda_plan* plan, const void* src, void* dst,
                                int32_t direction, void* stream);
 
+/* The three forward permutations of one attention layer in one pass, with
+ * the predictor's pooling fused in: q -> q_perm and k -> k_perm (permuted
+ * rows), v -> v_t (tile-transposed), each read once from HBM; while a tile of
+ * Q or K is in flight its mean (fp64 sum), max and min over the valid slots
+ * are written to `workspace` (fp32 [T, 3D] for Q, then for K), where
+ * veda_score_pooled picks them up.  Outputs are bit-identical to three
+ * veda_permute_tiles calls.  workspace may be NULL (no pooling); otherwise it
+ * must hold score_workspace_bytes. */
+veda_status veda_permute_qkv(const veda_plan* plan, const void* q, const void* k, const void* v,
+                             void* q_perm, void* k_perm, void* v_t, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Projection and pair scores from the pooled features that veda_permute_qkv
+ * left in `workspace`; same results as veda_score_tiles on the permuted Q/K. */
+veda_status veda_score_pooled(const veda_plan* plan, const float* w_q, const float* w_k, float* scores,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* The predictor (Key Features > "Veda sparse attention": mean/max/min pooling
  * plus a per-head residual projection; "Sparse acceleration (Veda)": scores
  * of (query tile, key tile) pairs).  For every tile, over its valid slots only:
@@ -216,16 +236,20 @@ veda_status veda_select_blocks(const veda_plan* plan, const float* scores, int32
  *   v_t:    device tile-transposed bf16 [T, D, 128]
  *   row_ptr, col_idx: device CSR as written by veda_select_blocks (or any CSR
  *           of this plan's shape with ascending, in-range, non-empty rows)
- *   o:      device permuted bf16 [R, D]; rows of padding slots are
- *           unspecified (they are finite)
- *   lse:    device fp32 [R] natural log, or NULL
+ *   o:      device bf16; o_layout VEDA_LAYOUT_PERMUTED: [R, D], rows of
+ *           padding slots unspecified (finite); VEDA_LAYOUT_NATURAL:
+ *           [N, H, D], every token of head h written at its natural place
+ *           (the inverse permutation fused into the epilogue), padding
+ *           slots dropped
+ *   lse:    device fp32 [R] natural log, permuted row order, or NULL
  *   blocks_visited: device uint32 counter the kernel adds the number of
  *           blocks it computed to (caller zeroes it), or NULL.
  * softmax_scale must be finite and > 0 (1/sqrt(D) for the usual scale). */
 veda_status veda_block_sparse_attn_fwd(const veda_plan* plan, const void* q, const void* k,
                                        const void* v_t, const int32_t* row_ptr,
                                        const int32_t* col_idx, float softmax_scale, void* o,
-                                       float* lse, uint32_t* blocks_visited, void* stream);
+                                       int32_t o_layout, float* lse, uint32_t* blocks_visited,
+                                       void* stream);
 
 /* Teacher block heat from the dense LSE (Key Features > "Veda sparse
  * attention": teacher block heat from the dense LSE, fused kernel).

@@ -9,29 +9,44 @@ from block_sparse_attention_10_amd import binding as vb
 from oracle import veda_oracle as vo
 
 
-def gpu_path(w, inp, budget_mode=None, dense_mask=True):
-    """All calls of the hot path on cuda:0; returns a dict of device tensors."""
+def gpu_path(w, inp, budget_mode=None, dense_mask=True, fused=True):
+    """All calls of the hot path on cuda:0; returns a dict of device tensors.
+
+    fused=True: veda_permute_qkv (permutes + pooling) -> veda_score_pooled ->
+    select -> attention writing O in natural order (the layout bench.py runs).
+    fused=False: one veda_permute_tiles per tensor -> veda_score_tiles ->
+    select -> attention into permuted rows -> veda_permute_tiles(INVERSE).
+    """
     plan = vb.Plan.from_workload(w, budget_mode=budget_mode)
     dev = "cuda"
     q, k, v = inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev)
     wq, wk = inp["w_q"].to(dev), inp["w_k"].to(dev)
     qp, kp, vt = plan.empty_perm(), plan.empty_perm(), plan.empty_vt()
-    plan.permute(q, qp, vb.VEDA_PERMUTE_FORWARD)
-    plan.permute(k, kp, vb.VEDA_PERMUTE_FORWARD)
-    plan.permute(v, vt, vb.VEDA_PERMUTE_FORWARD_TRANSPOSED)
     scores = torch.empty(plan.info["total_pairs"], dtype=torch.float32, device=dev)
     ws = plan.empty_workspace()
-    plan.score(qp, kp, wq, wk, scores, ws)
+    if fused:
+        plan.permute_qkv(q, k, v, qp, kp, vt, ws)
+        plan.score_pooled(wq, wk, scores, ws)
+    else:
+        plan.permute(q, qp, vb.VEDA_PERMUTE_FORWARD)
+        plan.permute(k, kp, vb.VEDA_PERMUTE_FORWARD)
+        plan.permute(v, vt, vb.VEDA_PERMUTE_FORWARD_TRANSPOSED)
+        plan.score(qp, kp, wq, wk, scores, ws)
     row_ptr = torch.empty(plan.T + 1, dtype=torch.int32, device=dev)
     col = torch.empty(plan.info["nnz"], dtype=torch.int32, device=dev)
     dm = torch.empty(plan.info["total_pairs"], dtype=torch.uint8, device=dev) if dense_mask else None
     plan.select(scores, row_ptr, col, dm)
-    o = plan.empty_perm()
     lse = torch.empty(plan.R, dtype=torch.float32, device=dev)
     visited = torch.zeros(1, dtype=torch.int32, device=dev)
-    plan.attention(qp, kp, vt, row_ptr, col, w.softmax_scale, o, lse, visited)
     o_nat = torch.zeros((w.num_tokens, w.num_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
-    plan.permute(o, o_nat, vb.VEDA_PERMUTE_INVERSE)
+    if fused:
+        plan.attention(qp, kp, vt, row_ptr, col, w.softmax_scale, o_nat, lse, visited,
+                       o_layout=vb.VEDA_LAYOUT_NATURAL)
+        o = None
+    else:
+        o = plan.empty_perm()
+        plan.attention(qp, kp, vt, row_ptr, col, w.softmax_scale, o, lse, visited)
+        plan.permute(o, o_nat, vb.VEDA_PERMUTE_INVERSE)
     torch.cuda.synchronize()
     return dict(plan=plan, q_perm=qp, k_perm=kp, v_t=vt, scores=scores, row_ptr=row_ptr, col_idx=col,
                 dense_mask=dm, o=o, lse=lse, visited=visited, o_nat=o_nat)

@@ -69,17 +69,21 @@ def check_front(w, inp, g, rows=None):
 
 
 def check_attention(w, inp, g, op, qp, kp, sel, rows=None):
+    """O (in natural order, or permuted rows when the path produced them) and
+    LSE against the oracle over valid rows; visited blocks == nnz."""
     vp = vo.permute_forward(op, gp.f64(inp["v"]))
     O, L = vo.block_sparse_attention(op, qp, kp, vp, sel, w.softmax_scale, rows=rows)
     vr = gp.valid_rows(op)
     vr = vr[~np.isnan(L[vr])]
-    o_gpu = gp.f64(g["o"])
+    if g["o"] is not None:
+        o_gpu = gp.f64(g["o"])
+    else:   # natural-order output: bring it to permuted rows with the oracle's permutation
+        o_gpu = vo.permute_forward(op, gp.f64(g["o_nat"]))
     max_abs, rel = gp.attn_errors(o_gpu, O, vr)
     lse_err = float(np.max(np.abs(g["lse"].cpu().numpy().astype(np.float64)[vr] - L[vr])))
     print("%s: rows=%d max_abs=%.3e rel_l2=%.3e lse=%.3e" % (w.name, len(vr), max_abs, rel, lse_err), flush=True)
     assert max_abs <= gp.MAX_ABS and rel <= gp.REL_L2 and lse_err <= gp.LSE_ABS
     assert int(g["visited"].item()) == op_nnz(op, sel)
-    # the inverse permutation puts every valid row back in natural order
     if rows is None:
         on = vo.permute_inverse(op, np.nan_to_num(O))
         got = gp.f64(g["o_nat"])
@@ -90,10 +94,11 @@ def op_nnz(op, sel):
     return sum(len(r) for rows in sel for r in rows)
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "separate"])
 @pytest.mark.parametrize("w", small_workloads(), ids=lambda w: w.name)
-def test_small_workloads(w):
+def test_small_workloads(w, fused):
     inp = wl.make_inputs(w, seed=w.index)
-    g = gp.gpu_path(w, inp)
+    g = gp.gpu_path(w, inp, fused=fused)
     op, qp, kp, sel = check_front(w, inp, g)
     check_attention(w, inp, g, op, qp, kp, sel)
 
@@ -105,6 +110,23 @@ def test_config_full(idx):
     g = gp.gpu_path(w, inp)
     op, qp, kp, sel = check_front(w, inp, g)
     check_attention(w, inp, g, op, qp, kp, sel)
+
+
+def test_config2_separate_calls():
+    w = wl.workload(2)
+    inp = wl.make_inputs(w)
+    g = gp.gpu_path(w, inp, fused=False)
+    op, qp, kp, sel = check_front(w, inp, g)
+    check_attention(w, inp, g, op, qp, kp, sel)
+
+
+def test_fused_equals_separate_bitwise():
+    w = wl.workload(3)
+    inp = wl.make_inputs(w)
+    a = gp.gpu_path(w, inp, fused=True)
+    b = gp.gpu_path(w, inp, fused=False)
+    for key in ("q_perm", "k_perm", "v_t", "scores", "col_idx", "lse", "o_nat"):
+        assert torch.equal(a[key], b[key]), key
 
 
 def test_config5_packed_sampled_rows():
@@ -136,7 +158,7 @@ def test_deterministic_bitwise():
     inp = wl.make_inputs(w)
     a = gp.gpu_path(w, inp)
     b = gp.gpu_path(w, inp)
-    for key in ("scores", "col_idx", "o", "lse"):
+    for key in ("scores", "col_idx", "o_nat", "lse"):
         assert torch.equal(a[key], b[key]), key
 
 
@@ -202,14 +224,15 @@ def test_config4_long_clip_sampled():
             assert np.array_equal(col_g[rp_g[t0 + i]:rp_g[t0 + i + 1]], sel[a][i])
         rows += [(a, i) for i in sel_rows[a]]
     O, L = vo.block_sparse_attention(sub, qp, kp, vp, sel, w.softmax_scale, rows=rows)
-    o_gpu = gp.f64(g["o"])
+    o_nat = gp.f64(g["o_nat"])
     lse_gpu = g["lse"].cpu().numpy()
     for a, i in rows:
         h = heads[a]
         n, r0, t0, p0 = vb.veda_plan_head(plan.handle, h)
         nv = sub.heads[a].tiles[i].valid
         ref = O[sub.row_offset[a] + 128 * i: sub.row_offset[a] + 128 * i + nv]
-        got = o_gpu[r0 + 128 * i: r0 + 128 * i + nv]
+        toks = sub.heads[a].perm()[128 * i: 128 * i + nv]
+        got = o_nat[toks, h]
         assert np.max(np.abs(got - ref)) <= gp.MAX_ABS
         assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= gp.REL_L2
         lref = L[sub.row_offset[a] + 128 * i: sub.row_offset[a] + 128 * i + nv]
@@ -229,7 +252,10 @@ def test_error_paths_on_device():
     assert lib.veda_permute_tiles(plan.handle, buf.data_ptr() + 2, buf.data_ptr() + 4096, 0, None) == 1
     assert lib.veda_block_sparse_attn_fwd(plan.handle, buf.data_ptr(), buf.data_ptr(), buf.data_ptr(),
                                           buf.data_ptr(), buf.data_ptr(), ctypes.c_float(float("nan")),
-                                          buf.data_ptr(), None, None, None) == 1
+                                          buf.data_ptr(), 0, None, None, None) == 1
+    assert lib.veda_block_sparse_attn_fwd(plan.handle, buf.data_ptr(), buf.data_ptr(), buf.data_ptr(),
+                                          buf.data_ptr(), buf.data_ptr(), ctypes.c_float(0.125),
+                                          buf.data_ptr() + 8192, 7, None, None, None) == 1
     assert lib.veda_score_tiles(plan.handle, buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(),
                                 buf.data_ptr(), buf.data_ptr(), 16, None) == 4
     with pytest.raises(vb.VedaError):
