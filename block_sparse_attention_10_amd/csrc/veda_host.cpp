@@ -185,8 +185,20 @@ void build_attn_order(veda_plan& p) {
     std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
       return (p.row_ptr[x + 1] - p.row_ptr[x]) > (p.row_ptr[y + 1] - p.row_ptr[y]);
     });
+    p.attn_order = order;
+    return;
   }
-  p.attn_order = order;
+  // Workgroup b runs on XCD b % 8 (8 XCDs, each with its own L2).  Give each
+  // XCD one contiguous run of the head-major order, so the query tiles that
+  // are resident together on an XCD are spatial neighbours of one head and
+  // share most of their key tiles in that XCD's L2.
+  constexpr int64_t kXcds = 8;
+  const int64_t per = (T + kXcds - 1) / kXcds;
+  p.attn_order.assign(per * kXcds, -1);
+  for (int64_t b = 0; b < per * kXcds; ++b) {
+    const int64_t logical = (b % kXcds) * per + b / kXcds;
+    if (logical < T) p.attn_order[b] = order[logical];
+  }
 }
 
 void build_staging(veda_plan& p) {

@@ -292,8 +292,10 @@ __global__ void __launch_bounds__(kThreads) pool_kernel(DevPlan p, const uint16_
 }
 
 // x_hat[t][d] = fp32(mean[d] + sum_e W[h][d][e] f[t][e]), e ascending, fp64.
-// Workgroup = (16-tile chunk of one head, head, tensor); W[h][d][:] is read
-// once per chunk.
+// Workgroup = (16-tile chunk of one head, head, tensor).  The chunk's
+// features sit in LDS as fp64 laid out [e][tile], so one 16-byte broadcast
+// read feeds two tiles; thread d streams W[h][d][:] in 16-byte chunks (the
+// next chunk in flight) and keeps the sums of kProjTiles / (256 / D) tiles.
 constexpr int kProjTiles = 16;
 
 template <int D>
@@ -305,7 +307,8 @@ __global__ void __launch_bounds__(kThreads) project_kernel(DevPlan p, const floa
   constexpr int E = 3 * D;
   constexpr int G = kThreads / D;           // tile groups
   constexpr int TPT = kProjTiles / G;       // tiles per thread
-  __shared__ __attribute__((aligned(16))) float f[kProjTiles][E];
+  static_assert(TPT % 2 == 0, "pairs of tiles per LDS read");
+  __shared__ __attribute__((aligned(16))) double f[E][kProjTiles];
   const int h = blockIdx.y;
   const DevShape& sh = p.shape[p.head_shape[h]];
   const int n = sh.num_tiles;
@@ -329,20 +332,25 @@ __global__ void __launch_bounds__(kThreads) project_kernel(DevPlan p, const floa
 #pragma unroll
     for (int u = 0; u < V4; ++u) {
       const int q4 = u * kThreads + threadIdx.x;
-      *reinterpret_cast<float4*>(&f[(4 * q4) / E][(4 * q4) % E]) = buf[u];
+      const int r = (4 * q4) / E, e = (4 * q4) % E;
+      f[e + 0][r] = (double)buf[u].x;
+      f[e + 1][r] = (double)buf[u].y;
+      f[e + 2][r] = (double)buf[u].z;
+      f[e + 3][r] = (double)buf[u].w;
     }
   }
   __syncthreads();
   const int d = threadIdx.x % D, grp = threadIdx.x / D;
   double acc[TPT];
 #pragma unroll
-  for (int u = 0; u < TPT; ++u) acc[u] = (double)f[grp * TPT + u][d];
+  for (int u = 0; u < TPT; ++u) acc[u] = f[d][grp * TPT + u];
   // W[h][d][:] streamed in 16-float chunks, the next chunk in flight while
   // the current one is used; the sum order stays e = 0, 1, ..., 3D-1.
   const float4* wr = reinterpret_cast<const float4*>(W + (int64_t)d * E);
   float4 cur[4], nxt[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) cur[u] = wr[u];
+#pragma unroll 1
   for (int e0 = 0; e0 < E; e0 += 16) {
     if (e0 + 16 < E) {
 #pragma unroll
@@ -355,8 +363,13 @@ __global__ void __launch_bounds__(kThreads) project_kernel(DevPlan p, const floa
       for (int c = 0; c < 4; ++c) {
         const int e = e0 + 4 * u + c;
         const double wd = (double)wv[c];
+        const double2* fe = reinterpret_cast<const double2*>(&f[e][grp * TPT]);
 #pragma unroll
-        for (int tt = 0; tt < TPT; ++tt) acc[tt] = fma(wd, (double)f[grp * TPT + tt][e], acc[tt]);
+        for (int tt = 0; tt < TPT / 2; ++tt) {
+          const double2 fv = fe[tt];
+          acc[2 * tt] = fma(wd, fv.x, acc[2 * tt]);
+          acc[2 * tt + 1] = fma(wd, fv.y, acc[2 * tt + 1]);
+        }
       }
     }
 #pragma unroll
@@ -382,10 +395,31 @@ __global__ void __launch_bounds__(kThreads) score_kernel(DevPlan p, const float*
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
   if (i0 >= n || j0 >= n) return;
   const int64_t t0 = p.head_tile_off[h];
-  for (int q = threadIdx.x; q < 64 * D; q += kThreads) {
-    const int r = q / D, d = q % D;
-    qs[d][r] = (i0 + r < n) ? hat_q[(t0 + i0 + r) * D + d] : 0.0f;
-    ks[d][r] = (j0 + r < n) ? hat_k[(t0 + j0 + r) * D + d] : 0.0f;
+  {   // 64 rows of q_hat and k_hat, 16-byte loads all in flight, stored [d][row]
+    constexpr int V4 = 64 * D / 4 / kThreads;
+    float4 bq[V4], bk[V4];
+#pragma unroll
+    for (int u = 0; u < V4; ++u) {
+      const int q4 = u * kThreads + threadIdx.x;
+      const int r = (4 * q4) / D, d = (4 * q4) % D;
+      // rows past the head's last tile read the last tile (in bounds) and are
+      // zeroed below, so every load is unconditional
+      bq[u] = *reinterpret_cast<const float4*>(hat_q + (t0 + min(i0 + r, n - 1)) * D + d);
+      bk[u] = *reinterpret_cast<const float4*>(hat_k + (t0 + min(j0 + r, n - 1)) * D + d);
+    }
+#pragma unroll
+    for (int u = 0; u < V4; ++u) {
+      const int r = (4 * (u * kThreads + threadIdx.x)) / D;
+      if (i0 + r >= n) bq[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j0 + r >= n) bk[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < V4; ++u) {
+      const int q4 = u * kThreads + threadIdx.x;
+      const int r = (4 * q4) / D, d = (4 * q4) % D;
+      qs[d][r] = bq[u].x; qs[d + 1][r] = bq[u].y; qs[d + 2][r] = bq[u].z; qs[d + 3][r] = bq[u].w;
+      ks[d][r] = bk[u].x; ks[d + 1][r] = bk[u].y; ks[d + 2][r] = bk[u].z; ks[d + 3][r] = bk[u].w;
+    }
   }
   __syncthreads();
   const int ti = threadIdx.x / 16, tj = threadIdx.x % 16;
@@ -689,9 +723,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, in
 }
 
 template <int D>
-__device__ __forceinline__ int k_lane_offset() {   // bytes
+__device__ __forceinline__ int k_lane_offset(int tid) {   // bytes; tid = thread index inside 256
   constexpr int CH = D / 8;
-  const int r = threadIdx.x / CH, pc = threadIdx.x % CH;      // row inside a 256/CH-row step
+  const int r = tid / CH, pc = tid % CH;      // row inside a 256/CH-row step
   const int c = pc ^ (r & (CH - 1));
   const int key = (r & ~31) | pi_row(r & 31);
   return 2 * (key * D + 8 * c);
@@ -708,8 +742,8 @@ __device__ __forceinline__ void dma_k_tile(uint16_t* ks, __amdgpu_buffer_rsrc_t 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, ks + 8 * (it * kThreads + 64 * wave), 16, lane_off,
                                              tile_byte + it * STEP * D * 2, 0, 0);
 }
-__device__ __forceinline__ int vt_lane_offset() {   // bytes
-  const int r = threadIdx.x / 16, pc = threadIdx.x % 16;
+__device__ __forceinline__ int vt_lane_offset(int tid) {   // bytes; tid = thread index inside 256
+  const int r = tid / 16, pc = tid % 16;
   return 2 * (r * kTile + 8 * (pc ^ (r & 15)));
 }
 template <int D>
@@ -758,7 +792,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
   const int wave = uni(threadIdx.x >> 6);
   const int beg = uni(row_ptr[t]), end = uni(row_ptr[t + 1]);
   const int w = threadIdx.x >> 6, lane = lane_id(), ln = lane & 31, hl = lane >> 5;
-  const int koff = k_lane_offset<D>(), voff = vt_lane_offset();
+  const int koff = k_lane_offset<D>(threadIdx.x), voff = vt_lane_offset(threadIdx.x);
 
   // Q^T operand: query row 32w + ln, channels 16s + 8hl .. +7
   bf16x8 qf[D / 16];
@@ -1075,12 +1109,13 @@ hipError_t launch_attn_fwd(const DevPlan& p, const void* q, const void* k, const
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(vt);
   uint16_t* oo = static_cast<uint16_t*>(o);
-  if (p.head_dim == 128)
+  if (p.head_dim == 128) {
     hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
                        scale_log2, oo, o_natural, lse, visited);
-  else
+  } else {
     hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
                        scale_log2, oo, o_natural, lse, visited);
+  }
   return hipGetLastError();
 }
 
