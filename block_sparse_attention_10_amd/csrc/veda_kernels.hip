@@ -730,30 +730,39 @@ __device__ __forceinline__ int k_lane_offset(int tid) {   // bytes; tid = thread
   const int key = (r & ~31) | pi_row(r & 31);
   return 2 * (key * D + 8 * c);
 }
+// Copy half hh (rows 64hh .. 64hh+63, i.e. key groups 2hh and 2hh+1) of a
+// K tile into its own LDS array `dst`; D/32 instructions per thread.
 template <int D>
-__device__ __forceinline__ void dma_k_tile(uint16_t* ks, __amdgpu_buffer_rsrc_t rk, int tile_byte, int lane_off,
-                                           int wave) {
+__device__ __forceinline__ void dma_k_half(uint16_t* __restrict__ dst, __amdgpu_buffer_rsrc_t rk, int tile_byte,
+                                           int lane_off, int wave, int hh) {
   constexpr int CH = D / 8;
   constexpr int STEP = kThreads / CH;           // rows per instruction
-  constexpr int PER = kTile / STEP;
   static_assert(STEP % 32 == 0 || 32 % STEP == 0, "pi order stays inside one step");
 #pragma unroll
-  for (int it = 0; it < PER; ++it)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, ks + 8 * (it * kThreads + 64 * wave), 16, lane_off,
-                                             tile_byte + it * STEP * D * 2, 0, 0);
+  for (int it = 0; it < 64 / STEP; ++it) {
+    const int r0 = it * STEP;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst + r0 * D + 512 * wave, 16, lane_off,
+                                             tile_byte + (64 * hh + r0) * D * 2, 0, 0);
+  }
 }
+
+// V^T in LDS: two halves [D][64 keys] (keys 64hh .. 64hh+63) in separate
+// arrays, so the half a wave has finished with can be refilled while the
+// other is in use.  In a half-row of eight 16-byte chunks, chunk c sits at
+// position c ^ ((d >> 1) & 7): the 16 rows read by 16 consecutive lanes then
+// start in 16 distinct 4-bank groups.
 __device__ __forceinline__ int vt_lane_offset(int tid) {   // bytes; tid = thread index inside 256
-  const int r = tid / 16, pc = tid % 16;
-  return 2 * (r * kTile + 8 * (pc ^ (r & 15)));
+  const int r = tid / 8, pos = tid % 8;                    // row inside a 32-row step
+  const int c = pos ^ ((r >> 1) & 7);
+  return 2 * (r * kTile + 8 * c);
 }
 template <int D>
-__device__ __forceinline__ void dma_vt_tile(uint16_t* vs, __amdgpu_buffer_rsrc_t rv, int tile_byte, int lane_off,
-                                            int wave) {
-  constexpr int PER = D * 16 / kThreads;        // 16 rows of 128 keys per instruction
+__device__ __forceinline__ void dma_vt_half(uint16_t* __restrict__ dst, __amdgpu_buffer_rsrc_t rv, int tile_byte,
+                                            int lane_off, int wave, int hh) {
 #pragma unroll
-  for (int it = 0; it < PER; ++it)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vs + 8 * (it * kThreads + 64 * wave), 16, lane_off,
-                                             tile_byte + it * 16 * kTile * 2, 0, 0);
+  for (int it = 0; it < D / 32; ++it)            // 32 rows of 64 keys per instruction
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst + it * 32 * 64 + 512 * wave, 16, lane_off,
+                                             tile_byte + it * 32 * kTile * 2 + hh * 128, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -761,10 +770,182 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
-// Pipelining over a row's key blocks with one K and one V^T buffer: the copy
-// of K(b+1) runs during softmax(b) and PV(b); the copy of V^T(b+1) runs
-// during QK^T(b+1) and softmax(b+1).  Two workgroups share a CU (64 KB of
-// LDS each), so one's waits are covered by the other's MFMA work.
+// Synchronous copy (plain loads and LDS stores) of one K tile and one V^T
+// tile into the four half arrays in the layouts the asynchronous copies
+// produce.
+template <int D>
+__device__ __forceinline__ void copy_kv_halves(uint16_t* __restrict__ kh0, uint16_t* __restrict__ kh1,
+                                               uint16_t* __restrict__ vh0, uint16_t* __restrict__ vh1,
+                                               const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg) {
+  constexpr int CH = D / 8;
+#pragma unroll 1
+  for (int q = threadIdx.x; q < kTile * CH; q += kThreads) {
+    const int m = q / CH, pos = q % CH;               // LDS row (pi order) and chunk position
+    const int key = (m & ~31) | pi_row(m & 31);
+    const int cc = pos ^ (m & (CH - 1));
+    uint16_t* dst = (m < 64 ? kh0 : kh1) + (m & 63) * D + 8 * pos;
+    st16(dst, ld16(kg + (int64_t)key * D + 8 * cc));
+  }
+#pragma unroll 1
+  for (int q = threadIdx.x; q < D * 16; q += kThreads) {
+    const int d = q / 16, pc = q % 16;                // V^T row and 16-byte chunk position in LDS
+    const int hh = pc / 8, pos = pc % 8;
+    const int cc = pos ^ ((d >> 1) & 7);
+    uint16_t* dst = (hh == 0 ? vh0 : vh1) + d * 64 + 8 * pos;
+    st16(dst, ld16(vg + (int64_t)d * kTile + 64 * hh + 8 * cc));
+  }
+}
+
+// S^T of key group kt (keys 32kt .. 32kt+31) against the wave's 32 queries,
+// accumulated onto `init`; khalf is the LDS array of K rows 64(kt/2) ...
+template <int D>
+__device__ __forceinline__ f32x16 qk_group(const uint16_t* __restrict__ khalf, const bf16x8 (&qf)[D / 16], int kt,
+                                           const f32x16& init) {
+  constexpr int CH = D / 8;
+  const int lane = lane_id();
+  const int ln = lane & 31, hl = lane >> 5;
+  const int m = 32 * (kt & 1) + ln;
+  f32x16 acc = init;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(khalf + m * D + 8 * ((2 * s + hl) ^ (m & (CH - 1)))));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// O^T += V^T P^T over key group kt; vhalf is the LDS array of V^T keys
+// 64(kt/2) ..; pg[s2] holds the lane's P values for keys 32kt + 16s2 + 8hl
+// .. +7.
+template <int D>
+__device__ __forceinline__ void pv_group(const uint16_t* __restrict__ vhalf, const bf16x8 (&pg)[2], int kt,
+                                         f32x16 (&oacc)[D / 32]) {
+  const int lane = lane_id();
+  const int ln = lane & 31, hl = lane >> 5;
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const int c = 4 * (kt & 1) + 2 * s2 + hl;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int d = 32 * db + ln;
+      const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(vhalf + d * 64 + 8 * (c ^ ((ln >> 1) & 7))));
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pg[s2], oacc[db], 0, 0, 0);
+    }
+  }
+}
+
+// Key slots >= nj of group kt become -inf (the singleton mask rule: slots at
+// or past a tile's valid count are padding).
+__device__ __forceinline__ void mask_group(f32x16& sg, int kt, int nj, int hl) {
+  if (32 * kt + 32 <= nj) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (sacc_key(kt, r, hl) >= nj) sg[r] = -INFINITY;
+}
+
+// p = exp2(s*c - m) for the lane's 16 keys of a group, packed to bf16 in key
+// order; with SUM, also returns the lane's fp32 sum of p.
+template <bool SUM>
+__device__ __forceinline__ float exp_group(const f32x16& sg, float c, float m, bf16x8 (&pg)[2]) {
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    u32x4 pk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sg[8 * s2 + 2 * e], c, -m));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sg[8 * s2 + 2 * e + 1], c, -m));
+      pk[e] = pack_bf16x2(p0, p1);
+      if (SUM) acc[e] += p0 + p1;
+    }
+    pg[s2] = __builtin_bit_cast(bf16x8, pk);
+  }
+  return SUM ? (acc[0] + acc[1]) + (acc[2] + acc[3]) : 0.0f;
+}
+
+// Row sums of P on the matrix core: with A = P (rows = queries, as the P^T
+// operand of PV already holds it) and B = a block of ones, D[i][j] = sum_k
+// P[i][k] for every column j.
+__device__ __forceinline__ void psum_group(const bf16x8 (&pg)[2], const bf16x8& ones, f32x16& lacc) {
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pg[s2], ones, lacc, 0, 0, 0);
+}
+
+// Scheduling pattern for one pipeline step: two LDS operand reads ahead,
+// then per MFMA one more read and up to `valu` vector instructions, so
+// operand reads stay a few deep (short register lifetimes) and the softmax
+// work is spread between the MFMAs.
+template <int NMFMA, int VALU>
+__device__ __forceinline__ void interleave_step() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // DS read
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // DS read
+    if (VALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);   // VALU
+  }
+}
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
+// Largest row sum of p that the fixed-reference pass accepts (p <= 2^64
+// keeps O and l finite), and the largest ratio of the removed padding mass to
+// the remaining sum (bounds the cancellation in l).
+constexpr float kMaxRowSum = 18446744073709551616.0f;   // 2^64
+constexpr float kMaxPadRatio = 8.0f;
+#ifndef VEDA_PSUM
+#define VEDA_PSUM 0
+#endif
+constexpr bool kPsum = VEDA_PSUM != 0;
+
+// Number of padding keys (slots >= nv) among the 64 keys of a block that a
+// lane of half hh holds: the 16-byte chunks c = 2v + hh, v = 0..7, i.e. keys
+// 8c .. 8c+7.
+__device__ __forceinline__ int half_pads(int nv, int hh) {
+  int n = 0;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) n += min(max(8 * (2 * v + hh) + 8 - nv, 0), 8);
+  return n;
+}
+
+// One workgroup of 4 waves per (head, 128-row query tile).  A key block is
+// worked in four 32-key groups, software-pipelined inside each wave: the QK^T
+// MFMAs of group t are issued together with the PV MFMAs of group t-2 and the
+// softmax VALU work of group t-1, none of which depend on each other, so one
+// wave keeps the matrix core and the vector ALU busy at the same time.  (On
+// gfx950 an MFMA overlaps VALU work of its own wave; a second wave's VALU
+// work largely waits for it.)  VALU work is the scarce resource, so the fast
+// pass spends none on maxima, rescaling, masking or row sums:
+//
+// Reference point.  p = exp2(s*c - m), c = softmax_scale * log2(e), with one
+// m per query for the whole row: the exact maximum of the row's first key
+// group.  Softmax does not depend on m; what matters is that no p overflows,
+// and the first group already holds p = 1 for its largest key.
+//
+// Row sums.  l = sum of the bf16-rounded P (the values PV uses), taken on the
+// matrix core by psum_group: two more MFMAs per group.
+//
+// Padding keys.  Key slots at or past a tile's valid count hold zero rows of
+// K and zero columns of V^T (the permutation writes them so), so their logit
+// is exactly 0, their p is exp2(-m) and their PV product is zero.  Instead of
+// masking, the row's count of padding keys times bf16(exp2(-m)) is
+// subtracted from l at the end.
+//
+// Guard.  A valid query row whose l exceeds kMaxRowSum (a logit more than
+// 64 log2 units above the first group's maximum; this also keeps O finite) or
+// whose removed padding mass exceeds kMaxPadRatio times its final l is
+// recomputed, together with the rest of its workgroup, by the classic online
+// softmax: explicit masking, exact running maximum, O and l rescaled whenever
+// it grows, fp32 row sums.
+//
+// K and V^T are single buffers per workgroup, each in two 64-key halves that
+// are refilled separately: K rows of groups 0-1 once every wave has done QK
+// of group 1, K rows of groups 2-3 and V^T keys 0-63 once every wave has done
+// QK of group 3 and PV of group 1, V^T keys 64-127 after the block.  Two
+// workgroups share a CU (73 KB of LDS each).
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
@@ -773,11 +954,18 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
                                                               const int32_t* __restrict__ col_idx, float scale_log2,
                                                               uint16_t* __restrict__ o, int o_natural,
                                                               float* __restrict__ lse, uint32_t* __restrict__ visited) {
-  constexpr int PER = kTile * D / 8 / kThreads;  // copy instructions per tile and thread
+  constexpr int H = D / 32;   // copy instructions per thread and half tile (K or V^T)
   constexpr int kRowList = 2048;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kTile * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[D * kTile];
+  // K and V^T halves as four separate arrays: the compiler then knows that
+  // reads of one half do not depend on copies into another, and does not
+  // make those reads wait for the copies.
+  __shared__ __attribute__((aligned(16))) uint16_t kh0[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t kh1[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vh0[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vh1[64 * D];
   __shared__ int32_t rowlist[kRowList];
+  __shared__ float lrow[kTile];
+  __shared__ int32_t redo;
   const int t = uni(p.attn_order[blockIdx.x]);
   if (t < 0) return;
   const int h = uni(p.row_head[t]);
@@ -793,129 +981,226 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
   const int beg = uni(row_ptr[t]), end = uni(row_ptr[t + 1]);
   const int w = threadIdx.x >> 6, lane = lane_id(), ln = lane & 31, hl = lane >> 5;
   const int koff = k_lane_offset<D>(threadIdx.x), voff = vt_lane_offset(threadIdx.x);
+  const float c = scale_log2;
+  const bool qvalid = 32 * w + ln < sh.valid[i];
+  if (threadIdx.x == 0) redo = 0;
 
   // Q^T operand: query row 32w + ln, channels 16s + 8hl .. +7
   bf16x8 qf[D / 16];
   const uint16_t* qrow = q + (row0 + 32 * w + ln) * D + 8 * hl;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld16(qrow + 16 * s));
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
   f32x16 oacc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  f32x16 lacc;          // fast pass: row sums of P (every column holds them)
+  float m_run, l_run;   // reference point; safe pass: the lane's fp32 sum
+  int npad;             // fast pass: padding keys over the row's blocks
 
-  // The row's key tiles and their valid counts, staged in LDS as
-  // (tile << 8 | valid) so the loop issues no vector loads besides the tile
-  // copies; rows longer than kRowList refill it at that boundary.
+  // The row's key tiles, staged in LDS as (tile << 14 | pads1 << 7 | pads0)
+  // (padsX = half_pads of the tile's valid count) so the loop issues no
+  // vector loads besides the tile copies; rows longer than kRowList refill it
+  // at that boundary.
   auto fill_list = [&](int base) {
     for (int e = threadIdx.x; e < kRowList && base + e < end; e += kThreads) {
       const int jj = min(max(col_idx[base + e], 0), nt - 1);   // stay inside the head
-      rowlist[e] = (jj << 8) | sh.valid[jj];
+      const int nv = sh.valid[jj];
+      rowlist[e] = (jj << 14) | (half_pads(nv, 1) << 7) | half_pads(nv, 0);
     }
   };
-  fill_list(beg);
-  dma_sync<0>();
-  int ent = uni(beg < end ? rowlist[0] : kTile);
-  int j = ent >> 8, nj = ent & 0xff;
-  if (beg < end) {
-    dma_k_tile<D>(ks, rk, j * kTile * D * 2, koff, wave);
-    dma_vt_tile<D>(vs, rv, j * kTile * D * 2, voff, wave);
-  }
-  dma_sync<0>();
-  for (int b = beg; b < end; ++b) {
-    const bool more = b + 1 < end;
-    int jn = 0, njn = kTile;
-    if (more) {
-      const int slot = (b + 1 - beg) % kRowList;
-      if (slot == 0) {   // only rows longer than kRowList blocks get here
+
+  // exact maximum of a group over both lane halves
+  auto group_max = [&](const f32x16& sg) {
+    float gm = sg[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) gm = fmaxf(gm, sg[r]);
+    return fmaxf(gm, __shfl_xor(gm, 32, 64));
+  };
+
+  // softmax of one group; SAFE re-bases m to the exact running maximum first
+  // and sums p on the VALU
+  auto softmax = [&](auto safe, f32x16& sg, bf16x8 (&pg)[2]) {
+    if constexpr (decltype(safe)::value) {
+      const float m_new = fmaxf(m_run, group_max(sg) * c);
+      if (m_new > m_run) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // m_run = -inf gives 0
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      l_run += exp_group<true>(sg, c, m_run, pg);
+    } else if constexpr (kPsum) {
+      exp_group<false>(sg, c, m_run, pg);
+    } else {
+      l_run += exp_group<true>(sg, c, m_run, pg);
+    }
+  };
+  // Keeps a group's softmax inside its own pipeline step: without it the
+  // compiler sinks the (pure) VALU work past the step's barrier and copy
+  // branch to its use in the next step, which leaves this step's MFMAs
+  // without VALU work and doubles the next step's.
+  auto pin = [](bf16x8 (&pg)[2]) { asm volatile("" : "+v"(pg[0]), "+v"(pg[1])); };
+  auto pv = [&](auto safe, const uint16_t* __restrict__ vhalf, const bf16x8 (&pg)[2], int kt) {
+    pv_group<D>(vhalf, pg, kt, oacc);
+    if constexpr (!decltype(safe)::value && kPsum) psum_group(pg, ones, lacc);
+  };
+
+  // One key block.  Steps are separated by scheduling barriers so that the
+  // compiler keeps each step's operand reads and MFMAs together with that
+  // step's softmax work (and register lifetimes short).  The fast pass
+  // (!SAFE) also issues the asynchronous copies of the next block here;
+  // `compute` = false runs only those (the pass's first iteration).
+  auto block = [&](auto safe, bool compute, bool first, int ent, bool more, int jn) {
+    constexpr bool SAFE = decltype(safe)::value;
+    const int nj = kTile - ((ent >> 7) & 127) - (ent & 127);
+    const f32x16 zero16 = {};
+    f32x16 s0, s1, s2, s3;
+    bf16x8 p0[2], p1[2], p2[2], p3[2];
+    if (compute) {
+      s0 = qk_group<D>(kh0, qf, 0, zero16);
+      interleave_step<8, 0>();
+      if constexpr (SAFE) mask_group(s0, 0, nj, hl);
+      if (first) m_run = group_max(s0) * c;   // key 0 is valid, so this is finite
+      __builtin_amdgcn_sched_barrier(0);
+      s1 = qk_group<D>(kh0, qf, 1, zero16);
+      if constexpr (SAFE) mask_group(s1, 1, nj, hl);
+      softmax(safe, s0, p0);
+      pin(p0);
+      interleave_step<8, 4>();
+    }
+    if constexpr (!SAFE) {
+      dma_sync<H>();                  // V^T(b) keys 0-63 have landed; K rows 0-63 are free
+      if (more) dma_k_half<D>(kh0, rk, jn * kTile * D * 2, koff, wave, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (compute) {
+      s2 = qk_group<D>(kh1, qf, 2, zero16);
+      if constexpr (SAFE) mask_group(s2, 2, nj, hl);
+      pv(safe, vh0, p0, 0);
+      softmax(safe, s1, p1);
+      pin(p1);
+      interleave_step<18, 2>();
+      __builtin_amdgcn_sched_barrier(0);
+      s3 = qk_group<D>(kh1, qf, 3, zero16);
+      if constexpr (SAFE) mask_group(s3, 3, nj, hl);
+      pv(safe, vh0, p1, 1);
+      softmax(safe, s2, p2);
+      pin(p2);
+      interleave_step<18, 2>();
+    }
+    if constexpr (!SAFE) {
+      if (more) dma_sync<H>(); else dma_sync<0>();   // V^T(b) keys 64-127 have landed; K, V^T keys 0-63 free
+      if (more) {
+        dma_k_half<D>(kh1, rk, jn * kTile * D * 2, koff, wave, 1);
+        dma_vt_half<D>(vh0, rv, jn * kTile * D * 2, voff, wave, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (compute) {
+      pv(safe, vh1, p2, 2);
+      softmax(safe, s3, p3);
+      pin(p3);
+      interleave_step<10, 4>();
+      __builtin_amdgcn_sched_barrier(0);
+      pv(safe, vh1, p3, 3);
+      interleave_step<10, 0>();
+      if constexpr (!SAFE) npad += kTile - nj;
+    }
+  };
+
+  auto reset_row = [&]() {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+    lacc = f32x16{};
+    m_run = -INFINITY;
+    l_run = 0.0f;
+    npad = 0;
+  };
+
+  // Fast pass.  Iteration b computes block b and copies block b+1; the first
+  // iteration (b = beg-1) only copies block beg.  Every asynchronous copy of
+  // the kernel is issued from the four call sites of this pass: the
+  // compiler tracks only a few distinct copy sites precisely and makes every
+  // LDS read wait for all copies once there are more.
+  auto run_fast = [&]() {
+    reset_row();
+    fill_list(beg);
+    dma_sync<0>();
+    int ent = 0;
+    int en = uni(beg < end ? rowlist[0] : 0);
+    for (int b = beg - 1; b < end; ++b) {
+      const bool more = b + 1 < end;
+      const int jn = en >> 14;
+      block(BoolC<false>{}, b >= beg, b == beg, ent, more, jn);
+      if (more) {
+        dma_sync<H>();                // K(b+1) has landed; every wave is done with V^T(b)
+        dma_vt_half<D>(vh1, rv, jn * kTile * D * 2, voff, wave, 1);
+      }
+      ent = en;
+      if (b + 2 < end) {
+        const int slot = (b + 2 - beg) % kRowList;
+        if (slot == 0) {   // only rows longer than kRowList blocks get here
+          lds_sync();
+          fill_list(b + 2);
+          dma_sync<0>();
+        }
+        en = uni(rowlist[slot]);
+      }
+    }
+  };
+
+  // Safe pass: plain synchronous tile copies, then the block.
+  auto run_safe = [&]() {
+    reset_row();
+    for (int b = beg; b < end; ++b) {
+      const int slot = (b - beg) % kRowList;
+      if (slot == 0) {
         lds_sync();
-        fill_list(b + 1);
+        fill_list(b);
         dma_sync<0>();
       }
-      const int en = uni(rowlist[slot]);
-      jn = en >> 8;
-      njn = en & 0xff;
+      const int ent = uni(rowlist[slot]);
+      const int j = ent >> 14;
+      lds_sync();                     // every wave is done with the previous tiles
+      copy_kv_halves<D>(kh0, kh1, vh0, vh1, k + (hrow + (int64_t)kTile * j) * D,
+                        vt + ((int64_t)uni(p.head_tile_off[h]) + j) * D * kTile);
+      lds_sync();
+      block(BoolC<true>{}, true, b == beg, ent, false, 0);
     }
-    f32x16 sacc[4];
-    qk_block<D>(ks, qf, sacc);
-    lds_sync();                       // every wave is done with K(b)
-    if (more) dma_k_tile<D>(ks, rk, jn * kTile * D * 2, koff, wave);
-    if (nj < kTile) {   // singleton mask rule: key slots >= valid(j) are padding
+  };
+
+  run_fast();
+  // Row sum of the fast pass: lane (ln, hl) register r holds the sum of query
+  // row 8(r/4) + 4hl + r%4 of the wave; every column holds the same values.
+  float l_all;
+  float e_pad = __builtin_amdgcn_exp2f(-m_run);   // a padding key's p
+  if constexpr (kPsum) {
+    if (ln == 0) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        if (32 * kt + 32 <= nj) continue;              // group fully valid
-        if (32 * kt >= nj) {                           // group fully padding
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kt][r] = -INFINITY;
-          continue;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (sacc_key(kt, r, hl) >= nj) sacc[kt][r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r) lrow[32 * w + 8 * (r >> 2) + 4 * hl + (r & 3)] = lacc[r];
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // The reference point m only moves up when the block max exceeds it by
-    // more than 2^8 (softmax does not depend on it; p stays <= 256), so the
-    // O rescale is rare.  The first block always sets it.
-    const float mx_s = mx * scale_log2;
-    const float m_new = (mx_s > m_run + 8.0f) ? mx_s : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
-    m_run = m_new;
-    if (b > beg && __any(alpha != 1.0f)) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-    // P = exp2(s*c - m), summed in fp32 and packed to bf16 pairs.
-    bf16x8 pb[4][2];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * s2 + 2 * e], scale_log2, -m_new));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * s2 + 2 * e + 1], scale_log2, -m_new));
-          pk[e] = pack_bf16x2(p0, p1);
-          l_run += p0 + p1;
-        }
-        pb[kt][s2] = __builtin_bit_cast(bf16x8, pk);
-      }
-    if (more) dma_sync<PER>(); else dma_sync<0>();   // V^T(b) has landed
-    // O^T[d][q] += V^T[d][keys] P^T[keys][q]
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int c = 4 * kt + 2 * s2 + hl;  // 16-byte chunk of keys in a V^T row
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int d = 32 * db + ln;
-          const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(vs + d * kTile + 8 * (c ^ (d & 15))));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][s2], oacc[db], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    if (more) {
-      lds_sync();                     // every wave is done with V^T(b)
-      dma_vt_tile<D>(vs, rv, jn * kTile * D * 2, voff, wave);
-      dma_sync<PER>();                // K(b+1) has landed
-    }
-    j = jn;
-    nj = njn;
+    lds_sync();
+    e_pad = (float)(__bf16)e_pad;                 // as PV used it
+    l_all = lrow[32 * w + ln];
+  } else {
+    l_all = l_run + __shfl_xor(l_run, 32, 64);
   }
-  // epilogue: combine the two lane halves' partial sums, normalise, store
-  const float l_all = l_run + __shfl_xor(l_run, 32, 64);
+  const float pad_mass = (float)npad * e_pad;
+  l_all -= pad_mass;
+  const bool bad = qvalid && !(l_all <= kMaxRowSum && pad_mass <= kMaxPadRatio * l_all);
+  if (__any(bad) && lane == 0) redo = 1;
+  lds_sync();
+  if (uni(redo)) {
+    run_safe();
+    l_all = l_run + __shfl_xor(l_run, 32, 64);
+  }
+
+  // epilogue: normalise, store
   const float inv = 1.0f / l_all;
   // permuted: row row0 + slot; natural: the slot's token, padding dropped
   uint16_t* orow = o + (row0 + 32 * w + ln) * D;
