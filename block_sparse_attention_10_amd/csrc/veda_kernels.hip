@@ -863,21 +863,18 @@ __device__ __forceinline__ float exp_group(const f32x16& sg, float c, float m, b
   return SUM ? (acc[0] + acc[1]) + (acc[2] + acc[3]) : 0.0f;
 }
 
-// Row sums of P on the matrix core: with A = P (rows = queries, as the P^T
-// operand of PV already holds it) and B = a block of ones, D[i][j] = sum_k
-// P[i][k] for every column j.
-__device__ __forceinline__ void psum_group(const bf16x8 (&pg)[2], const bf16x8& ones, f32x16& lacc) {
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pg[s2], ones, lacc, 0, 0, 0);
-}
-
-// Scheduling pattern for one pipeline step: two LDS operand reads ahead,
-// then per MFMA one more read and up to `valu` vector instructions, so
-// operand reads stay a few deep (short register lifetimes) and the softmax
-// work is spread between the MFMAs.
+// Scheduling pattern for one pipeline step: kLdsAhead LDS operand reads
+// ahead, then per MFMA one more read and up to `valu` vector instructions, so
+// the softmax work is spread between the MFMAs and an MFMA's operand has
+// usually arrived when it issues (a wave issues in order: an operand wait
+// also holds back the VALU work behind it).
+#ifndef VEDA_LDS_AHEAD
+#define VEDA_LDS_AHEAD 2
+#endif
+constexpr int kLdsAhead = VEDA_LDS_AHEAD;
 template <int NMFMA, int VALU>
 __device__ __forceinline__ void interleave_step() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // DS read
+  __builtin_amdgcn_sched_group_barrier(0x100, kLdsAhead, 0);  // DS read
 #pragma unroll
   for (int i = 0; i < NMFMA; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
@@ -891,15 +888,11 @@ struct BoolC {
   static constexpr bool value = B;
 };
 
-// Largest row sum of p that the fixed-reference pass accepts (p <= 2^64
-// keeps O and l finite), and the largest ratio of the removed padding mass to
-// the remaining sum (bounds the cancellation in l).
+// Largest row sum of p that the fast pass accepts (p <= 2^64 keeps O and l
+// finite), and the largest ratio of the removed padding mass to the
+// remaining sum (bounds the cancellation in l).
 constexpr float kMaxRowSum = 18446744073709551616.0f;   // 2^64
 constexpr float kMaxPadRatio = 8.0f;
-#ifndef VEDA_PSUM
-#define VEDA_PSUM 0
-#endif
-constexpr bool kPsum = VEDA_PSUM != 0;
 
 // Number of padding keys (slots >= nv) among the 64 keys of a block that a
 // lane of half hh holds: the 16-byte chunks c = 2v + hh, v = 0..7, i.e. keys
@@ -918,34 +911,31 @@ __device__ __forceinline__ int half_pads(int nv, int hh) {
 // wave keeps the matrix core and the vector ALU busy at the same time.  (On
 // gfx950 an MFMA overlaps VALU work of its own wave; a second wave's VALU
 // work largely waits for it.)  VALU work is the scarce resource, so the fast
-// pass spends none on maxima, rescaling, masking or row sums:
+// pass spends none on maxima, rescaling or masking:
 //
 // Reference point.  p = exp2(s*c - m), c = softmax_scale * log2(e), with one
 // m per query for the whole row: the exact maximum of the row's first key
 // group.  Softmax does not depend on m; what matters is that no p overflows,
 // and the first group already holds p = 1 for its largest key.
 //
-// Row sums.  l = sum of the bf16-rounded P (the values PV uses), taken on the
-// matrix core by psum_group: two more MFMAs per group.
-//
 // Padding keys.  Key slots at or past a tile's valid count hold zero rows of
 // K and zero columns of V^T (the permutation writes them so), so their logit
 // is exactly 0, their p is exp2(-m) and their PV product is zero.  Instead of
-// masking, the row's count of padding keys times bf16(exp2(-m)) is
-// subtracted from l at the end.
+// masking, the row's count of padding keys times exp2(-m) is subtracted from
+// l at the end.
 //
 // Guard.  A valid query row whose l exceeds kMaxRowSum (a logit more than
 // 64 log2 units above the first group's maximum; this also keeps O finite) or
 // whose removed padding mass exceeds kMaxPadRatio times its final l is
 // recomputed, together with the rest of its workgroup, by the classic online
-// softmax: explicit masking, exact running maximum, O and l rescaled whenever
-// it grows, fp32 row sums.
+// softmax (explicit masking, exact running maximum, O and l rescaled whenever
+// it grows), block by block with plain synchronous tile copies.
 //
-// K and V^T are single buffers per workgroup, each in two 64-key halves that
-// are refilled separately: K rows of groups 0-1 once every wave has done QK
-// of group 1, K rows of groups 2-3 and V^T keys 0-63 once every wave has done
-// QK of group 3 and PV of group 1, V^T keys 64-127 after the block.  Two
-// workgroups share a CU (73 KB of LDS each).
+// K and V^T are single buffers per workgroup, each in two 64-key halves
+// (four LDS arrays) that are refilled separately: K rows of groups 0-1 once
+// every wave has done QK of group 1, K rows of groups 2-3 and V^T keys 0-63
+// once every wave has done QK of group 3 and PV of group 1, V^T keys 64-127
+// after the block.  Two workgroups share a CU (72 KB of LDS each).
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
@@ -964,7 +954,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
   __shared__ __attribute__((aligned(16))) uint16_t vh0[64 * D];
   __shared__ __attribute__((aligned(16))) uint16_t vh1[64 * D];
   __shared__ int32_t rowlist[kRowList];
-  __shared__ float lrow[kTile];
   __shared__ int32_t redo;
   const int t = uni(p.attn_order[blockIdx.x]);
   if (t < 0) return;
@@ -974,9 +963,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
   const int i = t - uni(p.head_tile_off[h]);
   const int64_t hrow = uni64(p.head_row_off[h]);
   const int64_t row0 = hrow + (int64_t)kTile * i;
+  const int64_t htile = uni(p.head_tile_off[h]);
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + hrow * D, (int64_t)nt * kTile * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = head_rsrc(vt + (int64_t)uni(p.head_tile_off[h]) * D * kTile,
-                                              (int64_t)nt * kTile * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(vt + htile * D * kTile, (int64_t)nt * kTile * D * 2);
   const int wave = uni(threadIdx.x >> 6);
   const int beg = uni(row_ptr[t]), end = uni(row_ptr[t + 1]);
   const int w = threadIdx.x >> 6, lane = lane_id(), ln = lane & 31, hl = lane >> 5;
@@ -990,13 +979,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
   const uint16_t* qrow = q + (row0 + 32 * w + ln) * D + 8 * hl;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld16(qrow + 16 * s));
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
   f32x16 oacc[D / 32];
-  f32x16 lacc;          // fast pass: row sums of P (every column holds them)
-  float m_run, l_run;   // reference point; safe pass: the lane's fp32 sum
+  float m_run, l_run;   // reference point (log2 units) and the lane's sum of p
   int npad;             // fast pass: padding keys over the row's blocks
 
   // The row's key tiles, staged in LDS as (tile << 14 | pads1 << 7 | pads0)
@@ -1019,104 +1004,68 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
     return fmaxf(gm, __shfl_xor(gm, 32, 64));
   };
 
-  // softmax of one group; SAFE re-bases m to the exact running maximum first
-  // and sums p on the VALU
-  auto softmax = [&](auto safe, f32x16& sg, bf16x8 (&pg)[2]) {
-    if constexpr (decltype(safe)::value) {
-      const float m_new = fmaxf(m_run, group_max(sg) * c);
-      if (m_new > m_run) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // m_run = -inf gives 0
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
-      }
-      l_run += exp_group<true>(sg, c, m_run, pg);
-    } else if constexpr (kPsum) {
-      exp_group<false>(sg, c, m_run, pg);
-    } else {
-      l_run += exp_group<true>(sg, c, m_run, pg);
-    }
-  };
   // Keeps a group's softmax inside its own pipeline step: without it the
   // compiler sinks the (pure) VALU work past the step's barrier and copy
   // branch to its use in the next step, which leaves this step's MFMAs
   // without VALU work and doubles the next step's.
   auto pin = [](bf16x8 (&pg)[2]) { asm volatile("" : "+v"(pg[0]), "+v"(pg[1])); };
-  auto pv = [&](auto safe, const uint16_t* __restrict__ vhalf, const bf16x8 (&pg)[2], int kt) {
-    pv_group<D>(vhalf, pg, kt, oacc);
-    if constexpr (!decltype(safe)::value && kPsum) psum_group(pg, ones, lacc);
-  };
 
-  // One key block.  Steps are separated by scheduling barriers so that the
-  // compiler keeps each step's operand reads and MFMAs together with that
-  // step's softmax work (and register lifetimes short).  The fast pass
-  // (!SAFE) also issues the asynchronous copies of the next block here;
-  // `compute` = false runs only those (the pass's first iteration).
-  auto block = [&](auto safe, bool compute, bool first, int ent, bool more, int jn) {
-    constexpr bool SAFE = decltype(safe)::value;
-    const int nj = kTile - ((ent >> 7) & 127) - (ent & 127);
+  // One key block of the fast pass.  Steps are separated by scheduling
+  // barriers so that the compiler keeps each step's operand reads and MFMAs
+  // together with that step's softmax work (and register lifetimes short).
+  // It also issues the asynchronous copies of the next block; `compute` =
+  // false runs only those (the pass's first iteration).
+  auto block = [&](bool compute, bool first, int ent, bool more, int jn) {
     const f32x16 zero16 = {};
     f32x16 s0, s1, s2, s3;
     bf16x8 p0[2], p1[2], p2[2], p3[2];
     if (compute) {
       s0 = qk_group<D>(kh0, qf, 0, zero16);
       interleave_step<8, 0>();
-      if constexpr (SAFE) mask_group(s0, 0, nj, hl);
-      if (first) m_run = group_max(s0) * c;   // key 0 is valid, so this is finite
+      if (first) m_run = group_max(s0) * c;   // finite: key 0 always exists
       __builtin_amdgcn_sched_barrier(0);
       s1 = qk_group<D>(kh0, qf, 1, zero16);
-      if constexpr (SAFE) mask_group(s1, 1, nj, hl);
-      softmax(safe, s0, p0);
+      l_run += exp_group<true>(s0, c, m_run, p0);
       pin(p0);
-      interleave_step<8, 4>();
+      interleave_step<8, 6>();
     }
-    if constexpr (!SAFE) {
-      dma_sync<H>();                  // V^T(b) keys 0-63 have landed; K rows 0-63 are free
-      if (more) dma_k_half<D>(kh0, rk, jn * kTile * D * 2, koff, wave, 0);
-    }
+    dma_sync<H>();                    // V^T(b) keys 0-63 have landed; K rows 0-63 are free
+    if (more) dma_k_half<D>(kh0, rk, jn * kTile * D * 2, koff, wave, 0);
     __builtin_amdgcn_sched_barrier(0);
     if (compute) {
       s2 = qk_group<D>(kh1, qf, 2, zero16);
-      if constexpr (SAFE) mask_group(s2, 2, nj, hl);
-      pv(safe, vh0, p0, 0);
-      softmax(safe, s1, p1);
+      pv_group<D>(vh0, p0, 0, oacc);
+      l_run += exp_group<true>(s1, c, m_run, p1);
       pin(p1);
-      interleave_step<18, 2>();
+      interleave_step<16, 3>();
       __builtin_amdgcn_sched_barrier(0);
       s3 = qk_group<D>(kh1, qf, 3, zero16);
-      if constexpr (SAFE) mask_group(s3, 3, nj, hl);
-      pv(safe, vh0, p1, 1);
-      softmax(safe, s2, p2);
+      pv_group<D>(vh0, p1, 1, oacc);
+      l_run += exp_group<true>(s2, c, m_run, p2);
       pin(p2);
-      interleave_step<18, 2>();
+      interleave_step<16, 3>();
     }
-    if constexpr (!SAFE) {
-      if (more) dma_sync<H>(); else dma_sync<0>();   // V^T(b) keys 64-127 have landed; K, V^T keys 0-63 free
-      if (more) {
-        dma_k_half<D>(kh1, rk, jn * kTile * D * 2, koff, wave, 1);
-        dma_vt_half<D>(vh0, rv, jn * kTile * D * 2, voff, wave, 0);
-      }
+    if (more) dma_sync<H>(); else dma_sync<0>();   // V^T(b) keys 64-127 have landed; K, V^T keys 0-63 free
+    if (more) {
+      dma_k_half<D>(kh1, rk, jn * kTile * D * 2, koff, wave, 1);
+      dma_vt_half<D>(vh0, rv, jn * kTile * D * 2, voff, wave, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (compute) {
-      pv(safe, vh1, p2, 2);
-      softmax(safe, s3, p3);
+      pv_group<D>(vh1, p2, 2, oacc);
+      l_run += exp_group<true>(s3, c, m_run, p3);
       pin(p3);
-      interleave_step<10, 4>();
+      interleave_step<8, 6>();
       __builtin_amdgcn_sched_barrier(0);
-      pv(safe, vh1, p3, 3);
-      interleave_step<10, 0>();
-      if constexpr (!SAFE) npad += kTile - nj;
+      pv_group<D>(vh1, p3, 3, oacc);
+      interleave_step<8, 0>();
+      npad += ((ent >> 7) & 127) + (ent & 127);
     }
   };
 
   auto reset_row = [&]() {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-    lacc = f32x16{};
     m_run = -INFINITY;
     l_run = 0.0f;
     npad = 0;
@@ -1136,7 +1085,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
     for (int b = beg - 1; b < end; ++b) {
       const bool more = b + 1 < end;
       const int jn = en >> 14;
-      block(BoolC<false>{}, b >= beg, b == beg, ent, more, jn);
+      block(b >= beg, b == beg, ent, more, jn);
       if (more) {
         dma_sync<H>();                // K(b+1) has landed; every wave is done with V^T(b)
         dma_vt_half<D>(vh1, rv, jn * kTile * D * 2, voff, wave, 1);
@@ -1154,7 +1103,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
     }
   };
 
-  // Safe pass: plain synchronous tile copies, then the block.
+  // Safe pass: per block a plain synchronous tile copy, then the four groups
+  // one after another with explicit masking and exact re-basing.
   auto run_safe = [&]() {
     reset_row();
     for (int b = beg; b < end; ++b) {
@@ -1166,31 +1116,37 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
       }
       const int ent = uni(rowlist[slot]);
       const int j = ent >> 14;
+      const int nj = kTile - ((ent >> 7) & 127) - (ent & 127);
       lds_sync();                     // every wave is done with the previous tiles
       copy_kv_halves<D>(kh0, kh1, vh0, vh1, k + (hrow + (int64_t)kTile * j) * D,
-                        vt + ((int64_t)uni(p.head_tile_off[h]) + j) * D * kTile);
+                        vt + (htile + j) * D * kTile);
       lds_sync();
-      block(BoolC<true>{}, true, b == beg, ent, false, 0);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const f32x16 zero16 = {};
+        f32x16 sg = qk_group<D>(kt < 2 ? kh0 : kh1, qf, kt, zero16);
+        mask_group(sg, kt, nj, hl);
+        const float m_new = fmaxf(m_run, group_max(sg) * c);
+        if (m_new > m_run) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // m_run = -inf gives 0
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          l_run *= alpha;
+          m_run = m_new;
+        }
+        bf16x8 pg[2];
+        l_run += exp_group<true>(sg, c, m_run, pg);
+        pv_group<D>(kt < 2 ? vh0 : vh1, pg, kt, oacc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
   run_fast();
-  // Row sum of the fast pass: lane (ln, hl) register r holds the sum of query
-  // row 8(r/4) + 4hl + r%4 of the wave; every column holds the same values.
-  float l_all;
-  float e_pad = __builtin_amdgcn_exp2f(-m_run);   // a padding key's p
-  if constexpr (kPsum) {
-    if (ln == 0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) lrow[32 * w + 8 * (r >> 2) + 4 * hl + (r & 3)] = lacc[r];
-    }
-    lds_sync();
-    e_pad = (float)(__bf16)e_pad;                 // as PV used it
-    l_all = lrow[32 * w + ln];
-  } else {
-    l_all = l_run + __shfl_xor(l_run, 32, 64);
-  }
-  const float pad_mass = (float)npad * e_pad;
+  float l_all = l_run + __shfl_xor(l_run, 32, 64);
+  const float pad_mass = (float)npad * __builtin_amdgcn_exp2f(-m_run);
   l_all -= pad_mass;
   const bool bad = qvalid && !(l_all <= kMaxRowSum && pad_mass <= kMaxPadRatio * l_all);
   if (__any(bad) && lane == 0) redo = 1;

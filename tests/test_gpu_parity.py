@@ -103,6 +103,64 @@ def test_small_workloads(w, fused):
     check_attention(w, inp, g, op, qp, kp, sel)
 
 
+def _guard_workload():
+    # every key tile in every row (ascending), partial tiles, D = 64
+    return wl.Workload(96, "guard_all_blocks", (wl.Segment(wl.VIDEO3D, (4, 10, 12), 0),), 2, 64, ((2, 8, 8),) * 2,
+                       wl.ALL_BLOCKS)
+
+
+def test_guard_large_late_logits():
+    """Rows whose later key tiles hold logits far above their first key
+    group's maximum (more than 64 log2 units): the fast pass cannot keep p
+    bounded there and the kernel must fall back to exact re-basing.  Without
+    the fallback those rows overflow."""
+    w = _guard_workload()
+    inp = wl.make_inputs(w, seed=w.index)
+    op = vo.Plan.from_workload(w)
+    k = inp["k"].float()
+    for h in range(w.num_heads):            # scale the keys of each head's last tile by 64 (exact)
+        perm = op.heads[h].perm()
+        last = perm[(op.heads[h].num_tiles - 1) * 128:]
+        toks = torch.from_numpy(last[last >= 0].astype(np.int64))
+        k[toks, h, :] *= 64.0
+    inp["k"] = k.to(torch.bfloat16)
+    g = gp.gpu_path(w, inp)
+    op, qp, kp, sel = check_front(w, inp, g)
+    # precondition: some valid row's logits exceed its first group's maximum by > 70 (log2 units)
+    c = w.softmax_scale / np.log(2.0)
+    worst = 0.0
+    for h in range(w.num_heads):
+        o = op.row_offset[h]
+        for i, row in enumerate(sel[h]):
+            j0 = min(row)
+            q = qp[o + 128 * i: o + 128 * (i + 1)]
+            first = kp[o + 128 * j0: o + 128 * j0 + 32]
+            allk = np.concatenate([kp[o + 128 * j: o + 128 * (j + 1)] for j in row])
+            worst = max(worst, float(np.max((q @ allk.T).max(1) - (q @ first.T).max(1))) * c)
+    assert worst > 70.0, worst
+    check_attention(w, inp, g, op, qp, kp, sel)
+
+
+def test_guard_padding_mass():
+    """Rows whose valid logits all sit far below zero while their key tiles
+    have padding slots (logit exactly 0): the padding mass the fast pass
+    removes dwarfs the valid sum, so the kernel must fall back to explicit
+    masking."""
+    w = _guard_workload()
+    inp = wl.make_inputs(w, seed=w.index)
+    gen = torch.Generator().manual_seed(7)
+    q = 0.1 * torch.randn(inp["q"].shape, generator=gen)
+    k = 0.1 * torch.randn(inp["k"].shape, generator=gen)
+    q[..., 0] += 20.0
+    k[..., 0] -= 20.0                       # every logit about -400 * scale
+    inp["q"], inp["k"] = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    g = gp.gpu_path(w, inp)
+    op, qp, kp, sel = check_front(w, inp, g)
+    padded = [j for h in range(w.num_heads) for row in sel[h] for j in row if op.heads[h].valid_counts()[j] < 128]
+    assert padded, "the workload must select partial key tiles"
+    check_attention(w, inp, g, op, qp, kp, sel)
+
+
 @pytest.mark.parametrize("idx", [1, 2, 3])
 def test_config_full(idx):
     w = wl.workload(idx)
