@@ -4,8 +4,9 @@ One step = one attention layer through the whole hot path on one batch of
 resident synthetic input: permute Q, K (rows) and V (tile-transposed) with the
 tile pooling fused in, project and score tile pairs, select blocks, and run
 block-sparse attention whose epilogue writes O back in natural token order
-(plus, for the packed workload, the all-blocks forward for the dense LSE and
-the block heat).  Four seeded input
+(plus, for the packed workload, the all-blocks forward for the dense LSE, the
+block heat, the oracle mask selected on the heat and the attention mass of
+the predicted and the oracle mask).  Four seeded input
 sets rotate across steps, so each call sees a new block pattern.
 
 Prints one JSON line.  value = attention FLOP over computed blocks / layer
@@ -68,6 +69,11 @@ class Layer:
             self.d_o = p.empty_perm()
             self.d_lse = torch.empty(p.R, dtype=torch.float32, device=dev)
             self.heat = torch.empty(p.info["total_pairs"], dtype=torch.float32, device=dev)
+            # oracle mask (selection on the heat) and the attention mass of both masks
+            self.o_row_ptr = torch.empty(p.T + 1, dtype=torch.int32, device=dev)
+            self.o_col = torch.empty(p.info["nnz"], dtype=torch.int32, device=dev)
+            self.m_pred = torch.empty(w.num_heads, dtype=torch.float64, device=dev)
+            self.m_orc = torch.empty(w.num_heads, dtype=torch.float64, device=dev)
         self.attn_events = []
 
     def step(self, s, time_attn=False):
@@ -89,7 +95,10 @@ class Layer:
             d.select(self.scores, self.d_row_ptr, self.d_col)
             d.attention(self.qp, self.kp, self.vt, self.d_row_ptr, self.d_col, w.softmax_scale, self.d_o,
                         self.d_lse)
-            d.heat(self.qp, self.kp, self.d_lse, w.softmax_scale, self.heat)
+            p.heat(self.qp, self.kp, self.d_lse, w.softmax_scale, self.heat)
+            p.select(self.heat, self.o_row_ptr, self.o_col)
+            p.mask_mass(self.heat, self.row_ptr, self.col, self.m_pred)
+            p.mask_mass(self.heat, self.o_row_ptr, self.o_col, self.m_orc)
 
 
 def cpu_baseline(w, inp, budget_s):
@@ -200,6 +209,14 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
+    if layer.dense is not None:
+        mp, mo = layer.m_pred.cpu().numpy(), layer.m_orc.cpu().numpy()
+        out["mask_quality"] = {
+            "oracle_mask_mass_mean": round(float(mo.mean()), 4),
+            "predicted_mask_mass_mean": round(float(mp.mean()), 4),
+            "recall_mean": round(float((mp / mo).mean()), 4), "recall_min": round(float((mp / mo).min()), 4),
+            "note": "synthetic inputs and a random-init predictor; the pages' 0.63 / 0.71 come from real "
+                    "activations"}
     if not args.no_cpu_baseline:
         print("bench: oracle CPU baseline (~%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inputs[0], args.cpu_seconds)

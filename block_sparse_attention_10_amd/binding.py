@@ -89,6 +89,7 @@ _SIGS = {
     "veda_select_blocks": (_I32, [_P, _P, _P, _P, _P, _P]),
     "veda_block_sparse_attn_fwd": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _P, _P, _P]),
     "veda_block_heat": (_I32, [_P, _P, _P, _P, ctypes.c_float, _P, _P]),
+    "veda_mask_mass": (_I32, [_P, _P, _P, _P, _P, _P]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -254,6 +255,10 @@ def veda_block_heat(plan: int, q, k, lse, softmax_scale: float, heat, stream=Non
                                  _stream(stream)))
 
 
+def veda_mask_mass(plan: int, heat, row_ptr, col_idx, mass, stream=None) -> None:
+    _check(lib().veda_mask_mass(plan, _ptr(heat), _ptr(row_ptr), _ptr(col_idx), _ptr(mass), _stream(stream)))
+
+
 # ---------------------------------------------------------------------------
 # Plan: owns the handle and the device tables; checks tensor sizes
 # ---------------------------------------------------------------------------
@@ -413,6 +418,15 @@ class Plan:
         self._expect(lse, (self.R,), torch.float32, "lse")
         self._expect(heat, (self.info["total_pairs"],), torch.float32, "heat")
         veda_block_heat(self.handle, q, k, lse, scale, heat, stream)
+
+    def mask_mass(self, heat, row_ptr, col_idx, mass, stream=None):
+        import torch
+        self._expect(heat, (self.info["total_pairs"],), torch.float32, "heat")
+        self._expect(row_ptr, (self.T + 1,), torch.int32, "row_ptr")
+        if col_idx is None or col_idx.dtype != torch.int32 or not col_idx.is_cuda:
+            raise ValueError("col_idx must be a device int32 tensor")
+        self._expect(mass, (self.H,), torch.float64, "mass")
+        veda_mask_mass(self.handle, heat, row_ptr, col_idx, mass, stream)
 
     # allocation helpers (torch: device memory only)
     def empty_perm(self):

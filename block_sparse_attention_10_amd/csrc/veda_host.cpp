@@ -696,4 +696,14 @@ veda_status veda_block_heat(const veda_plan* p, const void* q, const void* k, co
   return launched(launch_heat(p->dev, q, k, lse, softmax_scale, heat, (hipStream_t)stream), "block heat");
 }
 
+veda_status veda_mask_mass(const veda_plan* p, const float* heat, const int32_t* row_ptr, const int32_t* col_idx,
+                           double* mass, void* stream) {
+  veda_status st = check_plan_ready(p);
+  if (st) return st;
+  if ((st = check_ptr(heat, "heat")) || (st = check_ptr(row_ptr, "row_ptr")) ||
+      (st = check_ptr(col_idx, "col_idx")) || (st = check_ptr(mass, "mass")))
+    return st;
+  return launched(launch_mask_mass(p->dev, heat, row_ptr, col_idx, mass, (hipStream_t)stream), "mask mass");
+}
+
 }  // extern "C"

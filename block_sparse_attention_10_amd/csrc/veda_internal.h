@@ -64,6 +64,8 @@ hipError_t launch_attn_fwd(const DevPlan& p, const void* q, const void* k, const
                            void* o, int o_natural, float* lse, uint32_t* visited, hipStream_t s);
 hipError_t launch_heat(const DevPlan& p, const void* q, const void* k, const float* lse,
                        float scale, float* heat, hipStream_t s);
+hipError_t launch_mask_mass(const DevPlan& p, const float* heat, const int32_t* row_ptr, const int32_t* col_idx,
+                            double* mass, hipStream_t s);
 
 // Scratch the score call needs: pooled features of Q and K (fp32 [T, 3D]
 // each) and their projections (fp32 [T, D] each).

@@ -1247,6 +1247,49 @@ __global__ void __launch_bounds__(kThreads, 2) heat_kernel(DevPlan p, const uint
   }
 }
 
+// ---------------------------------------------------------------------------
+// attention mass of a block mask
+// ---------------------------------------------------------------------------
+//
+// One workgroup per head.  Thread x takes the head's rows x, x + 256, ...;
+// each row's heat over its listed key tiles is summed in fp64 and weighted by
+// the row tile's valid query count; the partial sums and counts are combined
+// by a fixed-order tree in LDS, so the result does not depend on timing.
+__global__ void __launch_bounds__(kThreads) mask_mass_kernel(DevPlan p, const float* __restrict__ heat,
+                                                            const int32_t* __restrict__ row_ptr,
+                                                            const int32_t* __restrict__ col_idx,
+                                                            double* __restrict__ mass) {
+  __shared__ double kept_s[kThreads];
+  __shared__ double cnt_s[kThreads];
+  const int h = blockIdx.x;
+  const DevShape& sh = p.shape[p.head_shape[h]];
+  const int n = sh.num_tiles;
+  const int64_t t0 = p.head_tile_off[h];
+  const float* hm = heat + p.head_pair_off[h];
+  double kept = 0.0, cnt = 0.0;
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    double row = 0.0;
+    for (int e = row_ptr[t0 + i]; e < row_ptr[t0 + i + 1]; ++e) {
+      const int j = col_idx[e];
+      if (j >= 0 && j < n) row += (double)hm[(int64_t)i * n + j];
+    }
+    const double v = (double)sh.valid[i];
+    kept += v * row;
+    cnt += v;
+  }
+  kept_s[threadIdx.x] = kept;
+  cnt_s[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      kept_s[threadIdx.x] += kept_s[threadIdx.x + w];
+      cnt_s[threadIdx.x] += cnt_s[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) mass[h] = kept_s[0] / cnt_s[0];
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1370,6 +1413,13 @@ hipError_t launch_heat(const DevPlan& p, const void* q, const void* k, const flo
     hipLaunchKernelGGL(heat_kernel<128>, grid, dim3(kThreads), 0, s, p, qq, kk, lse, scale_log2, heat);
   else
     hipLaunchKernelGGL(heat_kernel<64>, grid, dim3(kThreads), 0, s, p, qq, kk, lse, scale_log2, heat);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_mass(const DevPlan& p, const float* heat, const int32_t* row_ptr, const int32_t* col_idx,
+                            double* mass, hipStream_t s) {
+  hipLaunchKernelGGL(mask_mass_kernel, dim3((unsigned)p.num_heads), dim3(kThreads), 0, s, p, heat, row_ptr, col_idx,
+                     mass);
   return hipGetLastError();
 }
 

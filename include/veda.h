@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define VEDA_ABI_VERSION 2
+#define VEDA_ABI_VERSION 3
 
 typedef int32_t veda_status;
 enum {
@@ -261,6 +261,23 @@ veda_status veda_block_sparse_attn_fwd(const veda_plan* plan, const void* q, con
  * A head may have at most 4096 tiles. */
 veda_status veda_block_heat(const veda_plan* plan, const void* q, const void* k,
                             const float* lse, float softmax_scale, float* heat, void* stream);
+
+/* Attention mass a block mask keeps ("Deploying this checkpoint", section 4:
+ * recall of a predicted mask against the oracle mask; section 6: the share
+ * of the attention mass an oracle mask at 10% keep recovers).  Per head h:
+ *   mass[h] = sum_i valid(i) * sum_{j in row i} heat[i][j] / sum_i valid(i),
+ * i.e. with the dense-LSE heat of veda_block_heat, the fraction of the
+ * attention probability of the head's valid queries that falls on the kept
+ * blocks.  The oracle mask is veda_select_blocks applied to the heat in
+ * place of the predicted scores (same budgets, forced diagonal, ties to the
+ * lowest key tile); recall = mass(predicted mask) / mass(oracle mask).
+ *   heat:    device fp32 [sum_h n_h^2], veda_block_heat's layout
+ *   row_ptr, col_idx: device CSR of this plan's shape (as veda_select_blocks
+ *            writes it); out-of-range columns are skipped
+ *   mass:    device fp64 [num_heads]
+ * fp64 accumulation in a fixed order: bitwise reproducible. */
+veda_status veda_mask_mass(const veda_plan* plan, const float* heat, const int32_t* row_ptr,
+                           const int32_t* col_idx, double* mass, void* stream);
 
 #ifdef __cplusplus
 }

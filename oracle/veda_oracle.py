@@ -508,6 +508,44 @@ def block_heat(plan: Plan, q_perm, k_perm, lse: np.ndarray, scale: float,
 
 
 # ---------------------------------------------------------------------------
+# O13: attention mass of a mask and recall against the oracle mask
+# ---------------------------------------------------------------------------
+
+def mask_mass(plan: Plan, heat: List[np.ndarray], selection: List[List[np.ndarray]]) -> np.ndarray:
+    """Fraction of each head's attention probability mass that a mask keeps
+    (reading A19): over the valid queries r of the head,
+    sum_r sum_{j in mask(tile(r))} P(keys of tile j | r) / #valid queries.
+    With heat[i, j] the mean of that inner sum over the valid queries of tile
+    i (O11), this is sum_i nq_i * sum_{j in mask_i} heat[i, j] / sum_i nq_i.
+    The "Deploying this checkpoint" page, section 6, quotes this quantity for
+    the oracle mask; section 4 names recall against the oracle mask.
+
+    heat: per head [n, n] (fp32 or fp64 values); returns fp64 [num_heads].
+    """
+    out = np.zeros(plan.num_heads, dtype=np.float64)
+    for h in range(plan.num_heads):
+        nq = plan.heads[h].valid_counts().astype(np.float64)
+        hm = np.asarray(heat[h], dtype=np.float64)
+        kept = 0.0
+        for i, row in enumerate(selection[h]):
+            kept += nq[i] * float(np.sum(hm[i, np.asarray(row, dtype=np.int64)]))
+        out[h] = kept / float(np.sum(nq))
+    return out
+
+
+def oracle_mask(plan: Plan, heat: List[np.ndarray]) -> List[List[np.ndarray]]:
+    """The oracle mask (A20): the same budgeted selection as the predictor's
+    (forced diagonal, per-row budgets, ties to the lowest key tile) applied to
+    the block heat instead of the predicted scores."""
+    return select_blocks(plan, heat)
+
+
+def recall(pred_mass: np.ndarray, oracle_mass: np.ndarray) -> np.ndarray:
+    """Recall of a predicted mask: its attention mass over the oracle mask's."""
+    return np.asarray(pred_mass, dtype=np.float64) / np.asarray(oracle_mass, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
 # O12: dense attention over natural order, by a library routine
 # ---------------------------------------------------------------------------
 

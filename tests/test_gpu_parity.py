@@ -161,6 +161,63 @@ def test_guard_padding_mass():
     check_attention(w, inp, g, op, qp, kp, sel)
 
 
+def test_oracle_mask_mass_and_recall():
+    """Oracle mask (veda_select_blocks on the block heat) and the attention
+    mass of the predicted and oracle masks (veda_mask_mass) against the
+    oracle: CSR bit-exact from the same fp32 heat, masses to fp64 rounding;
+    recall <= 1 (the oracle mask is the best mask under the same budgets)."""
+    w = small_workloads()[1]                  # two video segments + audio, two tile shapes, D = 128
+    inp = wl.make_inputs(w, seed=w.index)
+    g = gp.gpu_path(w, inp)
+    plan, dev = g["plan"], "cuda"
+    dense = vb.Plan.from_workload(w, budget_mode=wl.ALL_BLOCKS)
+    d_rp = torch.empty(plan.T + 1, dtype=torch.int32, device=dev)
+    d_col = torch.empty(dense.info["nnz"], dtype=torch.int32, device=dev)
+    dense.select(g["scores"], d_rp, d_col)
+    d_o, d_lse = dense.empty_perm(), torch.empty(plan.R, dtype=torch.float32, device=dev)
+    dense.attention(g["q_perm"], g["k_perm"], g["v_t"], d_rp, d_col, w.softmax_scale, d_o, d_lse)
+    heat = torch.empty(plan.info["total_pairs"], dtype=torch.float32, device=dev)
+    plan.heat(g["q_perm"], g["k_perm"], d_lse, w.softmax_scale, heat)
+    o_rp = torch.empty(plan.T + 1, dtype=torch.int32, device=dev)
+    o_col = torch.empty(plan.info["nnz"], dtype=torch.int32, device=dev)
+    plan.select(heat, o_rp, o_col)
+    m_pred = torch.empty(w.num_heads, dtype=torch.float64, device=dev)
+    m_orc = torch.empty(w.num_heads, dtype=torch.float64, device=dev)
+    plan.mask_mass(heat, g["row_ptr"], g["col_idx"], m_pred)
+    plan.mask_mass(heat, o_rp, o_col, m_orc)
+    torch.cuda.synchronize()
+
+    op = vo.Plan.from_workload(w)
+    heat_gpu = gp.split_scores(None, op, heat.cpu().numpy())
+    sel_o = vo.oracle_mask(op, heat_gpu)
+    rp, ci = vo.to_csr(op, sel_o)
+    assert np.array_equal(o_rp.cpu().numpy(), rp) and np.array_equal(o_col.cpu().numpy(), ci)
+    sel_p = _csr_to_selection(op, g["row_ptr"].cpu().numpy(), g["col_idx"].cpu().numpy())
+    ref_p, ref_o = vo.mask_mass(op, heat_gpu, sel_p), vo.mask_mass(op, heat_gpu, sel_o)
+    got_p, got_o = m_pred.cpu().numpy(), m_orc.cpu().numpy()
+    assert np.max(np.abs(got_p - ref_p) / ref_p) < 1e-12 and np.max(np.abs(got_o - ref_o) / ref_o) < 1e-12
+    r = got_p / got_o
+    print("oracle mask mass %s recall %s" % (np.round(got_o, 4), np.round(r, 4)), flush=True)
+    assert np.all(r <= 1.0 + 1e-12) and np.all(got_o <= 1.0 + 1e-6) and np.all(got_p > 0.0)
+    # the GPU heat itself against the oracle's (dense LSE in fp64)
+    qp, kp, _ = gp.oracle_front(op, inp)
+    _, L = vo.block_sparse_attention(op, qp, kp, kp, vo.all_blocks_selection(op), w.softmax_scale)
+    heat_ref = vo.block_heat(op, qp, kp, L, w.softmax_scale)
+    for h in range(w.num_heads):
+        assert np.max(np.abs(heat_gpu[h] - heat_ref[h])) <= gp.HEAT_ABS
+
+
+def _csr_to_selection(op, row_ptr, col):
+    sel, t = [], 0
+    for h in range(op.num_heads):
+        rows = []
+        for _ in range(op.heads[h].num_tiles):
+            rows.append(col[row_ptr[t]:row_ptr[t + 1]].astype(np.int64))
+            t += 1
+        sel.append(rows)
+    return sel
+
+
 @pytest.mark.parametrize("idx", [1, 2, 3])
 def test_config_full(idx):
     w = wl.workload(idx)

@@ -9,6 +9,7 @@ Features > "Veda sparse attention"); "Deploying this checkpoint" (intro,
 sections 0, 2 and 6); MiniMax-H3 cookbook page (heads, layers).
 """
 
+import itertools
 import math
 import os
 from fractions import Fraction
@@ -635,6 +636,78 @@ def test_heat_packed():
 
 
 # ---------------------------------------------------------------------------
+# P10: attention mass of a mask, oracle mask, recall
+# ---------------------------------------------------------------------------
+
+def _heat_and_probs(w, seed=11):
+    """Oracle heat of a workload and the token-level softmax probabilities
+    (library softmax over natural order) it summarises."""
+    plan = vo.Plan.from_workload(w)
+    N, H, D = w.num_tokens, w.num_heads, w.head_dim
+    q = _f64(_random_bf16((N, H, D), seed))
+    k = _f64(_random_bf16((N, H, D), seed + 1))
+    qp, kp = vo.permute_forward(plan, q), vo.permute_forward(plan, k)
+    _, L = vo.block_sparse_attention(plan, qp, kp, kp, vo.all_blocks_selection(plan), w.softmax_scale)
+    heat = vo.block_heat(plan, qp, kp, L, w.softmax_scale)
+    probs = [torch.softmax(w.softmax_scale * torch.from_numpy(q[:, h]) @ torch.from_numpy(k[:, h]).T,
+                           dim=-1).numpy() for h in range(H)]
+    return plan, heat, probs
+
+
+def check_mask_mass_token_level(mask_mass=vo.mask_mass):
+    """Mass of a mask = mean over valid query tokens of the probability they
+    put on the keys of their tile's kept key tiles, computed token by token."""
+    w = _small_partial_workload()
+    plan, heat, probs = _heat_and_probs(w)
+    rng = np.random.default_rng(3)
+    N = w.num_tokens
+    sel = []
+    for h in range(w.num_heads):
+        n = plan.heads[h].num_tiles
+        sel.append([np.sort(rng.choice(n, size=rng.integers(1, n + 1), replace=False)) for _ in range(n)])
+    got = mask_mass(plan, heat, sel)
+    for h in range(w.num_heads):
+        tile_of = _token_tile(plan, h, N)
+        kept = 0.0
+        for r in range(N):
+            keep_tiles = sel[h][tile_of[r]]
+            kept += probs[h][r, np.isin(tile_of, keep_tiles)].sum()
+        assert abs(got[h] - kept / N) < 1e-12, (h, got[h], kept / N)
+
+
+def test_mask_mass_token_level():
+    check_mask_mass_token_level()
+
+
+def test_mask_mass_all_blocks_is_one():
+    w = _small_packed_workload()
+    plan, heat, _ = _heat_and_probs(w)
+    m = vo.mask_mass(plan, heat, vo.all_blocks_selection(plan))
+    assert np.allclose(m, 1.0, atol=1e-12)
+
+
+def test_oracle_mask_is_best_under_the_budgets():
+    """Brute force: per row, no choice of key tiles with the row's budget that
+    contains the diagonal keeps more heat than the oracle mask; so the
+    recall of any such mask (the predictor's) is at most 1."""
+    w = _small_partial_workload()
+    plan, heat, _ = _heat_and_probs(w)
+    orc = vo.oracle_mask(plan, heat)
+    rng = np.random.default_rng(5)
+    scores = [rng.standard_normal(hm.shape) for hm in heat]
+    pred = vo.select_blocks(plan, scores)
+    for h in range(w.num_heads):
+        n = plan.heads[h].num_tiles
+        k = vo.row_budgets(plan, h).sum(axis=1)
+        for i in range(n):
+            best = max(heat[h][i, list(c)].sum() for c in itertools.combinations(range(n), int(k[i])) if i in c)
+            assert abs(heat[h][i, orc[h][i]].sum() - best) < 1e-15
+            assert len(orc[h][i]) == k[i] and i in orc[h][i]
+    r = vo.recall(vo.mask_mass(plan, heat, pred), vo.mask_mass(plan, heat, orc))
+    assert np.all(r <= 1.0 + 1e-15) and np.all(r > 0.0)
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each pin above must catch a plausible error in the oracle
 # ---------------------------------------------------------------------------
 
@@ -747,6 +820,13 @@ def _mut_heat_divide_by_volume(plan, q_perm, k_perm, lse, scale, heads=None):
     return heat
 
 
+def _mut_mass_unweighted(plan, heat, selection):
+    out = np.zeros(plan.num_heads)
+    for h in range(plan.num_heads):
+        out[h] = np.mean([heat[h][i, r].sum() for i, r in enumerate(selection[h])])
+    return out
+
+
 MUTATIONS = [
     ("tiling order inside a tile", lambda: check_handworked_tilings(_mut_tiles_colmajor)),
     ("mean over the padded volume", lambda: check_pool_special_cases(_mut_pool_divide_by_volume)),
@@ -759,6 +839,7 @@ MUTATIONS = [
     ("no padding mask on keys", lambda: check_attention_vs_library(_small_partial_workload(), "random",
                                                                   _mut_attention_no_padding_mask)),
     ("heat divided by 128", lambda: check_heat(_small_partial_workload(), _mut_heat_divide_by_volume)),
+    ("mask mass not weighted by valid queries", lambda: check_mask_mass_token_level(_mut_mass_unweighted)),
 ]
 
 
