@@ -1189,61 +1189,149 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
 // block heat from the dense LSE
 // ---------------------------------------------------------------------------
 //
-// One workgroup per (head, query tile); it walks every key tile of the head,
-// computes S^T as the attention kernel does, and sums
-// exp2(s * scale*log2e - lse*log2e) over valid (query, key) pairs.  Each
-// wave reduces its partial across lanes; the four wave partials are added in
-// a fixed order by thread 0 of the next iteration.
+// One workgroup (4 waves, 32 queries each) per (head, query tile); it walks
+// every key tile of the head with S^T = K Q^T on the matrix core as the
+// attention kernel does, and sums exp2(s*c - lse*log2(e)) over valid
+// (query, key) pairs.  Key tiles stream through two LDS buffers (A for even
+// j, B for odd j) with asynchronous copies one tile ahead; inside a tile the
+// four 32-key groups are software-pipelined (QK^T MFMAs of group g with the
+// exp/sum VALU work of group g-1).
+//
+// Padding keys hold zero rows of K, so their logit is exactly 0 and their
+// term is exp(-lse[r]); the fast variant sums all 128 keys and subtracts the
+// lane's padding count times that term.  A workgroup with a valid query whose
+// exp(-lse) exceeds 1/16 (where that subtraction could cancel) masks the
+// padding keys explicitly instead.  Each wave reduces its partial over lanes;
+// thread 0 adds the four wave partials in a fixed order one tile later.
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) heat_kernel(DevPlan p, const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const float* __restrict__ lse, float scale_log2,
                                                           float* __restrict__ heat) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kTile * D];
+  __shared__ __attribute__((aligned(16))) uint16_t ka0[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t ka1[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t kb0[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t kb1[64 * D];
   __shared__ float red[2][4];
+  __shared__ int32_t masked_s;
+  __shared__ uint8_t vcnt[kMaxHeatTiles];   // valid counts of the head's tiles (no vector loads in the loop)
   const int t = blockIdx.x;
-  const int h = p.row_head[t];
-  const DevShape& sh = p.shape[p.head_shape[h]];
+  const int h = uni(p.row_head[t]);
+  const DevShape& sh = p.shape[uni(p.head_shape[h])];
   const int n = sh.num_tiles;
-  const int i = t - p.head_tile_off[h];
-  const int ni = sh.valid[i];
-  const int64_t hrow = p.head_row_off[h];
+  const int i = t - uni(p.head_tile_off[h]);
+  const int ni = uni(sh.valid[i]);
+  const int64_t hrow = uni64(p.head_row_off[h]);
   const int64_t row0 = hrow + (int64_t)kTile * i;
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + hrow * D, (int64_t)n * kTile * D * 2);
+  const int wave = uni(threadIdx.x >> 6);
   const int w = threadIdx.x >> 6, lane = lane_id(), ln = lane & 31, hl = lane >> 5;
+  const int koff = k_lane_offset<D>(threadIdx.x);
   const int qr = 32 * w + ln;
   const bool qvalid = qr < ni;
+  const float c = scale_log2;
   bf16x8 qf[D / 16];
   const uint16_t* qrow = q + (row0 + qr) * D + 8 * hl;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld16(qrow + 16 * s));
   const float l2 = qvalid ? lse[row0 + qr] * 1.4426950408889634f : 0.0f;
+  const float e_pad = __builtin_amdgcn_exp2f(-l2);   // a padding key's term
+  if (threadIdx.x == 0) masked_s = 0;
+  for (int e = threadIdx.x; e < n; e += kThreads) vcnt[e] = (uint8_t)sh.valid[e];
+  __syncthreads();
+  if (__any(qvalid && !(e_pad <= 0.0625f)) && lane == 0) masked_s = 1;
+  __syncthreads();
+  const bool masked = uni(masked_s) != 0;
   float* hrow_out = heat + p.head_pair_off[h] + (int64_t)i * n;
   const float inv_ni = 1.0f / (float)ni;
-  for (int j = 0; j <= n; ++j) {
-    __syncthreads();
-    if (j > 0 && threadIdx.x == 0) {
-      const float* rr = red[(j - 1) & 1];
-      hrow_out[j - 1] = (((rr[0] + rr[1]) + rr[2]) + rr[3]) * inv_ni;
-    }
-    if (j == n) break;
-    const int nj = sh.valid[j];
-    load_kv_tile<D>(ks, nullptr, k + (hrow + (int64_t)kTile * j) * D, nullptr);
-    __syncthreads();
-    f32x16 sacc[4];
-    qk_block<D>(ks, qf, sacc);
-    float part = 0.0f;
-    if (qvalid) {
+
+  // sum of the lane's 64 terms of key tile j (nj valid keys) from one buffer
+  auto tile_sum = [&](const uint16_t* __restrict__ k0, const uint16_t* __restrict__ k1, int nj, auto msk)
+      __attribute__((always_inline)) {
+    constexpr bool M = decltype(msk)::value;
+    const f32x16 zero16 = {};
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto esum = [&](const f32x16& sg, int kt) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], scale_log2, -l2));
-          part += (sacc_key(kt, r, hl) < nj) ? pv : 0.0f;
-        }
+      for (int r = 0; r < 16; ++r) {
+        float e = __builtin_amdgcn_exp2f(fmaf(sg[r], c, -l2));
+        if (M) e = (sacc_key(kt, r, hl) < nj) ? e : 0.0f;
+        acc[r & 3] += e;
+      }
+    };
+    f32x16 s0 = qk_group<D>(k0, qf, 0, zero16);
+    interleave_step<8, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s1 = qk_group<D>(k0, qf, 1, zero16);
+    esum(s0, 0);
+    interleave_step<8, 6>();
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s2 = qk_group<D>(k1, qf, 2, zero16);
+    esum(s1, 1);
+    interleave_step<8, 6>();
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s3 = qk_group<D>(k1, qf, 3, zero16);
+    esum(s2, 2);
+    interleave_step<8, 6>();
+    __builtin_amdgcn_sched_barrier(0);
+    esum(s3, 3);
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  };
+
+  // Tile j's partial: the fast variant subtracts the lane's padding terms.
+  // The lane holds 64 keys, half of every 16-key run, so for nj valid keys
+  // its padding count is half_pads(nj, hl).
+  auto do_tile = [&](int j, auto bufb) {
+    constexpr bool BB = decltype(bufb)::value;   // buffer B (odd j) or A, fixed at compile time
+    const uint16_t* __restrict__ k0 = BB ? kb0 : ka0;
+    const uint16_t* __restrict__ k1 = BB ? kb1 : ka1;
+    const int nj = uni(vcnt[j]);
+    float part;
+    if (masked) {
+      part = tile_sum(k0, k1, nj, BoolC<true>{});
+    } else {
+      part = tile_sum(k0, k1, nj, BoolC<false>{});
+      part = fmaf(-(float)half_pads(nj, hl), e_pad, part);
     }
+    if (!qvalid) part = 0.0f;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
     if (lane == 0) red[j & 1][w] = part;
+  };
+
+  // Iteration j: wait for K(j), copy K(j+1) into the other buffer, work on
+  // tile j; thread 0 writes tile j-1's value.  The loop body handles an odd
+  // j (buffer B) and the following even j (buffer A), so the kernel has four
+  // copy call sites; the first iteration (j = -1) only copies K(0).
+  for (int j = -1; j < n; j += 2) {
+    // odd j (K(j) in B), copies K(j+1) into A
+    dma_sync<0>();
+    if (j >= 1 && threadIdx.x == 0) {
+      const float* rr = red[(j - 1) & 1];
+      hrow_out[j - 1] = (((rr[0] + rr[1]) + rr[2]) + rr[3]) * inv_ni;
+    }
+    if (j + 1 < n) {
+      dma_k_half<D>(ka0, rk, (j + 1) * kTile * D * 2, koff, wave, 0);
+      dma_k_half<D>(ka1, rk, (j + 1) * kTile * D * 2, koff, wave, 1);
+    }
+    if (j >= 0) do_tile(j, BoolC<true>{});
+    // even j + 1 (K(j+1) in A), copies K(j+2) into B
+    if (j + 1 >= n) break;
+    dma_sync<0>();
+    if (j >= 0 && threadIdx.x == 0) {
+      const float* rr = red[j & 1];
+      hrow_out[j] = (((rr[0] + rr[1]) + rr[2]) + rr[3]) * inv_ni;
+    }
+    if (j + 2 < n) {
+      dma_k_half<D>(kb0, rk, (j + 2) * kTile * D * 2, koff, wave, 0);
+      dma_k_half<D>(kb1, rk, (j + 2) * kTile * D * 2, koff, wave, 1);
+    }
+    do_tile(j + 1, BoolC<false>{});
+  }
+  dma_sync<0>();
+  if (threadIdx.x == 0) {
+    const float* rr = red[(n - 1) & 1];
+    hrow_out[n - 1] = (((rr[0] + rr[1]) + rr[2]) + rr[3]) * inv_ni;
   }
 }
 

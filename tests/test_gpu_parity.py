@@ -161,6 +161,33 @@ def test_guard_padding_mass():
     check_attention(w, inp, g, op, qp, kp, sel)
 
 
+def test_heat_masked_variant():
+    """Block heat where exp(-lse) is large (all logits far below zero, partial
+    tiles): the heat kernel must mask padding keys explicitly rather than
+    subtract their terms."""
+    w = _guard_workload()
+    inp = wl.make_inputs(w, seed=w.index)
+    gen = torch.Generator().manual_seed(9)
+    q = 0.1 * torch.randn(inp["q"].shape, generator=gen)
+    k = 0.1 * torch.randn(inp["k"].shape, generator=gen)
+    q[..., 0] += 20.0
+    k[..., 0] -= 20.0
+    inp["q"], inp["k"] = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    g = gp.gpu_path(w, inp)                  # ALL budget: its LSE is the dense LSE
+    plan = g["plan"]
+    heat = torch.empty(plan.info["total_pairs"], dtype=torch.float32, device="cuda")
+    plan.heat(g["q_perm"], g["k_perm"], g["lse"], w.softmax_scale, heat)
+    torch.cuda.synchronize()
+    op = vo.Plan.from_workload(w)
+    qp, kp, _ = gp.oracle_front(op, inp)
+    _, L = vo.block_sparse_attention(op, qp, kp, kp, vo.all_blocks_selection(op), w.softmax_scale)
+    assert np.nanmax(L) < -20.0                # exp(-lse) far above 1/16
+    heat_ref = vo.block_heat(op, qp, kp, L, w.softmax_scale)
+    heat_gpu = gp.split_scores(None, op, heat.cpu().numpy())
+    for h in range(w.num_heads):
+        assert np.max(np.abs(heat_gpu[h] - heat_ref[h])) <= gp.HEAT_ABS, h
+
+
 def test_oracle_mask_mass_and_recall():
     """Oracle mask (veda_select_blocks on the block heat) and the attention
     mass of the predicted and oracle masks (veda_mask_mass) against the
