@@ -546,6 +546,71 @@ def recall(pred_mass: np.ndarray, oracle_mass: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# O14: tile-plan search (relative output error under the best mask, vote)
+# ---------------------------------------------------------------------------
+
+def relative_output_error(o: np.ndarray, o_ref: np.ndarray) -> np.ndarray:
+    """Per head: sum over tokens and channels of (o - o_ref)^2 over the sum of
+    o_ref^2 (the relative output MSE of reading A21).  o, o_ref: [N, H, D]."""
+    d = np.asarray(o, dtype=np.float64) - np.asarray(o_ref, dtype=np.float64)
+    r = np.asarray(o_ref, dtype=np.float64)
+    return np.einsum("nhd,nhd->h", d, d) / np.einsum("nhd,nhd->h", r, r)
+
+
+def tile_plan_errors(segments, num_heads: int, head_dim: int, candidates, budget_mode: int, keep_num: int,
+                     keep_den: int, fixed_k: int, samples, scale: float) -> np.ndarray:
+    """Oracle tile-plan search, error table (reading A21; Miowtion project
+    page, Key Features: oracle tile-plan search by relative output MSE under
+    the best mask).  For every sample s (q, k, v fp64 [N, H, D]) and
+    candidate tile shape c (used by every head): the best mask is the oracle
+    mask (top-k of the dense-LSE block heat under the budgets, O13), the
+    sparse output is attention over it, and err[s, c, h] is its relative
+    output error against dense attention over all tokens."""
+    S, C, H = len(samples), len(candidates), num_heads
+    err = np.zeros((S, C, H), dtype=np.float64)
+    for si, (q, k, v) in enumerate(samples):
+        o_dense, _ = dense_attention(q, k, v, scale)
+        for ci, shape in enumerate(candidates):
+            plan = Plan(segments, H, head_dim, [tuple(shape)] * H, budget_mode, keep_num, keep_den, fixed_k)
+            qp, kp, vp = permute_forward(plan, q), permute_forward(plan, k), permute_forward(plan, v)
+            _, L = block_sparse_attention(plan, qp, kp, vp, all_blocks_selection(plan), scale)
+            heat = block_heat(plan, qp, kp, L, scale)
+            o, _ = block_sparse_attention(plan, qp, kp, vp, oracle_mask(plan, heat), scale)
+            err[si, ci] = relative_output_error(permute_inverse(plan, np.nan_to_num(o)), o_dense)
+    return err
+
+
+def vote_tile_shapes(err: np.ndarray, max_shapes: int = 2) -> np.ndarray:
+    """Majority vote over samples, at most `max_shapes` shapes per layer
+    (reading A21).  err [S, C, H] -> candidate index per head.
+
+    1. Each sample votes, per head, for its lowest-error candidate.
+    2. A head's preferred candidate is the one with the most votes.
+    3. The layer keeps the `max_shapes` candidates preferred by the most heads.
+    4. A head whose preferred candidate is kept uses it; any other head uses
+       the kept candidate with the lowest mean error over the samples.
+    Every tie goes to the lower candidate index.
+    """
+    S, C, H = err.shape
+    votes = np.zeros((C, H), dtype=np.int64)
+    for s in range(S):
+        for h in range(H):
+            votes[int(np.argmin(err[s, :, h])), h] += 1
+    pref = np.array([int(np.argmax(votes[:, h])) for h in range(H)], dtype=np.int64)
+    heads_for = np.bincount(pref, minlength=C)
+    order = sorted(range(C), key=lambda c: (-heads_for[c], c))
+    kept = [c for c in order[:max_shapes] if heads_for[c] > 0]
+    mean = err.mean(axis=0)
+    out = np.empty(H, dtype=np.int64)
+    for h in range(H):
+        if pref[h] in kept:
+            out[h] = pref[h]
+        else:
+            out[h] = min(kept, key=lambda c: (mean[c, h], c))
+    return out
+
+
+# ---------------------------------------------------------------------------
 # O12: dense attention over natural order, by a library routine
 # ---------------------------------------------------------------------------
 

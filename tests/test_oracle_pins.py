@@ -708,6 +708,96 @@ def test_oracle_mask_is_best_under_the_budgets():
 
 
 # ---------------------------------------------------------------------------
+# P11: tile-plan search
+# ---------------------------------------------------------------------------
+
+def test_relative_output_error_closed_forms():
+    rng = np.random.default_rng(1)
+    ref = rng.standard_normal((50, 3, 8))
+    eps = np.array([0.5, 0.1, 0.0])
+    o = ref * (1.0 + eps)[None, :, None]
+    assert np.allclose(vo.relative_output_error(o, ref), eps ** 2, rtol=1e-12, atol=1e-30)
+    assert np.allclose(vo.relative_output_error(np.zeros_like(ref), ref), 1.0, rtol=1e-15)
+
+
+_SEARCH_CANDIDATES = ((1, 8, 16), (2, 8, 8), (4, 4, 8))
+
+
+def _frame_local_samples(n_samples=2, heads=2, dim=64):
+    """q = k = a one-hot of the token's frame (t) plus small noise: attention
+    stays inside each frame of a (4, 8, 16) grid."""
+    segs = (wl.Segment(wl.VIDEO3D, (4, 8, 16), 0),)
+    N = 512
+    t_of = np.arange(N) // 128
+    out = []
+    for s in range(n_samples):
+        g = np.random.default_rng(100 + s)
+        base = np.zeros((N, heads, dim))
+        base[np.arange(N), :, t_of] = 10.0
+        q = _f64(torch.from_numpy(base + 0.05 * g.standard_normal((N, heads, dim))).to(torch.bfloat16))
+        k = _f64(torch.from_numpy(base + 0.05 * g.standard_normal((N, heads, dim))).to(torch.bfloat16))
+        v = _f64(torch.from_numpy(g.standard_normal((N, heads, dim))).to(torch.bfloat16))
+        out.append((q, k, v))
+    return segs, out
+
+
+def check_search_prefers_frame_tiles(errors=vo.tile_plan_errors):
+    """Attention confined to frames, two key tiles per row.  A (1, 8, 16)
+    tile is a whole frame: its diagonal block already holds the mass.  A
+    (2, 8, 8) tile is half of two frames: the diagonal plus the one other
+    tile with the other halves (the heat picks it) hold the mass.  A (4, 4, 8)
+    tile is a quarter of four frames and needs four blocks: large error."""
+    segs, samples = _frame_local_samples()
+    err = errors(segs, 2, 64, _SEARCH_CANDIDATES, wl.FIXED_K, 1, 10, 2, samples, 1.0 / 8.0)
+    assert np.all(err[:, :2, :] < 1e-3), err[:, :2, :]
+    assert np.all(err[:, 2, :] > 0.1), err[:, 2, :]
+    assert set(vo.vote_tile_shapes(err).tolist()) <= {0, 1}
+
+
+def test_search_prefers_frame_tiles():
+    check_search_prefers_frame_tiles()
+
+
+def test_search_all_blocks_has_no_error():
+    segs, samples = _frame_local_samples(n_samples=1)
+    err = vo.tile_plan_errors(segs, 2, 64, _SEARCH_CANDIDATES, wl.ALL_BLOCKS, 1, 10, 0, samples, 1.0 / 8.0)
+    assert np.all(err < 1e-25), err
+
+
+def test_vote_golden():
+    """Hand-worked vote tables (every tie to the lower index)."""
+    e = np.zeros((3, 4, 5))
+    # per sample lowest error:   head0: c2,c2,c1  head1: c0,c1,c1  head2: c3,c3,c3
+    #                            head3: c1,c2,c3 (one vote each -> c1)   head4: c0,c0,c2
+    best = [[2, 0, 3, 1, 0], [2, 1, 3, 2, 0], [1, 1, 3, 3, 2]]
+    for s in range(3):
+        for h in range(5):
+            e[s, :, h] = 1.0 + h + np.arange(4) * 0.01
+            e[s, best[s][h], h] = 0.5
+    # preferred: c2, c1, c3, c1, c0 -> heads per candidate: c0 1, c1 2, c2 1, c3 1
+    # kept (2 shapes): c1 (2 heads), then c0 (tie of 1 head with c2, c3 -> lowest index)
+    # heads 1, 3, 4 keep their preferred; heads 0 and 2 take the kept one with the lower mean error
+    got = vo.vote_tile_shapes(e, max_shapes=2)
+    # head 0 means: c0 = (1.0+1.0+1.0)/3 ... c1 = (1.01+1.01+0.5)/3 -> c1; head 2: c0 = 3.0, c1 = 3.01 -> c0
+    assert np.array_equal(got, [1, 1, 0, 1, 0]), got
+    assert np.array_equal(vo.vote_tile_shapes(e, max_shapes=4), [2, 1, 3, 1, 0])
+    assert np.array_equal(vo.vote_tile_shapes(e, max_shapes=1), [1, 1, 1, 1, 1])
+
+
+def test_vote_invariants_random():
+    rng = np.random.default_rng(8)
+    for _ in range(200):
+        S, C, H = rng.integers(1, 5), rng.integers(1, 6), rng.integers(1, 9)
+        e = rng.integers(0, 4, size=(S, C, H)).astype(np.float64)   # many ties
+        for m in (1, 2, 3):
+            out = vo.vote_tile_shapes(e, m)
+            assert len(set(out.tolist())) <= m and np.all((out >= 0) & (out < C))
+        # a head every sample agrees on, with at most two distinct such shapes, keeps its shape
+        if S == 1 and len(set(np.argmin(e[0], axis=0).tolist())) <= 2:
+            assert np.array_equal(vo.vote_tile_shapes(e, 2), np.argmin(e[0], axis=0))
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each pin above must catch a plausible error in the oracle
 # ---------------------------------------------------------------------------
 
@@ -827,6 +917,23 @@ def _mut_mass_unweighted(plan, heat, selection):
     return out
 
 
+def _mut_search_lowest_heat(segments, num_heads, head_dim, candidates, budget_mode, keep_num, keep_den, fixed_k,
+                            samples, scale):
+    """Takes the blocks of lowest heat as the best mask."""
+    S, C, H = len(samples), len(candidates), num_heads
+    err = np.zeros((S, C, H))
+    for si, (q, k, v) in enumerate(samples):
+        o_dense, _ = vo.dense_attention(q, k, v, scale)
+        for ci, shape in enumerate(candidates):
+            plan = vo.Plan(segments, H, head_dim, [tuple(shape)] * H, budget_mode, keep_num, keep_den, fixed_k)
+            qp, kp, vp = (vo.permute_forward(plan, x) for x in (q, k, v))
+            _, L = vo.block_sparse_attention(plan, qp, kp, vp, vo.all_blocks_selection(plan), scale)
+            heat = vo.block_heat(plan, qp, kp, L, scale)
+            o, _ = vo.block_sparse_attention(plan, qp, kp, vp, vo.oracle_mask(plan, [-x for x in heat]), scale)
+            err[si, ci] = vo.relative_output_error(vo.permute_inverse(plan, np.nan_to_num(o)), o_dense)
+    return err
+
+
 MUTATIONS = [
     ("tiling order inside a tile", lambda: check_handworked_tilings(_mut_tiles_colmajor)),
     ("mean over the padded volume", lambda: check_pool_special_cases(_mut_pool_divide_by_volume)),
@@ -840,6 +947,7 @@ MUTATIONS = [
                                                                   _mut_attention_no_padding_mask)),
     ("heat divided by 128", lambda: check_heat(_small_partial_workload(), _mut_heat_divide_by_volume)),
     ("mask mass not weighted by valid queries", lambda: check_mask_mass_token_level(_mut_mass_unweighted)),
+    ("search mask of the lowest heat", lambda: check_search_prefers_frame_tiles(_mut_search_lowest_heat)),
 ]
 
 

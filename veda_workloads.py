@@ -138,16 +138,20 @@ def _flush_round(x: torch.Tensor) -> torch.Tensor:
     return x.to(torch.bfloat16)
 
 
-def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
+def make_inputs(w: Workload, seed: Optional[int] = None, bias_seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
     """Seeded host tensors for one workload.
 
     Returns q, k, v: bf16 [N, H, D] (token-major, as a fused QKV projection
     emits them) and w_q, w_k: fp32 [H, D, 3D] predictor projection weights
     (columns ordered mean | max | min), std 0.02.
     Draw order: Q, K, V noise; per-head bias parameters; W_q; W_k.
+    bias_seed: draw the per-head bias parameters from their own generator
+    with this seed instead (several samples of one layer: the heads keep their
+    length scales while the noise changes).
     """
     seed = w.index if seed is None else seed
     gen = torch.Generator("cpu").manual_seed(seed)
+    bgen = gen if bias_seed is None else torch.Generator("cpu").manual_seed(bias_seed)
     N, H, D = w.num_tokens, w.num_heads, w.head_dim
     q = torch.randn((N, H, D), generator=gen, dtype=torch.float32)
     k = torch.randn((N, H, D), generator=gen, dtype=torch.float32)
@@ -156,9 +160,9 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tens
         F = D // 2
         amp = math.sqrt(3.0 * math.sqrt(D) / F)
         for h in range(H):
-            lt = _log_uniform(gen, 1.0, 4.0)
-            ls = _log_uniform(gen, 2.0, 8.0)
-            g = torch.randn((F, 3), generator=gen, dtype=torch.float64)
+            lt = _log_uniform(bgen, 1.0, 4.0)
+            ls = _log_uniform(bgen, 2.0, 8.0)
+            g = torch.randn((F, 3), generator=bgen, dtype=torch.float64)
             omega = g / torch.tensor([lt, ls, ls], dtype=torch.float64)
             for seg in w.segments:
                 if seg.kind != VIDEO3D:
