@@ -90,6 +90,8 @@ _SIGS = {
     "veda_block_sparse_attn_fwd": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _P, _P, _P]),
     "veda_block_heat": (_I32, [_P, _P, _P, _P, ctypes.c_float, _P, _P]),
     "veda_mask_mass": (_I32, [_P, _P, _P, _P, _P, _P]),
+    "veda_output_error": (_I32, [_P, _P, _P, _P, _P]),
+    "veda_tile_plan_vote": (_I32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -259,6 +261,23 @@ def veda_mask_mass(plan: int, heat, row_ptr, col_idx, mass, stream=None) -> None
     _check(lib().veda_mask_mass(plan, _ptr(heat), _ptr(row_ptr), _ptr(col_idx), _ptr(mass), _stream(stream)))
 
 
+def veda_output_error(plan: int, o, o_ref, err, stream=None) -> None:
+    _check(lib().veda_output_error(plan, _ptr(o), _ptr(o_ref), _ptr(err), _stream(stream)))
+
+
+def veda_tile_plan_vote(err, max_shapes: int = 2):
+    """err: host float64 array [samples, candidates, heads]; returns int32
+    [heads] candidate indices (host-only step, no device)."""
+    import numpy as np
+    e = np.ascontiguousarray(err, dtype=np.float64)
+    if e.ndim != 3:
+        raise ValueError("err must be [samples, candidates, heads]")
+    out = np.zeros(e.shape[2], dtype=np.int32)
+    _check(lib().veda_tile_plan_vote(e.shape[0], e.shape[1], e.shape[2], e.ctypes.data, int(max_shapes),
+                                     out.ctypes.data))
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Plan: owns the handle and the device tables; checks tensor sizes
 # ---------------------------------------------------------------------------
@@ -418,6 +437,14 @@ class Plan:
         self._expect(lse, (self.R,), torch.float32, "lse")
         self._expect(heat, (self.info["total_pairs"],), torch.float32, "heat")
         veda_block_heat(self.handle, q, k, lse, scale, heat, stream)
+
+    def output_error(self, o, o_ref, err, stream=None):
+        import torch
+        nat = (self.N, self.H, self.D)
+        self._expect(o, nat, torch.bfloat16, "o")
+        self._expect(o_ref, nat, torch.bfloat16, "o_ref")
+        self._expect(err, (self.H,), torch.float64, "err")
+        veda_output_error(self.handle, o, o_ref, err, stream)
 
     def mask_mass(self, heat, row_ptr, col_idx, mass, stream=None):
         import torch

@@ -706,4 +706,67 @@ veda_status veda_mask_mass(const veda_plan* p, const float* heat, const int32_t*
   return launched(launch_mask_mass(p->dev, heat, row_ptr, col_idx, mass, (hipStream_t)stream), "mask mass");
 }
 
+veda_status veda_output_error(const veda_plan* p, const void* o, const void* o_ref, double* err, void* stream) {
+  veda_status st = check_plan_ready(p);
+  if (st) return st;
+  if ((st = check_ptr(o, "o")) || (st = check_ptr(o_ref, "o_ref")) || (st = check_ptr(err, "err"))) return st;
+  return launched(launch_output_error(p->dev, p->info.num_tokens, o, o_ref, err, (hipStream_t)stream),
+                  "output error");
+}
+
+veda_status veda_tile_plan_vote(int32_t samples, int32_t candidates, int32_t heads, const double* err,
+                                int32_t max_shapes, int32_t* choice) {
+  if (samples <= 0 || candidates <= 0 || heads <= 0 || max_shapes <= 0)
+    return fail(VEDA_ERR_INVALID_ARG, "tile plan vote: counts must be positive");
+  if (!err || !choice) return fail(VEDA_ERR_INVALID_ARG, "tile plan vote: null pointer");
+  const int64_t S = samples, C = candidates, H = heads;
+  for (int64_t e = 0; e < S * C * H; ++e)
+    if (!std::isfinite(err[e])) return fail(VEDA_ERR_INVALID_ARG, "tile plan vote: non-finite error");
+  auto at = [&](int64_t s, int64_t c, int64_t h) { return err[(s * C + c) * H + h]; };
+  // 1-2: per sample and head the lowest-error candidate; per head the most voted
+  std::vector<int32_t> pref(H);
+  for (int64_t h = 0; h < H; ++h) {
+    std::vector<int64_t> votes(C, 0);
+    for (int64_t s = 0; s < S; ++s) {
+      int64_t best = 0;
+      for (int64_t c = 1; c < C; ++c)
+        if (at(s, c, h) < at(s, best, h)) best = c;
+      ++votes[best];
+    }
+    int64_t top = 0;
+    for (int64_t c = 1; c < C; ++c)
+      if (votes[c] > votes[top]) top = c;
+    pref[h] = (int32_t)top;
+  }
+  // 3: the max_shapes candidates preferred by the most heads
+  std::vector<int64_t> heads_for(C, 0);
+  for (int64_t h = 0; h < H; ++h) ++heads_for[pref[h]];
+  std::vector<int32_t> order(C);
+  for (int64_t c = 0; c < C; ++c) order[c] = (int32_t)c;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return heads_for[a] > heads_for[b]; });
+  std::vector<int32_t> kept;
+  for (int64_t r = 0; r < C && (int64_t)kept.size() < max_shapes; ++r)
+    if (heads_for[order[r]] > 0) kept.push_back(order[r]);
+  // 4: preferred if kept, else the kept candidate with the lowest mean error
+  for (int64_t h = 0; h < H; ++h) {
+    if (std::find(kept.begin(), kept.end(), pref[h]) != kept.end()) {
+      choice[h] = pref[h];
+      continue;
+    }
+    int32_t best = -1;
+    double best_mean = 0.0;
+    for (int32_t c : kept) {
+      double m = 0.0;
+      for (int64_t s = 0; s < S; ++s) m += at(s, c, h);
+      m /= (double)S;
+      if (best < 0 || m < best_mean || (m == best_mean && c < best)) {
+        best = c;
+        best_mean = m;
+      }
+    }
+    choice[h] = best;
+  }
+  return VEDA_OK;
+}
+
 }  // extern "C"

@@ -66,6 +66,8 @@ hipError_t launch_heat(const DevPlan& p, const void* q, const void* k, const flo
                        float scale, float* heat, hipStream_t s);
 hipError_t launch_mask_mass(const DevPlan& p, const float* heat, const int32_t* row_ptr, const int32_t* col_idx,
                             double* mass, hipStream_t s);
+hipError_t launch_output_error(const DevPlan& p, int64_t num_tokens, const void* o, const void* o_ref, double* err,
+                               hipStream_t s);
 
 // Scratch the score call needs: pooled features of Q and K (fp32 [T, 3D]
 // each) and their projections (fp32 [T, D] each).

@@ -1378,6 +1378,48 @@ __global__ void __launch_bounds__(kThreads) mask_mass_kernel(DevPlan p, const fl
   if (threadIdx.x == 0) mass[h] = kept_s[0] / cnt_s[0];
 }
 
+// ---------------------------------------------------------------------------
+// relative output error of two natural-order outputs
+// ---------------------------------------------------------------------------
+//
+// One workgroup of 512 threads per head.  Thread x takes the 16-byte chunks
+// x, x + 512, ... of the head's N x D values (strided by H*D between
+// tokens), accumulates (o - o_ref)^2 and o_ref^2 in fp64, and the partials
+// are combined by a fixed-order tree in LDS.
+template <int D>
+__global__ void __launch_bounds__(512) output_error_kernel(int64_t num_tokens, int num_heads,
+                                                          const uint16_t* __restrict__ o,
+                                                          const uint16_t* __restrict__ o_ref,
+                                                          double* __restrict__ err) {
+  constexpr int CH = D / 8;
+  __shared__ double num_s[512];
+  __shared__ double den_s[512];
+  const int h = blockIdx.x;
+  double num = 0.0, den = 0.0;
+  for (int64_t c = threadIdx.x; c < num_tokens * CH; c += 512) {
+    const int64_t n = c / CH, off = (n * num_heads + h) * D + 8 * (c % CH);
+    const u32x4 a = ld16(o + off), b = ld16(o_ref + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double a0 = bf16_to_f32((uint16_t)(a[e] & 0xffff)), a1 = bf16_to_f32((uint16_t)(a[e] >> 16));
+      const double b0 = bf16_to_f32((uint16_t)(b[e] & 0xffff)), b1 = bf16_to_f32((uint16_t)(b[e] >> 16));
+      num += (a0 - b0) * (a0 - b0) + (a1 - b1) * (a1 - b1);
+      den += b0 * b0 + b1 * b1;
+    }
+  }
+  num_s[threadIdx.x] = num;
+  den_s[threadIdx.x] = den;
+  __syncthreads();
+  for (int w = 256; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      num_s[threadIdx.x] += num_s[threadIdx.x + w];
+      den_s[threadIdx.x] += den_s[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) err[h] = num_s[0] / den_s[0];
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1508,6 +1550,19 @@ hipError_t launch_mask_mass(const DevPlan& p, const float* heat, const int32_t* 
                             double* mass, hipStream_t s) {
   hipLaunchKernelGGL(mask_mass_kernel, dim3((unsigned)p.num_heads), dim3(kThreads), 0, s, p, heat, row_ptr, col_idx,
                      mass);
+  return hipGetLastError();
+}
+
+hipError_t launch_output_error(const DevPlan& p, int64_t num_tokens, const void* o, const void* o_ref, double* err,
+                               hipStream_t s) {
+  const uint16_t* a = static_cast<const uint16_t*>(o);
+  const uint16_t* b = static_cast<const uint16_t*>(o_ref);
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL(output_error_kernel<128>, dim3((unsigned)p.num_heads), dim3(512), 0, s, num_tokens,
+                       p.num_heads, a, b, err);
+  else
+    hipLaunchKernelGGL(output_error_kernel<64>, dim3((unsigned)p.num_heads), dim3(512), 0, s, num_tokens,
+                       p.num_heads, a, b, err);
   return hipGetLastError();
 }
 

@@ -279,6 +279,31 @@ veda_status veda_block_heat(const veda_plan* plan, const void* q, const void* k,
 veda_status veda_mask_mass(const veda_plan* plan, const float* heat, const int32_t* row_ptr,
                            const int32_t* col_idx, double* mass, void* stream);
 
+/* Relative output error of a sparse attention output against a reference
+ * (Miowtion project page, Key Features: oracle tile-plan search by relative
+ * output MSE under the best mask).  Per head h, over every token and channel:
+ *   err[h] = sum (o - o_ref)^2 / sum o_ref^2
+ *   o, o_ref: device bf16 [N, H, D] (natural token order, as
+ *             veda_block_sparse_attn_fwd writes with VEDA_LAYOUT_NATURAL)
+ *   err:      device fp64 [num_heads]
+ * fp64 accumulation in a fixed order: bitwise reproducible. */
+veda_status veda_output_error(const veda_plan* plan, const void* o, const void* o_ref, double* err,
+                              void* stream);
+
+/* Tile-shape vote of the tile-plan search (same source): a host-only step
+ * on the error table of `samples` x `candidates` x `heads` (err[s][c][h],
+ * host fp64, row-major), e.g. veda_output_error of the output under each
+ * candidate tile shape's oracle mask for each sample.
+ *   1. every sample votes, per head, for its lowest-error candidate;
+ *   2. a head's preferred candidate is the one with the most votes;
+ *   3. the layer keeps the max_shapes candidates preferred by the most heads;
+ *   4. a head whose preferred candidate is kept uses it, any other head the
+ *      kept candidate with the lowest mean error over the samples.
+ * Every tie goes to the lower candidate index.  choice: host int32 [heads].
+ * VEDA_ERR_INVALID_ARG for non-positive counts or a non-finite error. */
+veda_status veda_tile_plan_vote(int32_t samples, int32_t candidates, int32_t heads, const double* err,
+                                int32_t max_shapes, int32_t* choice);
+
 #ifdef __cplusplus
 }
 #endif

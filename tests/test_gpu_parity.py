@@ -188,6 +188,55 @@ def test_heat_masked_variant():
         assert np.max(np.abs(heat_gpu[h] - heat_ref[h])) <= gp.HEAT_ABS, h
 
 
+def _search_case(kind):
+    """(segments, heads, dim, candidates, budget (mode, num, den, k), host samples)."""
+    cands = ((1, 8, 16), (2, 8, 8), (4, 4, 8))
+    if kind == "frame_local":
+        segs = (wl.Segment(wl.VIDEO3D, (4, 8, 16), 0),)
+        N, H, D = 512, 2, 64
+        t_of = np.arange(N) // 128
+        samples = []
+        for s in range(2):
+            g = np.random.default_rng(100 + s)
+            base = np.zeros((N, H, D))
+            base[np.arange(N), :, t_of] = 10.0
+            samples.append(tuple(torch.from_numpy(base * m + 0.05 * g.standard_normal((N, H, D))).to(torch.bfloat16)
+                                 for m in (1.0, 1.0, 0.0)))
+        return segs, H, D, cands, (wl.FIXED_K, 1, 10, 2), samples
+    # locality-biased layer: fixed per-head length scales, new noise per sample
+    w = wl.Workload(97, "search_layer", (wl.Segment(wl.VIDEO3D, (4, 16, 16), 0),), 4, 64, ((2, 8, 8),) * 4,
+                    wl.KEEP_RATIO, 1, 4)
+    samples = []
+    for s in range(2):
+        x = wl.make_inputs(w, seed=500 + s, bias_seed=97)
+        samples.append((x["q"], x["k"], x["v"]))
+    return w.segments, 4, 64, cands, (wl.KEEP_RATIO, 1, 4, 0), samples
+
+
+@pytest.mark.parametrize("kind", ["frame_local", "biased_layer"])
+def test_tile_plan_search(kind):
+    """Error table of the GPU search against the oracle's (tolerance from the
+    bf16 rounding of the two outputs compared), the vote bit-exact against
+    the oracle's vote on the same GPU table, and the chosen shapes against
+    the oracle's own choice where its margins are clear."""
+    from block_sparse_attention_10_amd import search
+    segs, H, D, cands, (mode, num, den, fk), samples = _search_case(kind)
+    scale = 1.0 / np.sqrt(D)
+    dev_samples = [tuple(t.to("cuda") for t in smp) for smp in samples]
+    err, choice = search.tile_plan_search(segs, H, D, cands, mode, num, den, fk, dev_samples, scale)
+    ref = vo.tile_plan_errors(segs, H, D, cands, mode, num, den, fk,
+                              [tuple(gp.f64(t) for t in smp) for smp in samples], scale)
+    print("%s: gpu err %s oracle err %s" % (kind, np.round(err, 5).tolist(), np.round(ref, 5).tolist()), flush=True)
+    tol = 2.0 * np.sqrt(ref) * 2.0 ** -7 + 2.0 ** -13
+    assert np.all(np.abs(err - ref) <= tol), np.abs(err - ref) - tol
+    assert np.array_equal(choice, vo.vote_tile_shapes(err, 2))
+    ref_choice = vo.vote_tile_shapes(ref, 2)
+    for h in range(H):   # where no sample's best candidate is within the tolerance of another
+        clear = all(np.sort(ref[s, :, h])[1] - np.sort(ref[s, :, h])[0] > 2 * tol[s].max() for s in range(len(samples)))
+        if clear:
+            assert choice[h] == ref_choice[h], h
+
+
 def test_oracle_mask_mass_and_recall():
     """Oracle mask (veda_select_blocks on the block heat) and the attention
     mass of the predicted and oracle masks (veda_mask_mass) against the

@@ -169,3 +169,17 @@ def test_compute_calls_check_on_host_before_any_launch():
         assert lib.veda_plan_upload(h, ctypes.c_void_p(0x1000), 16, None) == 4
     finally:
         vb.veda_plan_destroy(h)
+
+
+def test_tile_plan_vote_matches_oracle():
+    """The library's host-only vote step equals the oracle's on random error
+    tables full of ties, and on the hand-worked table."""
+    from oracle import veda_oracle as vo
+    rng = np.random.default_rng(21)
+    for _ in range(300):
+        S, C, H = (int(x) for x in rng.integers(1, 6, size=3))
+        e = rng.integers(0, 4, size=(S, C, H)).astype(np.float64) * 0.25
+        for m in (1, 2, 3):
+            assert np.array_equal(vb.veda_tile_plan_vote(e, m), vo.vote_tile_shapes(e, m))
+    with pytest.raises(vb.VedaError):
+        vb.veda_tile_plan_vote(np.full((1, 2, 2), np.nan))
