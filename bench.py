@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (known bytes) to scale HBM counters")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="rough budget of the oracle sample")
+    ap.add_argument("--search", action="store_true",
+                    help="also time the tile-plan search on the 8x32x32 grid (16 heads, D 128, 10%% keep, "
+                         "5 candidate shapes, 3 samples of one layer) and report it")
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                            "profiles", "traffic.json"))
     return ap.parse_args()
@@ -217,10 +220,39 @@ def main():
             "recall_mean": round(float((mp / mo).mean()), 4), "recall_min": round(float((mp / mo).min()), 4),
             "note": "synthetic inputs and a random-init predictor; the pages' 0.63 / 0.71 come from real "
                     "activations"}
+    if args.search:
+        out["tile_plan_search"] = time_search()
     if not args.no_cpu_baseline:
         print("bench: oracle CPU baseline (~%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inputs[0], args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+SEARCH_CANDIDATES = ((1, 8, 16), (2, 8, 8), (4, 4, 8), (2, 4, 16), (1, 16, 8))
+
+
+def time_search():
+    """Tile-plan search on one layer shaped like the 8x32x32 grid workload:
+    three samples (fixed per-head length scales, new noise), five candidate
+    shapes; one untimed run, then one timed run."""
+    from block_sparse_attention_10_amd import search
+    w = wl.Workload(98, "search_layer_8x32x32", (wl.Segment(wl.VIDEO3D, (8, 32, 32), 0),), 16, 128,
+                    ((4, 4, 8),) * 16, wl.KEEP_RATIO, 1, 10)
+    samples = []
+    for s in range(3):
+        x = wl.make_inputs(w, seed=700 + s, bias_seed=98)
+        samples.append((x["q"].cuda(), x["k"].cuda(), x["v"].cuda()))
+    args = (w.segments, w.num_heads, w.head_dim, SEARCH_CANDIDATES, w.budget_mode, w.keep_num, w.keep_den, 0,
+            samples, w.softmax_scale)
+    search.tile_plan_search(*args)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    err, choice = search.tile_plan_search(*args)
+    ms = 1e3 * (time.perf_counter() - t0)
+    counts = {str(SEARCH_CANDIDATES[c]): int((choice == c).sum()) for c in sorted(set(choice.tolist()))}
+    return {"ms": round(ms, 2), "samples": 3, "candidates": len(SEARCH_CANDIDATES), "heads": w.num_heads,
+            "grid": "8x32x32", "ms_per_sample_and_candidate": round(ms / (3 * len(SEARCH_CANDIDATES)), 3),
+            "heads_per_chosen_shape": counts}
 
 
 def _kernel_sha():
