@@ -231,9 +231,13 @@ veda_status veda_select_blocks(const veda_plan* plan, const float* scores, int32
  * row_ptr[t+1]) and computes, for each query slot r,
  *   O[r] = softmax_c(scale * q_r . k_c) v_c,  LSE[r] = log sum_c exp(scale q_r.k_c)
  * over the valid slots c of the listed key tiles (slots >= valid(j) are
- * masked: the only mask rule).  bf16 MFMA products, fp32 online softmax.
+ * masked: the only mask rule).  bf16 MFMA products, fp32 softmax.
  *   q, k:   device permuted bf16 [R, D]
  *   v_t:    device tile-transposed bf16 [T, D, 128]
+ * The padding slots of k (rows) and v_t (columns) must hold zeros, as
+ * veda_permute_qkv and veda_permute_tiles write them: the kernel removes the
+ * padding keys' share of the softmax sum by count instead of masking each
+ * logit (a padding key's logit is then exactly 0 and its PV term is 0).
  *   row_ptr, col_idx: device CSR as written by veda_select_blocks (or any CSR
  *           of this plan's shape with ascending, in-range, non-empty rows)
  *   o:      device bf16; o_layout VEDA_LAYOUT_PERMUTED: [R, D], rows of
@@ -255,7 +259,8 @@ veda_status veda_block_sparse_attn_fwd(const veda_plan* plan, const void* q, con
  * attention": teacher block heat from the dense LSE, fused kernel).
  * heat[i][j] = (1/valid(i)) * sum over valid query slots r of tile i and valid
  * key slots c of tile j of exp(scale * q_r . k_c - lse[r]), for every pair of
- * tiles of every head; with the dense LSE each row sums to 1.
+ * tiles of every head; with the dense LSE each row sums to 1.  The padding
+ * rows of k must hold zeros (as the permute entry points write them).
  *   q, k:  device permuted bf16 [R, D];  lse: device fp32 [R]
  *   heat:  device fp32 [sum_h n_h^2], layout of the scores.
  * A head may have at most 4096 tiles. */
