@@ -476,6 +476,63 @@ def block_sparse_attention(plan: Plan, q_perm, k_perm, v_perm,
 
 
 # ---------------------------------------------------------------------------
+# O15: block-sparse attention backward, per-key-tile lists
+# ---------------------------------------------------------------------------
+
+def mask_transpose(plan: Plan, selection: List[List[np.ndarray]]) -> List[List[np.ndarray]]:
+    """The transposed lists (reading A22): for every head and key tile j, the
+    query tiles whose rows selected j, ascending."""
+    out = []
+    for h in range(plan.num_heads):
+        n = plan.heads[h].num_tiles
+        cols: List[List[int]] = [[] for _ in range(n)]
+        for i, row in enumerate(selection[h]):
+            for j in row:
+                cols[int(j)].append(i)
+        out.append([np.array(c, dtype=np.int64) for c in cols])
+    return out
+
+
+def block_sparse_attention_backward(plan: Plan, q_perm, k_perm, v_perm, do_perm,
+                                    selection: List[List[np.ndarray]], scale: float):
+    """Gradients of the masked softmax attention O10 (reading A22; Miowtion
+    project page: the block-sparse backward the predictor and LoRA training
+    need), in fp64, by the textbook softmax backward per query tile row:
+      P = softmax(scale q K^T) over the valid keys of the selected tiles,
+      dV += P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
+      dQ = scale dS K,  dK += scale dS^T Q.
+    Padded query rows and padding keys carry no gradient (zero rows).
+
+    q/k/v/do_perm: [sum L_h, D].  Returns dQ, dK, dV fp64 [sum L_h, D].
+    """
+    D = q_perm.shape[1]
+    dQ = np.zeros((plan.total_rows, D))
+    dK = np.zeros((plan.total_rows, D))
+    dV = np.zeros((plan.total_rows, D))
+    for h in range(plan.num_heads):
+        ht = plan.heads[h]
+        base = plan.row_offset[h]
+        for i, row in enumerate(selection[h]):
+            nq = ht.tiles[i].valid
+            r0 = base + TILE_TOKENS * i
+            q = np.asarray(q_perm[r0:r0 + nq], dtype=np.float64)
+            do = np.asarray(do_perm[r0:r0 + nq], dtype=np.float64)
+            krows = np.concatenate([base + TILE_TOKENS * int(j) + np.arange(ht.tiles[int(j)].valid) for j in row])
+            K = np.asarray(k_perm[krows], dtype=np.float64)
+            V = np.asarray(v_perm[krows], dtype=np.float64)
+            z = scale * (q @ K.T)
+            p = np.exp(z - z.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            o = p @ V
+            dp = do @ V.T
+            ds = p * (dp - np.sum(do * o, axis=1, keepdims=True))
+            dQ[r0:r0 + nq] = scale * (ds @ K)
+            np.add.at(dK, krows, scale * (ds.T @ q))
+            np.add.at(dV, krows, p.T @ do)
+    return dQ, dK, dV
+
+
+# ---------------------------------------------------------------------------
 # O11: block heat from the dense LSE
 # ---------------------------------------------------------------------------
 

@@ -798,6 +798,81 @@ def test_vote_invariants_random():
 
 
 # ---------------------------------------------------------------------------
+# P12: block-sparse backward and transposed lists
+# ---------------------------------------------------------------------------
+
+def _random_selection(plan, seed):
+    rng = np.random.default_rng(seed)
+    sel = []
+    for h in range(plan.num_heads):
+        n = plan.heads[h].num_tiles
+        sel.append([np.array(sorted({i} | set(rng.choice(n, size=rng.integers(1, n + 1), replace=False).tolist())))
+                    for i in range(n)])
+    return sel
+
+
+def check_backward_vs_autograd(w, backward=vo.block_sparse_attention_backward, seed=3):
+    """Gradients against torch autograd (fp64) of library masked attention over
+    natural order, for a random upstream gradient dO."""
+    plan = vo.Plan.from_workload(w)
+    N, H, D = w.num_tokens, w.num_heads, w.head_dim
+    q = _f64(_random_bf16((N, H, D), seed))
+    k = _f64(_random_bf16((N, H, D), seed + 1))
+    v = _f64(_random_bf16((N, H, D), seed + 2))
+    do = _f64(_random_bf16((N, H, D), seed + 3))
+    sel = _random_selection(plan, seed)
+    scale = w.softmax_scale
+    perm = lambda x: vo.permute_forward(plan, x)   # noqa: E731
+    dQ, dK, dV = backward(plan, perm(q), perm(k), perm(v), perm(do), sel, scale)
+    got = [vo.permute_inverse(plan, g) for g in (dQ, dK, dV)]
+    for h in range(H):
+        tile_of = _token_tile(plan, h, N)
+        n = plan.heads[h].num_tiles
+        bm = np.zeros((n, n), dtype=bool)
+        for i, r in enumerate(sel[h]):
+            bm[i, r] = True
+        m = torch.from_numpy(bm[tile_of][:, tile_of])
+        qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x[:, h])).requires_grad_(True) for x in (q, k, v))
+        o = torch.nn.functional.scaled_dot_product_attention(qt[None], kt[None], vt[None], attn_mask=m[None],
+                                                             scale=scale)[0]
+        o.backward(torch.from_numpy(np.ascontiguousarray(do[:, h])))
+        for g, ref in zip(got, (qt.grad, kt.grad, vt.grad)):
+            assert np.max(np.abs(g[:, h] - ref.numpy())) < 1e-10
+
+
+def test_backward_vs_autograd_partial_tiles():
+    check_backward_vs_autograd(_small_partial_workload())
+
+
+def test_backward_vs_autograd_packed():
+    check_backward_vs_autograd(_small_packed_workload())
+
+
+def test_backward_padding_rows_are_zero():
+    w = _small_partial_workload()
+    plan = vo.Plan.from_workload(w)
+    N, H, D = w.num_tokens, w.num_heads, w.head_dim
+    xs = [vo.permute_forward(plan, _f64(_random_bf16((N, H, D), s))) for s in range(4)]
+    dQ, dK, dV = vo.block_sparse_attention_backward(plan, *xs, _random_selection(plan, 1), w.softmax_scale)
+    for h in range(H):
+        pad = plan.row_offset[h] + np.nonzero(plan.heads[h].perm() < 0)[0]
+        assert pad.size and not np.any(dQ[pad]) and not np.any(dK[pad]) and not np.any(dV[pad])
+
+
+def test_mask_transpose_brute_force():
+    w = _small_packed_workload()
+    plan = vo.Plan.from_workload(w)
+    sel = _random_selection(plan, 2)
+    tr = vo.mask_transpose(plan, sel)
+    for h in range(plan.num_heads):
+        n = plan.heads[h].num_tiles
+        for j in range(n):
+            expect = [i for i in range(n) if j in set(sel[h][i].tolist())]
+            assert tr[h][j].tolist() == expect
+        assert sum(len(c) for c in tr[h]) == sum(len(r) for r in sel[h])
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each pin above must catch a plausible error in the oracle
 # ---------------------------------------------------------------------------
 
@@ -934,6 +1009,30 @@ def _mut_search_lowest_heat(segments, num_heads, head_dim, candidates, budget_mo
     return err
 
 
+def _mut_backward_no_rowsum(plan, q_perm, k_perm, v_perm, do_perm, selection, scale):
+    """dS = P * dP (the rowsum(dO * O) term dropped)."""
+    D = q_perm.shape[1]
+    dQ, dK, dV = (np.zeros((plan.total_rows, D)) for _ in range(3))
+    for h in range(plan.num_heads):
+        ht = plan.heads[h]
+        base = plan.row_offset[h]
+        for i, row in enumerate(selection[h]):
+            nq = ht.tiles[i].valid
+            r0 = base + 128 * i
+            q = q_perm[r0:r0 + nq]
+            do = do_perm[r0:r0 + nq]
+            kr = np.concatenate([base + 128 * int(j) + np.arange(ht.tiles[int(j)].valid) for j in row])
+            K, V = k_perm[kr], v_perm[kr]
+            z = scale * (q @ K.T)
+            p = np.exp(z - z.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            ds = p * (do @ V.T)
+            dQ[r0:r0 + nq] = scale * (ds @ K)
+            np.add.at(dK, kr, scale * (ds.T @ q))
+            np.add.at(dV, kr, p.T @ do)
+    return dQ, dK, dV
+
+
 MUTATIONS = [
     ("tiling order inside a tile", lambda: check_handworked_tilings(_mut_tiles_colmajor)),
     ("mean over the padded volume", lambda: check_pool_special_cases(_mut_pool_divide_by_volume)),
@@ -948,6 +1047,8 @@ MUTATIONS = [
     ("heat divided by 128", lambda: check_heat(_small_partial_workload(), _mut_heat_divide_by_volume)),
     ("mask mass not weighted by valid queries", lambda: check_mask_mass_token_level(_mut_mass_unweighted)),
     ("search mask of the lowest heat", lambda: check_search_prefers_frame_tiles(_mut_search_lowest_heat)),
+    ("backward without the row-sum term", lambda: check_backward_vs_autograd(_small_partial_workload(),
+                                                                           _mut_backward_no_rowsum)),
 ]
 
 
