@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (known bytes) to scale HBM counters")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="rough budget of the oracle sample")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the block-sparse backward (transposed lists, dK/dV and dQ) of the same layer")
     ap.add_argument("--search", action="store_true",
                     help="also time the tile-plan search on the 8x32x32 grid (16 heads, D 128, 10%% keep, "
                          "5 candidate shapes, 3 samples of one layer) and report it")
@@ -220,12 +222,52 @@ def main():
             "recall_mean": round(float((mp / mo).mean()), 4), "recall_min": round(float((mp / mo).min()), 4),
             "note": "synthetic inputs and a random-init predictor; the pages' 0.63 / 0.71 come from real "
                     "activations"}
+    if args.backward:
+        out["backward"] = time_backward(layer, w, args.steps)
     if args.search:
         out["tile_plan_search"] = time_search()
     if not args.no_cpu_baseline:
         print("bench: oracle CPU baseline (~%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inputs[0], args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def time_backward(layer, w, steps):
+    """The backward of the layer's last forward (same mask): transposed lists
+    plus veda_block_sparse_attn_bwd, timed with HIP events; algorithmic work =
+    2.5x the forward's (dV, dP, dK, dQ and the recomputed S: 10 * 128^2 * D
+    flop per block)."""
+    p, vb = layer.plan, layer.vb
+    dev = "cuda"
+    x = layer.sets[0]
+    vp, dop, o = p.empty_perm(), p.empty_perm(), p.empty_perm()
+    p.permute(x["v"], vp, vb.VEDA_PERMUTE_FORWARD)
+    gen = torch.Generator().manual_seed(5)
+    p.permute(torch.randn(x["v"].shape, generator=gen).to(torch.bfloat16).to(dev), dop, vb.VEDA_PERMUTE_FORWARD)
+    p.attention(layer.qp, layer.kp, layer.vt, layer.row_ptr, layer.col, w.softmax_scale, o, layer.lse)
+    col_ptr = torch.empty(p.T + 1, dtype=torch.int32, device=dev)
+    row_idx = torch.empty(p.info["nnz"], dtype=torch.int32, device=dev)
+    wt, wb = p.empty_bytes("transpose_workspace_bytes"), p.empty_bytes("bwd_workspace_bytes")
+    dq, dk, dv = p.empty_perm(), p.empty_perm(), p.empty_perm()
+
+    def run():
+        p.transpose(layer.row_ptr, layer.col, col_ptr, row_idx, wt)
+        p.backward(layer.qp, layer.kp, vp, o, dop, layer.lse, layer.row_ptr, layer.col, col_ptr, row_idx,
+                   w.softmax_scale, dq, dk, dv, wb)
+    for _ in range(3):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(3, min(steps, 20))
+    e0.record()
+    for _ in range(n):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    flops = 10.0 * 128 * 128 * w.head_dim * p.info["nnz"]
+    return {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "flop_count": "10 * 128^2 * D per computed block (dV, dP, dK, dQ, recomputed S)",
+            "includes": "transposed lists, tile transposes, rowsum(dO*O), dK/dV and dQ kernels"}
 
 
 SEARCH_CANDIDATES = ((1, 8, 16), (2, 8, 8), (4, 4, 8), (2, 4, 16), (1, 16, 8))

@@ -61,6 +61,7 @@ class PlanInfo(ctypes.Structure):
                 ("total_tiles", ctypes.c_int64), ("total_pairs", ctypes.c_int64),
                 ("nnz", ctypes.c_int64), ("max_row_blocks", ctypes.c_int64),
                 ("device_table_bytes", ctypes.c_int64), ("score_workspace_bytes", ctypes.c_int64),
+                ("transpose_workspace_bytes", ctypes.c_int64), ("bwd_workspace_bytes", ctypes.c_int64),
                 ("max_tiles_per_head", ctypes.c_int32), ("uploaded", ctypes.c_int32)]
 
 
@@ -91,6 +92,9 @@ _SIGS = {
     "veda_block_heat": (_I32, [_P, _P, _P, _P, ctypes.c_float, _P, _P]),
     "veda_mask_mass": (_I32, [_P, _P, _P, _P, _P, _P]),
     "veda_output_error": (_I32, [_P, _P, _P, _P, _P]),
+    "veda_mask_transpose": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "veda_block_sparse_attn_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
+                                          _P, ctypes.c_size_t, _P]),
     "veda_tile_plan_vote": (_I32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P]),
 }
 EXPORTED = tuple(_SIGS)
@@ -265,6 +269,19 @@ def veda_output_error(plan: int, o, o_ref, err, stream=None) -> None:
     _check(lib().veda_output_error(plan, _ptr(o), _ptr(o_ref), _ptr(err), _stream(stream)))
 
 
+def veda_mask_transpose(plan: int, row_ptr, col_idx, col_ptr, row_idx, workspace, stream=None) -> None:
+    _check(lib().veda_mask_transpose(plan, _ptr(row_ptr), _ptr(col_idx), _ptr(col_ptr), _ptr(row_idx),
+                                     _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def veda_block_sparse_attn_bwd(plan: int, q, k, v, o, d_o, lse, row_ptr, col_idx, col_ptr, row_idx,
+                               softmax_scale: float, dq, dk, dv, workspace, stream=None) -> None:
+    _check(lib().veda_block_sparse_attn_bwd(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
+                                            _ptr(row_ptr), _ptr(col_idx), _ptr(col_ptr), _ptr(row_idx),
+                                            float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                            _nbytes(workspace), _stream(stream)))
+
+
 def veda_tile_plan_vote(err, max_shapes: int = 2):
     """err: host float64 array [samples, candidates, heads]; returns int32
     [heads] candidate indices (host-only step, no device)."""
@@ -437,6 +454,38 @@ class Plan:
         self._expect(lse, (self.R,), torch.float32, "lse")
         self._expect(heat, (self.info["total_pairs"],), torch.float32, "heat")
         veda_block_heat(self.handle, q, k, lse, scale, heat, stream)
+
+    def transpose(self, row_ptr, col_idx, col_ptr, row_idx, workspace, stream=None):
+        import torch
+        self._expect(row_ptr, (self.T + 1,), torch.int32, "row_ptr")
+        self._expect(col_idx, (self.info["nnz"],), torch.int32, "col_idx")
+        self._expect(col_ptr, (self.T + 1,), torch.int32, "col_ptr")
+        self._expect(row_idx, (self.info["nnz"],), torch.int32, "row_idx")
+        self._check_ws(workspace, "transpose_workspace_bytes")
+        veda_mask_transpose(self.handle, row_ptr, col_idx, col_ptr, row_idx, workspace, stream)
+
+    def backward(self, q, k, v, o, d_o, lse, row_ptr, col_idx, col_ptr, row_idx, scale, dq, dk, dv, workspace,
+                 stream=None):
+        import torch
+        bf = torch.bfloat16
+        for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+            self._expect(t, (self.R, self.D), bf, name)
+        self._expect(lse, (self.R,), torch.float32, "lse")
+        self._expect(row_ptr, (self.T + 1,), torch.int32, "row_ptr")
+        self._expect(col_idx, (self.info["nnz"],), torch.int32, "col_idx")
+        self._expect(col_ptr, (self.T + 1,), torch.int32, "col_ptr")
+        self._expect(row_idx, (self.info["nnz"],), torch.int32, "row_idx")
+        self._check_ws(workspace, "bwd_workspace_bytes")
+        veda_block_sparse_attn_bwd(self.handle, q, k, v, o, d_o, lse, row_ptr, col_idx, col_ptr, row_idx, scale,
+                                   dq, dk, dv, workspace, stream)
+
+    def _check_ws(self, ws, key):
+        if ws is None or not ws.is_cuda or not ws.is_contiguous() or _nbytes(ws) < self.info[key]:
+            raise ValueError("workspace must be a contiguous CUDA tensor of at least %d bytes" % self.info[key])
+
+    def empty_bytes(self, key):
+        import torch
+        return torch.empty(max(self.info[key], 1), dtype=torch.uint8, device="cuda")
 
     def output_error(self, o, o_ref, err, stream=None):
         import torch

@@ -500,6 +500,8 @@ veda_status veda_plan_create(const veda_plan_desc* d, veda_plan** out) {
   in.max_row_blocks = maxrow;
   in.max_tiles_per_head = maxtiles;
   in.score_workspace_bytes = score_workspace_bytes(tiles, d->head_dim);
+  in.transpose_workspace_bytes = transpose_workspace_bytes(in.total_pairs, in.total_tiles);
+  in.bwd_workspace_bytes = bwd_workspace_bytes(in.total_rows, d->head_dim);
   build_attn_order(*p);
   build_staging(*p);
   in.device_table_bytes = (int64_t)p->staging.size();
@@ -712,6 +714,44 @@ veda_status veda_output_error(const veda_plan* p, const void* o, const void* o_r
   if ((st = check_ptr(o, "o")) || (st = check_ptr(o_ref, "o_ref")) || (st = check_ptr(err, "err"))) return st;
   return launched(launch_output_error(p->dev, p->info.num_tokens, o, o_ref, err, (hipStream_t)stream),
                   "output error");
+}
+
+veda_status veda_mask_transpose(const veda_plan* p, const int32_t* row_ptr, const int32_t* col_idx, int32_t* col_ptr,
+                                int32_t* row_idx, void* workspace, size_t workspace_bytes, void* stream) {
+  veda_status st = check_plan_ready(p);
+  if (st) return st;
+  if ((st = check_ptr(row_ptr, "row_ptr")) || (st = check_ptr(col_idx, "col_idx")) ||
+      (st = check_ptr(col_ptr, "col_ptr")) || (st = check_ptr(row_idx, "row_idx")) ||
+      (st = check_ptr(workspace, "workspace")))
+    return st;
+  if ((int64_t)workspace_bytes < p->info.transpose_workspace_bytes)
+    return fail(VEDA_ERR_WORKSPACE, "mask transpose needs %lld workspace bytes",
+                (long long)p->info.transpose_workspace_bytes);
+  return launched(launch_mask_transpose(p->dev, row_ptr, col_idx, col_ptr, row_idx, workspace,
+                                        p->info.total_pairs, (hipStream_t)stream),
+                  "mask transpose");
+}
+
+veda_status veda_block_sparse_attn_bwd(const veda_plan* p, const void* q, const void* k, const void* v,
+                                       const void* o, const void* d_o, const float* lse, const int32_t* row_ptr,
+                                       const int32_t* col_idx, const int32_t* col_ptr, const int32_t* row_idx,
+                                       float softmax_scale, void* dq, void* dk, void* dv, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  veda_status st = check_plan_ready(p);
+  if (st) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(o, "o")) ||
+      (st = check_ptr(d_o, "d_o")) || (st = check_ptr(lse, "lse")) || (st = check_ptr(row_ptr, "row_ptr")) ||
+      (st = check_ptr(col_idx, "col_idx")) || (st = check_ptr(col_ptr, "col_ptr")) ||
+      (st = check_ptr(row_idx, "row_idx")) || (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) ||
+      (st = check_ptr(dv, "dv")) || (st = check_ptr(workspace, "workspace")))
+    return st;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return fail(VEDA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if ((int64_t)workspace_bytes < p->info.bwd_workspace_bytes)
+    return fail(VEDA_ERR_WORKSPACE, "backward needs %lld workspace bytes", (long long)p->info.bwd_workspace_bytes);
+  return launched(launch_attn_bwd(p->dev, q, k, v, o, d_o, lse, row_ptr, col_idx, col_ptr, row_idx, softmax_scale, dq,
+                                  dk, dv, workspace, (hipStream_t)stream),
+                  "attention backward");
 }
 
 veda_status veda_tile_plan_vote(int32_t samples, int32_t candidates, int32_t heads, const double* err,

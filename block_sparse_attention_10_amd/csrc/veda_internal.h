@@ -16,6 +16,16 @@ constexpr int kMaxShapes = 2;       // at most two tile shapes per layer
 constexpr int kMaxTilesPerHead = 16384;
 constexpr int kMaxHeatTiles = 4096;
 
+inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+// Byte matrix of the kept blocks (sum n_h^2) and per-key-tile counts.
+inline int64_t transpose_workspace_bytes(int64_t total_pairs, int64_t total_tiles) {
+  return align256(total_pairs) + align256(total_tiles * 4);
+}
+// Tile-transposed Q, K and dO ([T, D, 128] bf16 each) and rowsum(dO * O) (fp32 [R]).
+inline int64_t bwd_workspace_bytes(int64_t total_rows, int head_dim) {
+  return 3 * align256(total_rows * head_dim * 2) + align256(total_rows * 4);
+}
+
 // Device view of the tables of one distinct tile shape.  Heads that share a
 // shape share these tables (tiling, valid counts, budgets, local CSR offsets).
 struct DevShape {
@@ -68,6 +78,12 @@ hipError_t launch_mask_mass(const DevPlan& p, const float* heat, const int32_t* 
                             double* mass, hipStream_t s);
 hipError_t launch_output_error(const DevPlan& p, int64_t num_tokens, const void* o, const void* o_ref, double* err,
                                hipStream_t s);
+hipError_t launch_mask_transpose(const DevPlan& p, const int32_t* row_ptr, const int32_t* col_idx, int32_t* col_ptr,
+                                 int32_t* row_idx, void* workspace, int64_t total_pairs, hipStream_t s);
+hipError_t launch_attn_bwd(const DevPlan& p, const void* q, const void* k, const void* v, const void* o,
+                           const void* d_o, const float* lse, const int32_t* row_ptr, const int32_t* col_idx,
+                           const int32_t* col_ptr, const int32_t* row_idx, float scale, void* dq, void* dk,
+                           void* dv, void* workspace, hipStream_t s);
 
 // Scratch the score call needs: pooled features of Q and K (fp32 [T, 3D]
 // each) and their projections (fp32 [T, D] each).

@@ -1420,6 +1420,395 @@ __global__ void __launch_bounds__(512) output_error_kernel(int64_t num_tokens, i
   if (threadIdx.x == 0) err[h] = num_s[0] / den_s[0];
 }
 
+// ---------------------------------------------------------------------------
+// backward: transposed lists
+// ---------------------------------------------------------------------------
+//
+// The per-key-tile lists come from a byte matrix per head (m[i][j] = 1 iff
+// key tile j is in query tile i's row): scatter the CSR into it, then one
+// thread per key tile walks its column twice, counting and then listing the
+// query tiles in ascending order.  No atomics, so the order is fixed.
+__global__ void __launch_bounds__(kThreads) fill_u32_kernel(uint32_t* __restrict__ x, int64_t n, uint32_t v) {
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += (int64_t)gridDim.x * kThreads) x[e] = v;
+}
+
+__global__ void __launch_bounds__(64) csc_scatter_kernel(DevPlan p, const int32_t* __restrict__ row_ptr,
+                                                        const int32_t* __restrict__ col_idx,
+                                                        uint8_t* __restrict__ bitmap) {
+  const int t = blockIdx.x;
+  const int h = p.row_head[t];
+  const int n = p.shape[p.head_shape[h]].num_tiles;
+  const int i = t - p.head_tile_off[h];
+  uint8_t* m = bitmap + p.head_pair_off[h] + (int64_t)i * n;
+  for (int e = row_ptr[t] + (int)threadIdx.x; e < row_ptr[t + 1]; e += 64) {
+    const int j = col_idx[e];
+    if (j >= 0 && j < n) m[j] = 1;
+  }
+}
+
+template <bool FILL>
+__global__ void __launch_bounds__(kThreads) csc_column_kernel(DevPlan p, const uint8_t* __restrict__ bitmap,
+                                                             int32_t* __restrict__ counts,
+                                                             const int32_t* __restrict__ col_ptr,
+                                                             int32_t* __restrict__ row_idx) {
+  const int64_t tc = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (tc >= p.total_tiles) return;
+  const int h = p.row_head[tc];
+  const int n = p.shape[p.head_shape[h]].num_tiles;
+  const int j = (int)(tc - p.head_tile_off[h]);
+  const uint8_t* m = bitmap + p.head_pair_off[h] + j;
+  if (!FILL) {
+    int c = 0;
+    for (int i = 0; i < n; ++i) c += m[(int64_t)i * n];
+    counts[tc] = c;
+  } else {
+    int32_t pos = col_ptr[tc];
+    for (int i = 0; i < n; ++i)
+      if (m[(int64_t)i * n]) row_idx[pos++] = i;
+  }
+}
+
+// Exclusive scan of counts[0..n) into col_ptr[0..n]; one workgroup, chunks
+// of 1024 with a running carry.
+__global__ void __launch_bounds__(1024) csc_scan_kernel(const int32_t* __restrict__ counts, int64_t n,
+                                                       int32_t* __restrict__ col_ptr) {
+  __shared__ int32_t buf[1024];
+  __shared__ int32_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < n; base += 1024) {
+    const int64_t e = base + threadIdx.x;
+    const int32_t v = e < n ? counts[e] : 0;
+    buf[threadIdx.x] = v;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {       // inclusive Hillis-Steele scan
+      const int32_t add = (int)threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
+      __syncthreads();
+      buf[threadIdx.x] += add;
+      __syncthreads();
+    }
+    if (e < n) col_ptr[e] = carry + buf[threadIdx.x] - v;
+    __syncthreads();
+    if (threadIdx.x == 1023) carry += buf[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) col_ptr[n] = carry;
+}
+
+// ---------------------------------------------------------------------------
+// backward: helpers
+// ---------------------------------------------------------------------------
+
+// Permuted rows [R, D] -> tile-transposed [T, D, 128] (one workgroup per tile).
+template <int D>
+__global__ void __launch_bounds__(kThreads) tile_transpose_kernel(const uint16_t* __restrict__ src,
+                                                                 uint16_t* __restrict__ dst) {
+  constexpr int CH = D / 8;
+  constexpr int LD = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t tileb[kTile * LD];
+  const int64_t t = blockIdx.x;
+  const uint16_t* in = src + t * kTile * D;
+  for (int q = threadIdx.x; q < kTile * CH; q += kThreads) {
+    const int r = q / CH, c = q % CH;
+    *reinterpret_cast<u32x4*>(&tileb[r * LD + 8 * c]) = ld16(in + (int64_t)r * D + 8 * c);
+  }
+  __syncthreads();
+  uint16_t* out = dst + t * (int64_t)D * kTile;
+  for (int q = threadIdx.x; q < D * 16; q += kThreads) {
+    const int d = q / 16, c = q % 16;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = tileb[(8 * c + 2 * e) * LD + d];
+      const uint32_t hi = tileb[(8 * c + 2 * e + 1) * LD + d];
+      w[e] = lo | (hi << 16);
+    }
+    u32x4 v = {w[0], w[1], w[2], w[3]};
+    st16(out + (int64_t)d * kTile + 8 * c, v);
+  }
+}
+
+// Dsum[r] = sum_d dO[r][d] * O[r][d] in fp32 (one thread per permuted row).
+template <int D>
+__global__ void __launch_bounds__(kThreads) bwd_dsum_kernel(int64_t rows, const uint16_t* __restrict__ o,
+                                                           const uint16_t* __restrict__ d_o,
+                                                           float* __restrict__ dsum) {
+  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (r >= rows) return;
+  float acc = 0.0f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const u32x4 a = ld16(o + r * D + 8 * c), b = ld16(d_o + r * D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(bf16_to_f32((uint16_t)(a[e] & 0xffff)), bf16_to_f32((uint16_t)(b[e] & 0xffff)), acc);
+      acc = fmaf(bf16_to_f32((uint16_t)(a[e] >> 16)), bf16_to_f32((uint16_t)(b[e] >> 16)), acc);
+    }
+  }
+  dsum[r] = acc;
+}
+
+// A 128-row tile of permuted rows into LDS in the layout qk_group reads
+// (rows in pi order inside each 32-row group, 16-byte chunks XOR-swizzled),
+// as one array.
+template <int D>
+__device__ __forceinline__ void load_rows_tile(uint16_t* __restrict__ dst, const uint16_t* __restrict__ src) {
+  constexpr int CH = D / 8;
+#pragma unroll 1
+  for (int q = threadIdx.x; q < kTile * CH; q += kThreads) {
+    const int m = q / CH, pos = q % CH;
+    const int slot = (m & ~31) | pi_row(m & 31);
+    st16(dst + m * D + 8 * pos, ld16(src + (int64_t)slot * D + 8 * (pos ^ (m & (CH - 1)))));
+  }
+}
+
+// A tile-transposed tile [D][128] into LDS, 16-byte chunk c of row d at
+// position c ^ (d & 15).
+template <int D>
+__device__ __forceinline__ void load_t_tile(uint16_t* __restrict__ dst, const uint16_t* __restrict__ src) {
+#pragma unroll 1
+  for (int q = threadIdx.x; q < D * 16; q += kThreads) {
+    const int d = q / 16, pos = q % 16;
+    st16(dst + d * kTile + 8 * pos, ld16(src + (int64_t)d * kTile + 8 * (pos ^ (d & 15))));
+  }
+}
+
+// Rows 32g .. 32g+31 of a rows tile (A operand) against the wave's B operand
+// (32 columns): the qk_group product on a one-array tile.
+template <int D>
+__device__ __forceinline__ f32x16 rows_group(const uint16_t* __restrict__ tile, const bf16x8 (&bop)[D / 16],
+                                             int g) {
+  constexpr int CH = D / 8;
+  const int lane = lane_id();
+  const int ln = lane & 31, hl = lane >> 5;
+  const int m = 32 * g + ln;
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(tile + m * D + 8 * ((2 * s + hl) ^ (m & (CH - 1)))));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[s], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// acc^T (D x 32) += T-tile^T (D x 32 slots of group g) * pg (the 32 slots'
+// packed bf16 values, 8 consecutive per lane and 16-slot step).
+template <int D>
+__device__ __forceinline__ void t_group(const uint16_t* __restrict__ ttile, const bf16x8 (&pg)[2], int g,
+                                        f32x16 (&acc)[D / 32]) {
+  const int lane = lane_id();
+  const int ln = lane & 31, hl = lane >> 5;
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const int c = 4 * g + 2 * s2 + hl;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int d = 32 * db + ln;
+      const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(ttile + d * kTile + 8 * (c ^ (d & 15))));
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pg[s2], acc[db], 0, 0, 0);
+    }
+  }
+}
+
+// The wave's B operand for 32 rows of a permuted tile: lane (ln, hl) holds
+// row r0 + ln, channels 16s + 8hl .. +7.
+template <int D>
+__device__ __forceinline__ void load_bop(bf16x8 (&bop)[D / 16], const uint16_t* __restrict__ rows, int64_t r0) {
+  const int lane = lane_id();
+  const int ln = lane & 31, hl = lane >> 5;
+  const uint16_t* r = rows + (r0 + ln) * D + 8 * hl;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) bop[s] = __builtin_bit_cast(bf16x8, ld16(r + 16 * s));
+}
+
+// Store acc^T (D x 32 columns; lane (ln, hl) holds rows 32db + 8j + 4hl + i)
+// times `mul` as bf16 into row r0 + ln of a [R, D] array, or zeros.
+template <int D>
+__device__ __forceinline__ void store_t_rows(uint16_t* __restrict__ out, int64_t r0, const f32x16 (&acc)[D / 32],
+                                             float mul, bool zero) {
+  const int lane = lane_id();
+  const int ln = lane & 31, hl = lane >> 5;
+  uint16_t* row = out + (r0 + ln) * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      uint2 v;
+      v.x = zero ? 0u : pack_bf16x2(acc[db][4 * jj + 0] * mul, acc[db][4 * jj + 1] * mul);
+      v.y = zero ? 0u : pack_bf16x2(acc[db][4 * jj + 2] * mul, acc[db][4 * jj + 3] * mul);
+      *reinterpret_cast<uint2*>(row + 32 * db + 8 * jj + 4 * hl) = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward: dK, dV over the transposed lists
+// ---------------------------------------------------------------------------
+//
+// One workgroup (4 waves) per (head, key tile j); wave w owns keys
+// 32w .. 32w+31, whose K and V rows it holds as B operands.  For every query
+// tile i that selected j: S' = Q_i K_w^T and dP' = dO_i V_w^T (A = Q and dO
+// rows from LDS, rows in pi order), P' = exp2(S' c - lse2), dS' = P' (dP' -
+// Dsum); dV_w^T += dO_i^T P' and dK_w^T += Q_i^T dS' (A = the transposed tiles
+// from LDS, B = P' / dS' straight from registers: with the pi row order a
+// lane's eight values of a 16-query step are eight consecutive queries).
+// Padding keys' rows are written as zeros; padding queries have zero dO rows
+// and contribute nothing.
+template <int D>
+__global__ void __launch_bounds__(kThreads, 1) attn_bwd_dkdv_kernel(
+    DevPlan p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ d_o, const uint16_t* __restrict__ q_t, const uint16_t* __restrict__ do_t,
+    const float* __restrict__ lse, const float* __restrict__ dsum, const int32_t* __restrict__ col_ptr,
+    const int32_t* __restrict__ row_idx, float scale_log2, float scale, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv) {
+  __shared__ __attribute__((aligned(16))) uint16_t qs[kTile * D];
+  __shared__ __attribute__((aligned(16))) uint16_t dos[kTile * D];
+  __shared__ __attribute__((aligned(16))) uint16_t qts[D * kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t dots[D * kTile];
+  __shared__ __attribute__((aligned(16))) float lse2s[kTile];
+  __shared__ __attribute__((aligned(16))) float dss[kTile];
+  const int t = blockIdx.x;
+  const int h = uni(p.row_head[t]);
+  const DevShape& sh = p.shape[uni(p.head_shape[h])];
+  const int j = t - uni(p.head_tile_off[h]);
+  const int nvk = uni(sh.valid[j]);
+  const int64_t hrow = uni64(p.head_row_off[h]);
+  const int64_t htile = uni(p.head_tile_off[h]);
+  const int w = threadIdx.x >> 6, lane = lane_id(), ln = lane & 31, hl = lane >> 5;
+  const float c = scale_log2;
+  const int64_t krow0 = hrow + (int64_t)kTile * j + 32 * w;
+  bf16x8 kf[D / 16], vf[D / 16];
+  load_bop<D>(kf, k, krow0);
+  load_bop<D>(vf, v, krow0);
+  f32x16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
+  }
+  const int e0 = uni(col_ptr[t]), e1 = uni(col_ptr[t + 1]);
+  for (int e = e0; e < e1; ++e) {
+    const int i = uni(row_idx[e]);
+    const int64_t qrow0 = hrow + (int64_t)kTile * i;
+    __syncthreads();                 // every wave is done with the previous query tile
+    load_rows_tile<D>(qs, q + qrow0 * D);
+    load_rows_tile<D>(dos, d_o + qrow0 * D);
+    load_t_tile<D>(qts, q_t + (htile + i) * D * kTile);
+    load_t_tile<D>(dots, do_t + (htile + i) * D * kTile);
+    if (threadIdx.x < kTile) {
+      lse2s[threadIdx.x] = lse[qrow0 + threadIdx.x] * 1.4426950408889634f;
+      dss[threadIdx.x] = dsum[qrow0 + threadIdx.x];
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int g = 0; g < 4; ++g) {
+      const f32x16 sg = rows_group<D>(qs, kf, g);
+      const f32x16 dpg = rows_group<D>(dos, vf, g);
+      // register r holds query 32g + 16(r >> 3) + 8hl + (r & 7)
+      float l2[16], ds[16];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int q0 = 32 * g + 16 * half + 8 * hl;
+        const float4 a0 = *reinterpret_cast<const float4*>(&lse2s[q0]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&lse2s[q0 + 4]);
+        const float4 b0 = *reinterpret_cast<const float4*>(&dss[q0]);
+        const float4 b1 = *reinterpret_cast<const float4*>(&dss[q0 + 4]);
+        l2[8 * half + 0] = a0.x; l2[8 * half + 1] = a0.y; l2[8 * half + 2] = a0.z; l2[8 * half + 3] = a0.w;
+        l2[8 * half + 4] = a1.x; l2[8 * half + 5] = a1.y; l2[8 * half + 6] = a1.z; l2[8 * half + 7] = a1.w;
+        ds[8 * half + 0] = b0.x; ds[8 * half + 1] = b0.y; ds[8 * half + 2] = b0.z; ds[8 * half + 3] = b0.w;
+        ds[8 * half + 4] = b1.x; ds[8 * half + 5] = b1.y; ds[8 * half + 6] = b1.z; ds[8 * half + 7] = b1.w;
+      }
+      bf16x8 pp[2], dsp[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        u32x4 pk, dk4;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int r0 = 8 * s2 + 2 * e2, r1 = r0 + 1;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sg[r0], c, -l2[r0]));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sg[r1], c, -l2[r1]));
+          pk[e2] = pack_bf16x2(p0, p1);
+          dk4[e2] = pack_bf16x2(p0 * (dpg[r0] - ds[r0]), p1 * (dpg[r1] - ds[r1]));
+        }
+        pp[s2] = __builtin_bit_cast(bf16x8, pk);
+        dsp[s2] = __builtin_bit_cast(bf16x8, dk4);
+      }
+      t_group<D>(dots, pp, g, dvacc);
+      t_group<D>(qts, dsp, g, dkacc);
+    }
+  }
+  const bool pad = 32 * w + ln >= nvk;
+  store_t_rows<D>(dk, krow0, dkacc, scale, pad);
+  store_t_rows<D>(dv, krow0, dvacc, 1.0f, pad);
+}
+
+// ---------------------------------------------------------------------------
+// backward: dQ over the row lists
+// ---------------------------------------------------------------------------
+//
+// One workgroup (4 waves) per (head, query tile i), wave w owning queries
+// 32w .. 32w+31 as in the forward: S^T = K Q^T and dP^T = V dO^T (A = K and
+// V rows from LDS in pi order, B = Q and dO rows in registers), P^T and dS^T
+// per lane (lse and Dsum are per query, i.e. per lane), dQ^T += K^T dS^T.
+template <int D>
+__global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(
+    DevPlan p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ d_o, const uint16_t* __restrict__ k_t, const float* __restrict__ lse,
+    const float* __restrict__ dsum, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    float scale_log2, float scale, uint16_t* __restrict__ dq) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kTile * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kTile * D];
+  __shared__ __attribute__((aligned(16))) uint16_t kts[D * kTile];
+  const int t = blockIdx.x;
+  const int h = uni(p.row_head[t]);
+  const DevShape& sh = p.shape[uni(p.head_shape[h])];
+  const int nt = sh.num_tiles;
+  const int i = t - uni(p.head_tile_off[h]);
+  const int64_t hrow = uni64(p.head_row_off[h]);
+  const int64_t htile = uni(p.head_tile_off[h]);
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  const float c = scale_log2;
+  const int64_t qrow0 = hrow + (int64_t)kTile * i + 32 * w;
+  const int ln = lane & 31;
+  bf16x8 qf[D / 16], dof[D / 16];
+  load_bop<D>(qf, q, qrow0);
+  load_bop<D>(dof, d_o, qrow0);
+  const float l2 = lse[qrow0 + ln] * 1.4426950408889634f;
+  const float dsq = dsum[qrow0 + ln];
+  f32x16 dqacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dqacc[db] = f32x16{};
+  const int e0 = uni(row_ptr[t]), e1 = uni(row_ptr[t + 1]);
+  for (int e = e0; e < e1; ++e) {
+    const int jj = min(max(uni(col_idx[e]), 0), nt - 1);
+    const int64_t krow0 = hrow + (int64_t)kTile * jj;
+    __syncthreads();
+    load_rows_tile<D>(ks, k + krow0 * D);
+    load_rows_tile<D>(vs, v + krow0 * D);
+    load_t_tile<D>(kts, k_t + (htile + jj) * D * kTile);
+    __syncthreads();
+#pragma unroll 1
+    for (int kt = 0; kt < 4; ++kt) {
+      const f32x16 sg = rows_group<D>(ks, qf, kt);
+      const f32x16 dpg = rows_group<D>(vs, dof, kt);
+      bf16x8 dsp[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        u32x4 dk4;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int r0 = 8 * s2 + 2 * e2, r1 = r0 + 1;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sg[r0], c, -l2));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sg[r1], c, -l2));
+          dk4[e2] = pack_bf16x2(p0 * (dpg[r0] - dsq), p1 * (dpg[r1] - dsq));
+        }
+        dsp[s2] = __builtin_bit_cast(bf16x8, dk4);
+      }
+      t_group<D>(kts, dsp, kt, dqacc);
+    }
+  }
+  store_t_rows<D>(dq, qrow0, dqacc, scale, false);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1563,6 +1952,62 @@ hipError_t launch_output_error(const DevPlan& p, int64_t num_tokens, const void*
   else
     hipLaunchKernelGGL(output_error_kernel<64>, dim3((unsigned)p.num_heads), dim3(512), 0, s, num_tokens,
                        p.num_heads, a, b, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_transpose(const DevPlan& p, const int32_t* row_ptr, const int32_t* col_idx, int32_t* col_ptr,
+                                 int32_t* row_idx, void* workspace, int64_t total_pairs, hipStream_t s) {
+  uint8_t* bitmap = static_cast<uint8_t*>(workspace);
+  int32_t* counts = reinterpret_cast<int32_t*>(bitmap + align256(total_pairs));
+  const int64_t words = (total_pairs + 3) / 4;
+  const unsigned fill_blocks = (unsigned)std::min<int64_t>((words + kThreads - 1) / kThreads, 65536);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(std::max(fill_blocks, 1u)), dim3(kThreads), 0, s,
+                     reinterpret_cast<uint32_t*>(bitmap), words, 0u);
+  hipLaunchKernelGGL(csc_scatter_kernel, dim3((unsigned)p.total_tiles), dim3(64), 0, s, p, row_ptr, col_idx, bitmap);
+  const dim3 gcol((unsigned)((p.total_tiles + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL(csc_column_kernel<false>, gcol, dim3(kThreads), 0, s, p, bitmap, counts, nullptr, nullptr);
+  hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(1024), 0, s, counts, (int64_t)p.total_tiles, col_ptr);
+  hipLaunchKernelGGL(csc_column_kernel<true>, gcol, dim3(kThreads), 0, s, p, bitmap, counts, col_ptr, row_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd(const DevPlan& p, const void* q, const void* k, const void* v, const void* o,
+                           const void* d_o, const float* lse, const int32_t* row_ptr, const int32_t* col_idx,
+                           const int32_t* col_ptr, const int32_t* row_idx, float scale, void* dq, void* dk,
+                           void* dv, void* workspace, hipStream_t s) {
+  const int D = p.head_dim;
+  const int64_t R = p.total_rows, T = p.total_tiles;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint16_t* q_t = reinterpret_cast<uint16_t*>(ws);
+  uint16_t* k_t = reinterpret_cast<uint16_t*>(ws + align256(R * D * 2));
+  uint16_t* do_t = reinterpret_cast<uint16_t*>(ws + 2 * align256(R * D * 2));
+  float* dsum = reinterpret_cast<float*>(ws + 3 * align256(R * D * 2));
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  const uint16_t* oo = static_cast<const uint16_t*>(o);
+  const uint16_t* dd = static_cast<const uint16_t*>(d_o);
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const dim3 gt((unsigned)T), grows((unsigned)((R + kThreads - 1) / kThreads));
+  if (D == 128) {
+    hipLaunchKernelGGL(tile_transpose_kernel<128>, gt, dim3(kThreads), 0, s, qq, q_t);
+    hipLaunchKernelGGL(tile_transpose_kernel<128>, gt, dim3(kThreads), 0, s, kk, k_t);
+    hipLaunchKernelGGL(tile_transpose_kernel<128>, gt, dim3(kThreads), 0, s, dd, do_t);
+    hipLaunchKernelGGL(bwd_dsum_kernel<128>, grows, dim3(kThreads), 0, s, R, oo, dd, dsum);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, gt, dim3(kThreads), 0, s, p, qq, kk, vv, dd, q_t, do_t, lse, dsum,
+                       col_ptr, row_idx, scale_log2, scale, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, gt, dim3(kThreads), 0, s, p, qq, kk, vv, dd, k_t, lse, dsum, row_ptr,
+                       col_idx, scale_log2, scale, static_cast<uint16_t*>(dq));
+  } else {
+    hipLaunchKernelGGL(tile_transpose_kernel<64>, gt, dim3(kThreads), 0, s, qq, q_t);
+    hipLaunchKernelGGL(tile_transpose_kernel<64>, gt, dim3(kThreads), 0, s, kk, k_t);
+    hipLaunchKernelGGL(tile_transpose_kernel<64>, gt, dim3(kThreads), 0, s, dd, do_t);
+    hipLaunchKernelGGL(bwd_dsum_kernel<64>, grows, dim3(kThreads), 0, s, R, oo, dd, dsum);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, gt, dim3(kThreads), 0, s, p, qq, kk, vv, dd, q_t, do_t, lse, dsum,
+                       col_ptr, row_idx, scale_log2, scale, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, gt, dim3(kThreads), 0, s, p, qq, kk, vv, dd, k_t, lse, dsum, row_ptr,
+                       col_idx, scale_log2, scale, static_cast<uint16_t*>(dq));
+  }
   return hipGetLastError();
 }
 

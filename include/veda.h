@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define VEDA_ABI_VERSION 3
+#define VEDA_ABI_VERSION 4
 
 typedef int32_t veda_status;
 enum {
@@ -120,6 +120,8 @@ typedef struct veda_plan_info {
   int64_t max_row_blocks;     /* longest CSR row                              */
   int64_t device_table_bytes; /* bytes veda_plan_upload needs                 */
   int64_t score_workspace_bytes; /* bytes veda_score_tiles needs              */
+  int64_t transpose_workspace_bytes; /* bytes veda_mask_transpose needs       */
+  int64_t bwd_workspace_bytes; /* bytes veda_block_sparse_attn_bwd needs       */
   int32_t max_tiles_per_head;
   int32_t uploaded;           /* 1 after a successful veda_plan_upload        */
 } veda_plan_info;
@@ -294,6 +296,41 @@ veda_status veda_mask_mass(const veda_plan* plan, const float* heat, const int32
  * fp64 accumulation in a fixed order: bitwise reproducible. */
 veda_status veda_output_error(const veda_plan* plan, const void* o, const void* o_ref, double* err,
                               void* stream);
+
+/* Transposed block lists for the backward (Miowtion project page: the
+ * block-sparse backward that predictor and LoRA training need; dK and dV are
+ * gathered per key tile): for every head h and key tile j, the query tiles
+ * whose rows hold j, ascending.
+ *   row_ptr, col_idx: device CSR of this plan's shape (veda_select_blocks)
+ *   col_ptr:  device int32 [T + 1], key tiles in the same head-major order as
+ *             the rows; col_ptr[T] = nnz
+ *   row_idx:  device int32 [nnz], head-local query tile indices
+ *   workspace: device, transpose_workspace_bytes (contents overwritten)
+ * Deterministic (no atomics). */
+veda_status veda_mask_transpose(const veda_plan* plan, const int32_t* row_ptr, const int32_t* col_idx,
+                                int32_t* col_ptr, int32_t* row_idx, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Block-sparse attention backward over the same mask as the forward
+ * (same source).  With P = softmax over the valid keys of the kept blocks:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
+ *   dQ = scale dS K,  dK = scale dS^T Q.
+ * dQ is gathered per query tile over the row lists, dK and dV per key tile
+ * over the transposed lists, so no output is accumulated by atomics.
+ *   q, k, v, o, d_o: device permuted bf16 [R, D] (o and lse as the forward
+ *             wrote them with VEDA_LAYOUT_PERMUTED; d_o's padding rows zero,
+ *             as veda_permute_tiles writes them; k's and v's padding rows
+ *             zero)
+ *   lse:      device fp32 [R] (the forward's natural-log LSE, every row)
+ *   row_ptr, col_idx: the forward's CSR; col_ptr, row_idx: its transpose
+ *             (veda_mask_transpose)
+ *   dq, dk, dv: device permuted bf16 [R, D]; rows of padding slots are zero
+ *   workspace: device, bwd_workspace_bytes (contents overwritten) */
+veda_status veda_block_sparse_attn_bwd(const veda_plan* plan, const void* q, const void* k, const void* v,
+                                       const void* o, const void* d_o, const float* lse, const int32_t* row_ptr,
+                                       const int32_t* col_idx, const int32_t* col_ptr, const int32_t* row_idx,
+                                       float softmax_scale, void* dq, void* dk, void* dv, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /* Tile-shape vote of the tile-plan search (same source): a host-only step
  * on the error table of `samples` x `candidates` x `heads` (err[s][c][h],

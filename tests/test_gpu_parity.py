@@ -237,6 +237,59 @@ def test_tile_plan_search(kind):
             assert choice[h] == ref_choice[h], h
 
 
+def _backward_case(w, seed):
+    """GPU forward (permuted O and LSE), transposed lists and backward for a
+    random upstream gradient; returns the GPU tensors and the oracle's fp64
+    gradients on the same inputs."""
+    inp = wl.make_inputs(w, seed=seed)
+    g = gp.gpu_path(w, inp)
+    plan, dev = g["plan"], "cuda"
+    gen = torch.Generator().manual_seed(seed + 1)
+    do_nat = torch.randn((w.num_tokens, w.num_heads, w.head_dim), generator=gen).to(torch.bfloat16)
+    vp, dop, o = plan.empty_perm(), plan.empty_perm(), plan.empty_perm()
+    plan.permute(inp["v"].to(dev), vp, vb.VEDA_PERMUTE_FORWARD)
+    plan.permute(do_nat.to(dev), dop, vb.VEDA_PERMUTE_FORWARD)
+    lse = torch.empty(plan.R, dtype=torch.float32, device=dev)
+    plan.attention(g["q_perm"], g["k_perm"], g["v_t"], g["row_ptr"], g["col_idx"], w.softmax_scale, o, lse)
+    col_ptr = torch.empty(plan.T + 1, dtype=torch.int32, device=dev)
+    row_idx = torch.empty(plan.info["nnz"], dtype=torch.int32, device=dev)
+    plan.transpose(g["row_ptr"], g["col_idx"], col_ptr, row_idx, plan.empty_bytes("transpose_workspace_bytes"))
+    dq, dk, dv = plan.empty_perm(), plan.empty_perm(), plan.empty_perm()
+    plan.backward(g["q_perm"], g["k_perm"], vp, o, dop, lse, g["row_ptr"], g["col_idx"], col_ptr, row_idx,
+                  w.softmax_scale, dq, dk, dv, plan.empty_bytes("bwd_workspace_bytes"))
+    torch.cuda.synchronize()
+    op = vo.Plan.from_workload(w)
+    sel = _csr_to_selection(op, g["row_ptr"].cpu().numpy(), g["col_idx"].cpu().numpy())
+    ref = vo.block_sparse_attention_backward(op, gp.f64(g["q_perm"]), gp.f64(g["k_perm"]), gp.f64(vp), gp.f64(dop),
+                                             sel, w.softmax_scale)
+    return op, sel, col_ptr, row_idx, (dq, dk, dv), ref
+
+
+@pytest.mark.parametrize("w", [small_workloads()[0], small_workloads()[1], small_workloads()[3], wl.workload(2)],
+                         ids=lambda w: w.name)
+def test_backward(w):
+    """Transposed lists bit-exact; dQ, dK, dV against the fp64 oracle over
+    valid rows (bars derived like the forward's: bf16 P and dS, bf16 outputs),
+    padding rows exactly zero."""
+    op, sel, col_ptr, row_idx, got, ref = _backward_case(w, w.index)
+    tr = vo.mask_transpose(op, sel)
+    counts = [len(c) for rows in tr for c in rows]
+    cp = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    ri = np.concatenate([c for rows in tr for c in rows]).astype(np.int32)
+    assert np.array_equal(col_ptr.cpu().numpy(), cp) and np.array_equal(row_idx.cpu().numpy(), ri)
+    vr = gp.valid_rows(op)
+    pad = np.setdiff1d(np.arange(op.total_rows), vr)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        a = gp.f64(a)
+        d = a[vr] - b[vr]
+        max_abs = float(np.max(np.abs(d)))
+        rel = float(np.linalg.norm(d) / np.linalg.norm(b[vr]))
+        print("%s %s: max_abs %.3e (ref max %.3e) rel_l2 %.3e" % (w.name, name, max_abs, np.max(np.abs(b[vr])), rel),
+              flush=True)
+        assert rel <= gp.REL_L2 and max_abs <= gp.MAX_ABS * max(1.0, float(np.max(np.abs(b[vr]))))
+        assert not np.any(a[pad]), name
+
+
 def test_oracle_mask_mass_and_recall():
     """Oracle mask (veda_select_blocks on the block heat) and the attention
     mass of the predicted and oracle masks (veda_mask_mass) against the

@@ -37,7 +37,7 @@ def test_abi_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert vb.veda_abi_version() == 3
+    assert vb.veda_abi_version() == 4
 
 
 def test_available_reports_reason_without_gpu():
