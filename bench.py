@@ -267,7 +267,7 @@ def time_backward(layer, w, steps):
     flops = 10.0 * 128 * 128 * w.head_dim * p.info["nnz"]
     return {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
             "flop_count": "10 * 128^2 * D per computed block (dV, dP, dK, dQ, recomputed S)",
-            "includes": "transposed lists, tile transposes, rowsum(dO*O), dK/dV and dQ kernels"}
+            "includes": "transposed lists, per-row (lse, rowsum(dO*O)), key-tile dispatch order, dK/dV and dQ kernels"}
 
 
 SEARCH_CANDIDATES = ((1, 8, 16), (2, 8, 8), (4, 4, 8), (2, 4, 16), (1, 16, 8))

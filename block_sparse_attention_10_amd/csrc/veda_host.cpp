@@ -501,7 +501,7 @@ veda_status veda_plan_create(const veda_plan_desc* d, veda_plan** out) {
   in.max_tiles_per_head = maxtiles;
   in.score_workspace_bytes = score_workspace_bytes(tiles, d->head_dim);
   in.transpose_workspace_bytes = transpose_workspace_bytes(in.total_pairs, in.total_tiles);
-  in.bwd_workspace_bytes = bwd_workspace_bytes(in.total_rows, d->head_dim);
+  in.bwd_workspace_bytes = bwd_workspace_bytes(in.total_rows, in.total_tiles);
   build_attn_order(*p);
   build_staging(*p);
   in.device_table_bytes = (int64_t)p->staging.size();

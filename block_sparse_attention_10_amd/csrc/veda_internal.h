@@ -21,9 +21,10 @@ inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 inline int64_t transpose_workspace_bytes(int64_t total_pairs, int64_t total_tiles) {
   return align256(total_pairs) + align256(total_tiles * 4);
 }
-// Tile-transposed Q, K and dO ([T, D, 128] bf16 each) and rowsum(dO * O) (fp32 [R]).
-inline int64_t bwd_workspace_bytes(int64_t total_rows, int head_dim) {
-  return 3 * align256(total_rows * head_dim * 2) + align256(total_rows * 4);
+// Per permuted row: (lse * log2(e), rowsum(dO * O)), fp32 pairs [R, 2]; then
+// the dispatch order of the key tiles, int32 [T].
+inline int64_t bwd_workspace_bytes(int64_t total_rows, int64_t total_tiles) {
+  return align256(total_rows * 8) + align256(total_tiles * 4);
 }
 
 // Device view of the tables of one distinct tile shape.  Heads that share a

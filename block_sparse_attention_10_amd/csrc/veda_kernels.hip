@@ -1499,45 +1499,60 @@ __global__ void __launch_bounds__(1024) csc_scan_kernel(const int32_t* __restric
 // backward: helpers
 // ---------------------------------------------------------------------------
 
-// Permuted rows [R, D] -> tile-transposed [T, D, 128] (one workgroup per tile).
-template <int D>
-__global__ void __launch_bounds__(kThreads) tile_transpose_kernel(const uint16_t* __restrict__ src,
-                                                                 uint16_t* __restrict__ dst) {
-  constexpr int CH = D / 8;
-  constexpr int LD = D + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t tileb[kTile * LD];
-  const int64_t t = blockIdx.x;
-  const uint16_t* in = src + t * kTile * D;
-  for (int q = threadIdx.x; q < kTile * CH; q += kThreads) {
-    const int r = q / CH, c = q % CH;
-    *reinterpret_cast<u32x4*>(&tileb[r * LD + 8 * c]) = ld16(in + (int64_t)r * D + 8 * c);
+// Dispatch order of the dK/dV workgroups: key tiles by descending list length
+// (a counting sort in one workgroup), so the long lists of popular key tiles
+// start first and the grid ends evenly.  The order inside one length is that
+// of the LDS atomics; it only changes the schedule, never a result.
+constexpr int kOrderBins = 4096;
+__global__ void __launch_bounds__(1024) bwd_order_kernel(const int32_t* __restrict__ col_ptr, int64_t n,
+                                                        int32_t* __restrict__ order) {
+  __shared__ int32_t start[kOrderBins];
+  __shared__ int32_t part[1024];
+  const int tid = threadIdx.x;
+  for (int b = tid; b < kOrderBins; b += 1024) start[b] = 0;
+  __syncthreads();
+  auto bin = [&](int64_t t) {   // bin 0 holds the longest lists
+    return kOrderBins - 1 - min(col_ptr[t + 1] - col_ptr[t], kOrderBins - 1);
+  };
+  for (int64_t t = tid; t < n; t += 1024) atomicAdd(&start[bin(t)], 1);
+  __syncthreads();
+  int32_t loc[kOrderBins / 1024], sum = 0;
+#pragma unroll
+  for (int u = 0; u < kOrderBins / 1024; ++u) {
+    loc[u] = start[(kOrderBins / 1024) * tid + u];
+    sum += loc[u];
+  }
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {          // inclusive Hillis-Steele scan
+    const int32_t add = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  int32_t run = part[tid] - sum;
+#pragma unroll
+  for (int u = 0; u < kOrderBins / 1024; ++u) {
+    start[(kOrderBins / 1024) * tid + u] = run;
+    run += loc[u];
   }
   __syncthreads();
-  uint16_t* out = dst + t * (int64_t)D * kTile;
-  for (int q = threadIdx.x; q < D * 16; q += kThreads) {
-    const int d = q / 16, c = q % 16;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = tileb[(8 * c + 2 * e) * LD + d];
-      const uint32_t hi = tileb[(8 * c + 2 * e + 1) * LD + d];
-      w[e] = lo | (hi << 16);
-    }
-    u32x4 v = {w[0], w[1], w[2], w[3]};
-    st16(out + (int64_t)d * kTile + 8 * c, v);
-  }
+  for (int64_t t = tid; t < n; t += 1024) order[atomicAdd(&start[bin(t)], 1)] = (int32_t)t;
 }
 
-// Dsum[r] = sum_d dO[r][d] * O[r][d] in fp32 (one thread per permuted row).
+// aux[r] = (lse[r] * log2(e), sum_d dO[r][d] * O[r][d]) in fp32 for every
+// permuted row; D/8 lanes per row, one 16-byte chunk of O and dO each.
 template <int D>
-__global__ void __launch_bounds__(kThreads) bwd_dsum_kernel(int64_t rows, const uint16_t* __restrict__ o,
+__global__ void __launch_bounds__(kThreads) bwd_prep_kernel(int64_t rows, const uint16_t* __restrict__ o,
                                                            const uint16_t* __restrict__ d_o,
-                                                           float* __restrict__ dsum) {
-  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (r >= rows) return;
+                                                           const float* __restrict__ lse,
+                                                           float2* __restrict__ aux) {
+  constexpr int CH = D / 8;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t r = idx / CH;
+  const int c = (int)(idx % CH);
   float acc = 0.0f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
+  if (r < rows) {
     const u32x4 a = ld16(o + r * D + 8 * c), b = ld16(d_o + r * D + 8 * c);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1545,69 +1560,160 @@ __global__ void __launch_bounds__(kThreads) bwd_dsum_kernel(int64_t rows, const 
       acc = fmaf(bf16_to_f32((uint16_t)(a[e] >> 16)), bf16_to_f32((uint16_t)(b[e] >> 16)), acc);
     }
   }
-  dsum[r] = acc;
+#pragma unroll
+  for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (r < rows && c == 0) aux[r] = make_float2(lse[r] * 1.4426950408889634f, acc);
 }
 
-// A 128-row tile of permuted rows into LDS in the layout qk_group reads
-// (rows in pi order inside each 32-row group, 16-byte chunks XOR-swizzled),
-// as one array.
+// Row tiles of the backward in LDS: 128 rows of D bf16, rows in pi order
+// inside every 32 (as the attention kernels hold K), 16-byte chunk c of row m
+// at position c ^ bsw(m).  Both ways the tile is read stay free of bank
+// conflicts: row reads (16 consecutive rows, one chunk each) and transpose
+// reads (4 consecutive rows, 32 bytes of each per 16 lanes).
 template <int D>
-__device__ __forceinline__ void load_rows_tile(uint16_t* __restrict__ dst, const uint16_t* __restrict__ src) {
+__device__ __forceinline__ int bsw(int m) {
+  if constexpr (D == 128)
+    return ((m & 3) << 2) | ((m >> 2) & 3);
+  else
+    return (((m >> 1) & 1) << 2) | ((m >> 2) & 3);
+}
+
+template <int D>
+__device__ __forceinline__ int brow_off(int m, int c) {
+  return m * D + 8 * (c ^ bsw<D>(m));
+}
+
+// Asynchronous copy of a [128, D] row tile into that layout through a buffer
+// resource: each lane moves 16 bytes per instruction and a wave's 64 chunks
+// land contiguously, so the swizzle is applied on the global side.  A
+// workgroup instruction of 512 threads fills STEP = 512 / (D / 8) rows (32 or
+// 64); the swizzle and the pi order only use the low five bits of the row, so
+// every instruction of a thread uses one byte offset plus a uniform step.
+constexpr int kBwdThreads = 512;   // backward workgroups: 8 waves, 2 per SIMD
+
+template <int D>
+__device__ __forceinline__ int brow_lane_offset(int tid) {   // bytes
   constexpr int CH = D / 8;
-#pragma unroll 1
-  for (int q = threadIdx.x; q < kTile * CH; q += kThreads) {
-    const int m = q / CH, pos = q % CH;
-    const int slot = (m & ~31) | pi_row(m & 31);
-    st16(dst + m * D + 8 * pos, ld16(src + (int64_t)slot * D + 8 * (pos ^ (m & (CH - 1)))));
-  }
+  const int m = tid / CH, pos = tid % CH;
+  return 2 * (((m & ~31) | pi_row(m & 31)) * D + 8 * (pos ^ bsw<D>(m)));
+}
+template <int D>
+__device__ __forceinline__ void dma_row_tile(uint16_t* __restrict__ dst, __amdgpu_buffer_rsrc_t rs, int tile_byte,
+                                             int lane_off, int wave) {
+  constexpr int STEP = kBwdThreads / (D / 8);   // rows per workgroup instruction (32 or 64)
+#pragma unroll
+  for (int it = 0; it < kTile / STEP; ++it)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + it * STEP * D + 512 * wave, 16, lane_off,
+                                             tile_byte + it * STEP * D * 2, 0, 0);
 }
 
-// A tile-transposed tile [D][128] into LDS, 16-byte chunk c of row d at
-// position c ^ (d & 15).
+// Per-lane byte offsets of a wave's operand reads inside a backward row
+// tile.  Row group g adds 32 g D 2 bytes and the 16-row step s2 of a
+// transpose read 16 s2 D 2 bytes: neither changes the swizzle (it only uses
+// the row's low bits), so both become immediate offsets of the reads.
 template <int D>
-__device__ __forceinline__ void load_t_tile(uint16_t* __restrict__ dst, const uint16_t* __restrict__ src) {
-#pragma unroll 1
-  for (int q = threadIdx.x; q < D * 16; q += kThreads) {
-    const int d = q / 16, pos = q % 16;
-    st16(dst + d * kTile + 8 * pos, ld16(src + (int64_t)d * kTile + 8 * (pos ^ (d & 15))));
-  }
+struct BwdOffsets {
+  int row[D / 16];     // row reads, 16-channel step s: row ln, chunk 2s + hl
+  int tr[D / 32][2];   // transpose reads, channel block db, 4-row half r
+};
+
+template <int D>
+__device__ __forceinline__ BwdOffsets<D> bwd_offsets(int lane) {
+  const int ln = lane & 31, hl = lane >> 5, gq = (lane >> 4) & 1, j = lane & 15;
+  BwdOffsets<D> o;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) o.row[s] = 2 * brow_off<D>(ln, 2 * s + hl);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      // query 8hl + 4r + (j >> 2) of the first 16-row step, in pi order
+      const int m = pi_row(8 * hl + 4 * r + (j >> 2));
+      const int d = 32 * db + 16 * gq + 4 * (j & 3);
+      o.tr[db][r] = 2 * (brow_off<D>(m, d >> 3) + (d & 7));
+    }
+  return o;
 }
 
-// Rows 32g .. 32g+31 of a rows tile (A operand) against the wave's B operand
-// (32 columns): the qk_group product on a one-array tile.
+// The offsets formed where a tile's products start, from a lane index the
+// compiler cannot see through: the addresses are then computed per tile and
+// not kept live across the tile loop.
 template <int D>
-__device__ __forceinline__ f32x16 rows_group(const uint16_t* __restrict__ tile, const bf16x8 (&bop)[D / 16],
-                                             int g) {
-  constexpr int CH = D / 8;
-  const int lane = lane_id();
-  const int ln = lane & 31, hl = lane >> 5;
-  const int m = 32 * g + ln;
+__device__ __forceinline__ BwdOffsets<D> bwd_offsets_here() {
+  int lane = lane_id();
+  asm volatile("" : "+v"(lane));
+  return bwd_offsets<D>(lane);
+}
+
+template <int D>
+__device__ __forceinline__ const uint16_t* at_byte(const uint16_t* tile, int bytes) {
+  return reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(tile) + bytes);
+}
+
+// Rows 32g .. 32g+31 of a row tile (A operand) against the wave's B operand
+// (32 columns of D channels).
+template <int D>
+__device__ __forceinline__ f32x16 brows_group(const uint16_t* __restrict__ tile, const BwdOffsets<D>& o,
+                                              const bf16x8 (&bop)[D / 16], int g) {
   f32x16 acc = {};
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(tile + m * D + 8 * ((2 * s + hl) ^ (m & (CH - 1)))));
+    const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(at_byte<D>(tile, o.row[s] + 64 * g * D)));
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[s], acc, 0, 0, 0);
   }
   return acc;
 }
 
-// acc^T (D x 32) += T-tile^T (D x 32 slots of group g) * pg (the 32 slots'
-// packed bf16 values, 8 consecutive per lane and 16-slot step).
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// LDS transpose read (CDNA4): in every group of 16 lanes, lane 4x + a names
+// 4 consecutive 16-bit values; lane 4a + b receives value b of lanes a, 4 + a,
+// 8 + a, 12 + a, in that order.
+__device__ __forceinline__ s16x4 tr_read(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
+
+// acc^T (D x 32) += T^T * pg, T the 32 rows of group g of a row tile and pg
+// the 32 columns' packed bf16 values (8 consecutive rows per lane and 16-row
+// step, rows in natural order).  The A operand (lane (ln, hl) of channel
+// block db: channel 32db + ln, rows 16 s2 + 8hl .. +7) comes from two
+// transpose reads of 4 rows each: in each 16-lane group, lane j names row
+// 4r + (j >> 2) of the 8 and channels 4 (j & 3) .. +3 of the group's 16.
 template <int D>
-__device__ __forceinline__ void t_group(const uint16_t* __restrict__ ttile, const bf16x8 (&pg)[2], int g,
-                                        f32x16 (&acc)[D / 32]) {
-  const int lane = lane_id();
-  const int ln = lane & 31, hl = lane >> 5;
+__device__ __forceinline__ void tr_group(const uint16_t* __restrict__ tile, const BwdOffsets<D>& o,
+                                         const bf16x8 (&pg)[2], int g, f32x16 (&acc)[D / 32]) {
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
-    const int c = 4 * g + 2 * s2 + hl;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const int d = 32 * db + ln;
-      const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(ttile + d * kTile + 8 * (c ^ (d & 15))));
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pg[s2], acc[db], 0, 0, 0);
+      const int imm = (64 * g + 32 * s2) * D;   // bytes: 32g + 16 s2 rows
+      const s16x4 lo = tr_read(at_byte<D>(tile, o.tr[db][0] + imm));
+      const s16x4 hi = tr_read(at_byte<D>(tile, o.tr[db][1] + imm));
+      const s16x8 a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pg[s2], acc[db], 0, 0, 0);
     }
   }
+}
+
+// Scheduling pattern of one backward pipeline step: NMFMA MFMAs, each
+// followed by DS reads (alternately R0 and R1 of them, operands of later
+// MFMAs) and VALU instructions of the softmax step.
+template <int NMFMA, int R0, int R1, int VALU>
+__device__ __forceinline__ void bwd_interleave() {
+#ifndef VEDA_BWD_NO_INTERLEAVE
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // DS read
+#pragma unroll
+  for (int i = 0; i < NMFMA / 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, R0, 0);
+    if (VALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R1, 0);
+    if (VALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
+  }
+#endif
 }
 
 // The wave's B operand for 32 rows of a permuted tile: lane (ln, hl) holds
@@ -1644,152 +1750,176 @@ __device__ __forceinline__ void store_t_rows(uint16_t* __restrict__ out, int64_t
 // backward: dK, dV over the transposed lists
 // ---------------------------------------------------------------------------
 //
-// One workgroup (4 waves) per (head, key tile j); wave w owns keys
-// 32w .. 32w+31, whose K and V rows it holds as B operands.  For every query
-// tile i that selected j: S' = Q_i K_w^T and dP' = dO_i V_w^T (A = Q and dO
-// rows from LDS, rows in pi order), P' = exp2(S' c - lse2), dS' = P' (dP' -
-// Dsum); dV_w^T += dO_i^T P' and dK_w^T += Q_i^T dS' (A = the transposed tiles
-// from LDS, B = P' / dS' straight from registers: with the pi row order a
-// lane's eight values of a 16-query step are eight consecutive queries).
-// Padding keys' rows are written as zeros; padding queries have zero dO rows
+// One workgroup of 8 waves per (head, key tile j), longest lists first.
+// Waves 0-3 are dV waves,
+// waves 4-7 dK waves; wave w & 3 of either kind owns keys 32(w & 3) .. +31,
+// whose K (and for dK, V) rows it holds as B operands.  For every query tile
+// i that selected j, group g of 32 queries at a time:
+//   dV wave:  S' = Q K_w^T, P' = exp2(S' c - lse2), dV_w^T += dO^T P'
+//   dK wave:  S' = Q K_w^T, dP' = dO V_w^T, dS' = P' (dP' - Dsum),
+//             dK_w^T += Q^T dS'
+// (A = Q and dO rows from LDS, read as rows or transposed; B = P' / dS'
+// straight from registers: with the pi row order a lane's eight values of a
+// 16-query step are eight consecutive queries).  The dK waves recompute S'
+// (a quarter more MFMA work than one fused wave) so that every wave fits in
+// 256 registers and two waves share each SIMD.  Query tiles are double-
+// buffered in LDS (two fixed buffer sets, the loop unrolled by two), the next
+// one copied asynchronously during the current one's products.  Padding
+// keys' rows are written as zeros; padding queries have zero Q and dO rows
 // and contribute nothing.
 template <int D>
-__global__ void __launch_bounds__(kThreads, 1) attn_bwd_dkdv_kernel(
+__global__ void __launch_bounds__(kBwdThreads, 1) attn_bwd_dkdv_kernel(
     DevPlan p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ d_o, const uint16_t* __restrict__ q_t, const uint16_t* __restrict__ do_t,
-    const float* __restrict__ lse, const float* __restrict__ dsum, const int32_t* __restrict__ col_ptr,
-    const int32_t* __restrict__ row_idx, float scale_log2, float scale, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv) {
-  __shared__ __attribute__((aligned(16))) uint16_t qs[kTile * D];
-  __shared__ __attribute__((aligned(16))) uint16_t dos[kTile * D];
-  __shared__ __attribute__((aligned(16))) uint16_t qts[D * kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t dots[D * kTile];
-  __shared__ __attribute__((aligned(16))) float lse2s[kTile];
-  __shared__ __attribute__((aligned(16))) float dss[kTile];
-  const int t = blockIdx.x;
+    const uint16_t* __restrict__ d_o, const float2* __restrict__ aux, const int32_t* __restrict__ col_ptr,
+    const int32_t* __restrict__ row_idx, const int32_t* __restrict__ order, float scale_log2, float scale,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  constexpr int TS = kTile * D;   // bf16 elements of a row tile
+  // Q tile + its 128 (lse2, Dsum) pairs, and the dO tile, per buffer set
+  __shared__ __attribute__((aligned(16))) uint16_t q0[TS + 512];
+  __shared__ __attribute__((aligned(16))) uint16_t d0[TS];
+  __shared__ __attribute__((aligned(16))) uint16_t q1[TS + 512];
+  __shared__ __attribute__((aligned(16))) uint16_t d1[TS];
+  const int t = uni(order[blockIdx.x]);
   const int h = uni(p.row_head[t]);
   const DevShape& sh = p.shape[uni(p.head_shape[h])];
+  const int nt = sh.num_tiles;
   const int j = t - uni(p.head_tile_off[h]);
   const int nvk = uni(sh.valid[j]);
   const int64_t hrow = uni64(p.head_row_off[h]);
-  const int64_t htile = uni(p.head_tile_off[h]);
-  const int w = threadIdx.x >> 6, lane = lane_id(), ln = lane & 31, hl = lane >> 5;
+  const int wave = threadIdx.x >> 6, w = wave & 3, lane = lane_id(), ln = lane & 31, hl = lane >> 5;
+  const bool dk_wave = wave >= 4;
   const float c = scale_log2;
   const int64_t krow0 = hrow + (int64_t)kTile * j + 32 * w;
-  bf16x8 kf[D / 16], vf[D / 16];
-  load_bop<D>(kf, k, krow0);
-  load_bop<D>(vf, v, krow0);
-  f32x16 dkacc[D / 32], dvacc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    dkacc[db] = f32x16{};
-    dvacc[db] = f32x16{};
-  }
+  const int64_t tile_bytes = (int64_t)kTile * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = head_rsrc(q + hrow * D, nt * tile_bytes);
+  const __amdgpu_buffer_rsrc_t rd = head_rsrc(d_o + hrow * D, nt * tile_bytes);
+  const __amdgpu_buffer_rsrc_t rx = head_rsrc(aux + hrow, (int64_t)nt * kTile * 8);
+  const int loff = brow_lane_offset<D>(threadIdx.x);
+  // copies query tile i into one buffer set
+  auto copy = [&](uint16_t* qd, uint16_t* dd, int i) {
+    dma_row_tile<D>(qd, rq, i * (int)tile_bytes, loff, wave);
+    dma_row_tile<D>(dd, rd, i * (int)tile_bytes, loff, wave);
+    if (wave == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, qd + TS, 16, 16 * lane, i * kTile * 8, 0, 0);
+  };
   const int e0 = uni(col_ptr[t]), e1 = uni(col_ptr[t + 1]);
-  for (int e = e0; e < e1; ++e) {
-    const int i = uni(row_idx[e]);
-    const int64_t qrow0 = hrow + (int64_t)kTile * i;
-    __syncthreads();                 // every wave is done with the previous query tile
-    load_rows_tile<D>(qs, q + qrow0 * D);
-    load_rows_tile<D>(dos, d_o + qrow0 * D);
-    load_t_tile<D>(qts, q_t + (htile + i) * D * kTile);
-    load_t_tile<D>(dots, do_t + (htile + i) * D * kTile);
-    if (threadIdx.x < kTile) {
-      lse2s[threadIdx.x] = lse[qrow0 + threadIdx.x] * 1.4426950408889634f;
-      dss[threadIdx.x] = dsum[qrow0 + threadIdx.x];
-    }
-    __syncthreads();
+  auto run = [&](auto dkc) {
+    constexpr bool DK = decltype(dkc)::value;
+    bf16x8 kf[D / 16], vf[D / 16];
+    load_bop<D>(kf, k, krow0);
+    if constexpr (DK) load_bop<D>(vf, v, krow0);
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+    // the products of one query tile held in (qc, dc)
+    auto tile = [&](const uint16_t* qc, const uint16_t* dc) {
+      const BwdOffsets<D> o = bwd_offsets_here<D>();
+      const float2* xc = reinterpret_cast<const float2*>(qc + TS);
 #pragma unroll 1
-    for (int g = 0; g < 4; ++g) {
-      const f32x16 sg = rows_group<D>(qs, kf, g);
-      const f32x16 dpg = rows_group<D>(dos, vf, g);
-      // register r holds query 32g + 16(r >> 3) + 8hl + (r & 7)
-      float l2[16], ds[16];
+      for (int g = 0; g < 4; ++g) {
+        const f32x16 sg = brows_group<D>(qc, o, kf, g);
+        f32x16 dpg;
+        if constexpr (DK) dpg = brows_group<D>(dc, o, vf, g);
+        // register r holds query 32g + 16(r >> 3) + 8hl + (r & 7)
+        bf16x8 pg[2];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int q0 = 32 * g + 16 * half + 8 * hl;
-        const float4 a0 = *reinterpret_cast<const float4*>(&lse2s[q0]);
-        const float4 a1 = *reinterpret_cast<const float4*>(&lse2s[q0 + 4]);
-        const float4 b0 = *reinterpret_cast<const float4*>(&dss[q0]);
-        const float4 b1 = *reinterpret_cast<const float4*>(&dss[q0 + 4]);
-        l2[8 * half + 0] = a0.x; l2[8 * half + 1] = a0.y; l2[8 * half + 2] = a0.z; l2[8 * half + 3] = a0.w;
-        l2[8 * half + 4] = a1.x; l2[8 * half + 5] = a1.y; l2[8 * half + 6] = a1.z; l2[8 * half + 7] = a1.w;
-        ds[8 * half + 0] = b0.x; ds[8 * half + 1] = b0.y; ds[8 * half + 2] = b0.z; ds[8 * half + 3] = b0.w;
-        ds[8 * half + 4] = b1.x; ds[8 * half + 5] = b1.y; ds[8 * half + 6] = b1.z; ds[8 * half + 7] = b1.w;
-      }
-      bf16x8 pp[2], dsp[2];
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const float4* src = reinterpret_cast<const float4*>(&xc[32 * g + 16 * s2 + 8 * hl]);
+          u32x4 pk;
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        u32x4 pk, dk4;
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int r0 = 8 * s2 + 2 * e2, r1 = r0 + 1;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sg[r0], c, -l2[r0]));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sg[r1], c, -l2[r1]));
-          pk[e2] = pack_bf16x2(p0, p1);
-          dk4[e2] = pack_bf16x2(p0 * (dpg[r0] - ds[r0]), p1 * (dpg[r1] - ds[r1]));
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float4 f = src[e2];   // (lse2, Dsum) of two consecutive queries
+            const int r0 = 8 * s2 + 2 * e2, r1 = r0 + 1;
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sg[r0], c, -f.x));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sg[r1], c, -f.z));
+            if constexpr (DK)
+              pk[e2] = pack_bf16x2(p0 * (dpg[r0] - f.y), p1 * (dpg[r1] - f.w));
+            else
+              pk[e2] = pack_bf16x2(p0, p1);
+          }
+          pg[s2] = __builtin_bit_cast(bf16x8, pk);
         }
-        pp[s2] = __builtin_bit_cast(bf16x8, pk);
-        dsp[s2] = __builtin_bit_cast(bf16x8, dk4);
+        tr_group<D>(DK ? qc : dc, o, pg, g, acc);
       }
-      t_group<D>(dots, pp, g, dvacc);
-      t_group<D>(qts, dsp, g, dkacc);
+    };
+    if (e0 < e1) copy(q0, d0, uni(row_idx[e0]));
+    dma_sync<0>();
+    for (int e = e0; e < e1; e += 2) {
+      if (e + 1 < e1) copy(q1, d1, uni(row_idx[e + 1]));
+      tile(q0, d0);
+      dma_sync<0>();                // tile e+1 has landed; every wave is done with set 0
+      if (e + 1 >= e1) break;
+      if (e + 2 < e1) copy(q0, d0, uni(row_idx[e + 2]));
+      tile(q1, d1);
+      dma_sync<0>();
     }
-  }
-  const bool pad = 32 * w + ln >= nvk;
-  store_t_rows<D>(dk, krow0, dkacc, scale, pad);
-  store_t_rows<D>(dv, krow0, dvacc, 1.0f, pad);
+    const bool pad = 32 * w + ln >= nvk;
+    if constexpr (DK)
+      store_t_rows<D>(dk, krow0, acc, scale, pad);
+    else
+      store_t_rows<D>(dv, krow0, acc, 1.0f, pad);
+  };
+  if (dk_wave)
+    run(BoolC<true>{});
+  else
+    run(BoolC<false>{});
 }
 
 // ---------------------------------------------------------------------------
 // backward: dQ over the row lists
 // ---------------------------------------------------------------------------
 //
-// One workgroup (4 waves) per (head, query tile i), wave w owning queries
-// 32w .. 32w+31 as in the forward: S^T = K Q^T and dP^T = V dO^T (A = K and
-// V rows from LDS in pi order, B = Q and dO rows in registers), P^T and dS^T
-// per lane (lse and Dsum are per query, i.e. per lane), dQ^T += K^T dS^T.
+// One workgroup of 8 waves per (head, query tile i): wave w & 3 owns queries
+// 32(w & 3) .. +31 as in the forward, and wave w >> 2 of the pair takes key
+// groups 2(w >> 2) and 2(w >> 2) + 1 of every key tile.  S^T = K Q^T and
+// dP^T = V dO^T (A = K and V rows from LDS, B = Q and dO rows in registers),
+// P^T and dS^T per lane (lse and Dsum are per query, i.e. per lane), dQ^T +=
+// K^T dS^T (A = the K tile read transposed).  The two partial dQ of a pair
+// are summed through LDS at the end.  Key tiles are double-buffered like the
+// query tiles of the dK/dV kernel.
 template <int D>
-__global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(
+__global__ void __launch_bounds__(kBwdThreads, 1) attn_bwd_dq_kernel(
     DevPlan p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ d_o, const uint16_t* __restrict__ k_t, const float* __restrict__ lse,
-    const float* __restrict__ dsum, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    float scale_log2, float scale, uint16_t* __restrict__ dq) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kTile * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[kTile * D];
-  __shared__ __attribute__((aligned(16))) uint16_t kts[D * kTile];
+    const uint16_t* __restrict__ d_o, const float2* __restrict__ aux, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ col_idx, float scale_log2, float scale, uint16_t* __restrict__ dq) {
+  constexpr int TS = kTile * D;
+  __shared__ __attribute__((aligned(16))) uint16_t k0[TS];
+  __shared__ __attribute__((aligned(16))) uint16_t v0[TS];
+  __shared__ __attribute__((aligned(16))) uint16_t k1[TS];
+  __shared__ __attribute__((aligned(16))) uint16_t v1[TS];
   const int t = blockIdx.x;
   const int h = uni(p.row_head[t]);
   const DevShape& sh = p.shape[uni(p.head_shape[h])];
   const int nt = sh.num_tiles;
   const int i = t - uni(p.head_tile_off[h]);
   const int64_t hrow = uni64(p.head_row_off[h]);
-  const int64_t htile = uni(p.head_tile_off[h]);
-  const int w = threadIdx.x >> 6, lane = lane_id();
+  const int wave = threadIdx.x >> 6, w = wave & 3, kh = wave >> 2, lane = lane_id();
   const float c = scale_log2;
   const int64_t qrow0 = hrow + (int64_t)kTile * i + 32 * w;
   const int ln = lane & 31;
+  const int64_t tile_bytes = (int64_t)kTile * D * 2;
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + hrow * D, nt * tile_bytes);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(v + hrow * D, nt * tile_bytes);
+  const int loff = brow_lane_offset<D>(threadIdx.x);
   bf16x8 qf[D / 16], dof[D / 16];
   load_bop<D>(qf, q, qrow0);
   load_bop<D>(dof, d_o, qrow0);
-  const float l2 = lse[qrow0 + ln] * 1.4426950408889634f;
-  const float dsq = dsum[qrow0 + ln];
+  const float2 xq = aux[qrow0 + ln];
+  const float l2 = xq.x, dsq = xq.y;
   f32x16 dqacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dqacc[db] = f32x16{};
-  const int e0 = uni(row_ptr[t]), e1 = uni(row_ptr[t + 1]);
-  for (int e = e0; e < e1; ++e) {
-    const int jj = min(max(uni(col_idx[e]), 0), nt - 1);
-    const int64_t krow0 = hrow + (int64_t)kTile * jj;
-    __syncthreads();
-    load_rows_tile<D>(ks, k + krow0 * D);
-    load_rows_tile<D>(vs, v + krow0 * D);
-    load_t_tile<D>(kts, k_t + (htile + jj) * D * kTile);
-    __syncthreads();
-#pragma unroll 1
-    for (int kt = 0; kt < 4; ++kt) {
-      const f32x16 sg = rows_group<D>(ks, qf, kt);
-      const f32x16 dpg = rows_group<D>(vs, dof, kt);
+  auto copy = [&](uint16_t* kd, uint16_t* vd, int jj) {
+    jj = min(max(jj, 0), nt - 1);   // stay inside the head
+    dma_row_tile<D>(kd, rk, jj * (int)tile_bytes, loff, wave);
+    dma_row_tile<D>(vd, rv, jj * (int)tile_bytes, loff, wave);
+  };
+  auto tile = [&](const uint16_t* kc, const uint16_t* vc) {
+    const BwdOffsets<D> o = bwd_offsets_here<D>();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kt = 2 * kh + u;
+      const f32x16 sg = brows_group<D>(kc, o, qf, kt);
+      const f32x16 dpg = brows_group<D>(vc, o, dof, kt);
       bf16x8 dsp[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -1803,10 +1933,38 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(
         }
         dsp[s2] = __builtin_bit_cast(bf16x8, dk4);
       }
-      t_group<D>(kts, dsp, kt, dqacc);
+      tr_group<D>(kc, o, dsp, kt, dqacc);
     }
+  };
+  const int e0 = uni(row_ptr[t]), e1 = uni(row_ptr[t + 1]);
+  if (e0 < e1) copy(k0, v0, uni(col_idx[e0]));
+  dma_sync<0>();
+  for (int e = e0; e < e1; e += 2) {
+    if (e + 1 < e1) copy(k1, v1, uni(col_idx[e + 1]));
+    tile(k0, v0);
+    dma_sync<0>();
+    if (e + 1 >= e1) break;
+    if (e + 2 < e1) copy(k0, v0, uni(col_idx[e + 2]));
+    tile(k1, v1);
+    dma_sync<0>();
   }
-  store_t_rows<D>(dq, qrow0, dqacc, scale, false);
+  // pair reduction: the second wave of each pair parks its partial dQ in the
+  // (now free) tile buffers, lane-major, the first adds it and stores
+  float* park = reinterpret_cast<float*>(w < 2 ? k0 : v0) + (w & 1) * (D / 2) * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) park[(16 * db + r) * 64 + lane] = dqacc[db][r];
+  }
+  lds_sync();
+  if (kh == 0) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqacc[db][r] += park[(16 * db + r) * 64 + lane];
+    store_t_rows<D>(dq, qrow0, dqacc, scale, false);
+  }
 }
 
 }  // namespace
@@ -1977,36 +2135,29 @@ hipError_t launch_attn_bwd(const DevPlan& p, const void* q, const void* k, const
                            void* dv, void* workspace, hipStream_t s) {
   const int D = p.head_dim;
   const int64_t R = p.total_rows, T = p.total_tiles;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint16_t* q_t = reinterpret_cast<uint16_t*>(ws);
-  uint16_t* k_t = reinterpret_cast<uint16_t*>(ws + align256(R * D * 2));
-  uint16_t* do_t = reinterpret_cast<uint16_t*>(ws + 2 * align256(R * D * 2));
-  float* dsum = reinterpret_cast<float*>(ws + 3 * align256(R * D * 2));
+  float2* aux = static_cast<float2*>(workspace);
+  int32_t* order = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + align256(R * 8));
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   const uint16_t* oo = static_cast<const uint16_t*>(o);
   const uint16_t* dd = static_cast<const uint16_t*>(d_o);
   const float scale_log2 = scale * 1.4426950408889634f;
-  const dim3 gt((unsigned)T), grows((unsigned)((R + kThreads - 1) / kThreads));
+  const dim3 gt((unsigned)T), gprep((unsigned)((R * (D / 8) + kThreads - 1) / kThreads));
   if (D == 128) {
-    hipLaunchKernelGGL(tile_transpose_kernel<128>, gt, dim3(kThreads), 0, s, qq, q_t);
-    hipLaunchKernelGGL(tile_transpose_kernel<128>, gt, dim3(kThreads), 0, s, kk, k_t);
-    hipLaunchKernelGGL(tile_transpose_kernel<128>, gt, dim3(kThreads), 0, s, dd, do_t);
-    hipLaunchKernelGGL(bwd_dsum_kernel<128>, grows, dim3(kThreads), 0, s, R, oo, dd, dsum);
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, gt, dim3(kThreads), 0, s, p, qq, kk, vv, dd, q_t, do_t, lse, dsum,
-                       col_ptr, row_idx, scale_log2, scale, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, gt, dim3(kThreads), 0, s, p, qq, kk, vv, dd, k_t, lse, dsum, row_ptr,
-                       col_idx, scale_log2, scale, static_cast<uint16_t*>(dq));
+    hipLaunchKernelGGL(bwd_prep_kernel<128>, gprep, dim3(kThreads), 0, s, R, oo, dd, lse, aux);
+    hipLaunchKernelGGL(bwd_order_kernel, dim3(1), dim3(1024), 0, s, col_ptr, T, order);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, gt, dim3(kBwdThreads), 0, s, p, qq, kk, vv, dd, aux, col_ptr, row_idx,
+                       order, scale_log2, scale, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, gt, dim3(kBwdThreads), 0, s, p, qq, kk, vv, dd, aux, row_ptr, col_idx,
+                       scale_log2, scale, static_cast<uint16_t*>(dq));
   } else {
-    hipLaunchKernelGGL(tile_transpose_kernel<64>, gt, dim3(kThreads), 0, s, qq, q_t);
-    hipLaunchKernelGGL(tile_transpose_kernel<64>, gt, dim3(kThreads), 0, s, kk, k_t);
-    hipLaunchKernelGGL(tile_transpose_kernel<64>, gt, dim3(kThreads), 0, s, dd, do_t);
-    hipLaunchKernelGGL(bwd_dsum_kernel<64>, grows, dim3(kThreads), 0, s, R, oo, dd, dsum);
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, gt, dim3(kThreads), 0, s, p, qq, kk, vv, dd, q_t, do_t, lse, dsum,
-                       col_ptr, row_idx, scale_log2, scale, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, gt, dim3(kThreads), 0, s, p, qq, kk, vv, dd, k_t, lse, dsum, row_ptr,
-                       col_idx, scale_log2, scale, static_cast<uint16_t*>(dq));
+    hipLaunchKernelGGL(bwd_prep_kernel<64>, gprep, dim3(kThreads), 0, s, R, oo, dd, lse, aux);
+    hipLaunchKernelGGL(bwd_order_kernel, dim3(1), dim3(1024), 0, s, col_ptr, T, order);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, gt, dim3(kBwdThreads), 0, s, p, qq, kk, vv, dd, aux, col_ptr, row_idx,
+                       order, scale_log2, scale, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, gt, dim3(kBwdThreads), 0, s, p, qq, kk, vv, dd, aux, row_ptr, col_idx,
+                       scale_log2, scale, static_cast<uint16_t*>(dq));
   }
   return hipGetLastError();
 }
