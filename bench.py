@@ -297,12 +297,23 @@ def time_search():
             "heads_per_chosen_shape": counts}
 
 
+FWD_SOURCE_END = b"// block heat from the dense LSE"
+
+
 def _kernel_sha():
+    """Hash of the source the attention kernel is built from: the kernel file
+    up to the first section after the attention forward (shared helpers, the
+    layer kernels and the attention kernel itself), so that edits to later
+    kernels (heat, backward, search) keep the recorded traffic valid."""
     import hashlib
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_sparse_attention_10_amd", "csrc",
                         "veda_kernels.hip")
     with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        src = f.read()
+    end = src.find(FWD_SOURCE_END)
+    if end < 0:
+        raise RuntimeError("kernel source layout changed: no heat section marker")
+    return hashlib.sha256(src[:end]).hexdigest()[:16]
 
 
 if __name__ == "__main__":
