@@ -1751,20 +1751,21 @@ __device__ __forceinline__ void store_t_rows(uint16_t* __restrict__ out, int64_t
 // ---------------------------------------------------------------------------
 //
 // One workgroup of 8 waves per (head, key tile j), longest lists first.
-// Waves 0-3 are dV waves,
-// waves 4-7 dK waves; wave w & 3 of either kind owns keys 32(w & 3) .. +31,
-// whose K (and for dK, V) rows it holds as B operands.  For every query tile
-// i that selected j, group g of 32 queries at a time:
-//   dV wave:  S' = Q K_w^T, P' = exp2(S' c - lse2), dV_w^T += dO^T P'
-//   dK wave:  S' = Q K_w^T, dP' = dO V_w^T, dS' = P' (dP' - Dsum),
-//             dK_w^T += Q^T dS'
+// Waves 0-3 are dV waves, waves 4-7 dK waves; wave w & 3 of either kind owns
+// keys 32(w & 3) .. +31, whose K (dV wave) or V (dK wave) rows it holds as B
+// operands.  For every query tile i that selected j, group g of 32 queries
+// at a time:
+//   dV wave:  S' = Q K_w^T, P' = exp2(S' c - lse2) (packed bf16, also handed
+//             to the dK wave of the same keys through LDS), dV_w^T += dO^T P'
+//   dK wave:  dP' = dO V_w^T, dS' = P' (dP' - Dsum), dK_w^T += Q^T dS'
 // (A = Q and dO rows from LDS, read as rows or transposed; B = P' / dS'
 // straight from registers: with the pi row order a lane's eight values of a
-// 16-query step are eight consecutive queries).  The dK waves recompute S'
-// (a quarter more MFMA work than one fused wave) so that every wave fits in
-// 256 registers and two waves share each SIMD.  Query tiles are double-
-// buffered in LDS (two fixed buffer sets, the loop unrolled by two), the next
-// one copied asynchronously during the current one's products.  Padding
+// 16-query step are eight consecutive queries).  Splitting the products over
+// two waves keeps every wave within 256 registers, so two waves share each
+// SIMD, and each does 16 MFMAs per group; a workgroup barrier per group
+// publishes P'.  Query tiles are double-buffered in LDS (two fixed buffer
+// sets, the loop unrolled by two), the next one copied asynchronously during
+// the current one's products.  Padding
 // keys' rows are written as zeros; padding queries have zero Q and dO rows
 // and contribute nothing.
 template <int D>
@@ -1779,6 +1780,9 @@ __global__ void __launch_bounds__(kBwdThreads, 1) attn_bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t d0[TS];
   __shared__ __attribute__((aligned(16))) uint16_t q1[TS + 512];
   __shared__ __attribute__((aligned(16))) uint16_t d1[TS];
+  // P' of group g handed from the dV wave to the dK wave of the same keys:
+  // [group parity][key slice][16-query step][lane], packed bf16
+  __shared__ __attribute__((aligned(16))) u32x4 xp[2][4][2][64];
   const int t = uni(order[blockIdx.x]);
   const int h = uni(p.row_head[t]);
   const DevShape& sh = p.shape[uni(p.head_shape[h])];
@@ -1804,9 +1808,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) attn_bwd_dkdv_kernel(
   const int e0 = uni(col_ptr[t]), e1 = uni(col_ptr[t + 1]);
   auto run = [&](auto dkc) {
     constexpr bool DK = decltype(dkc)::value;
-    bf16x8 kf[D / 16], vf[D / 16];
-    load_bop<D>(kf, k, krow0);
-    if constexpr (DK) load_bop<D>(vf, v, krow0);
+    bf16x8 bop[D / 16];   // K rows (dV wave) or V rows (dK wave) of the wave's 32 keys
+    load_bop<D>(bop, DK ? v : k, krow0);
     f32x16 acc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
@@ -1816,29 +1819,46 @@ __global__ void __launch_bounds__(kBwdThreads, 1) attn_bwd_dkdv_kernel(
       const float2* xc = reinterpret_cast<const float2*>(qc + TS);
 #pragma unroll 1
       for (int g = 0; g < 4; ++g) {
-        const f32x16 sg = brows_group<D>(qc, o, kf, g);
-        f32x16 dpg;
-        if constexpr (DK) dpg = brows_group<D>(dc, o, vf, g);
         // register r holds query 32g + 16(r >> 3) + 8hl + (r & 7)
+        u32x4* slot = &xp[g & 1][w][0][lane];
         bf16x8 pg[2];
+        if constexpr (!DK) {
+          const f32x16 sg = brows_group<D>(qc, o, bop, g);
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const float4* src = reinterpret_cast<const float4*>(&xc[32 * g + 16 * s2 + 8 * hl]);
-          u32x4 pk;
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const float4* src = reinterpret_cast<const float4*>(&xc[32 * g + 16 * s2 + 8 * hl]);
+            u32x4 pk;
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const float4 f = src[e2];   // (lse2, Dsum) of two consecutive queries
-            const int r0 = 8 * s2 + 2 * e2, r1 = r0 + 1;
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sg[r0], c, -f.x));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sg[r1], c, -f.z));
-            if constexpr (DK)
-              pk[e2] = pack_bf16x2(p0 * (dpg[r0] - f.y), p1 * (dpg[r1] - f.w));
-            else
-              pk[e2] = pack_bf16x2(p0, p1);
+            for (int e2 = 0; e2 < 4; ++e2) {
+              const float4 f = src[e2];   // (lse2, Dsum) of two consecutive queries
+              const int r0 = 8 * s2 + 2 * e2, r1 = r0 + 1;
+              pk[e2] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sg[r0], c, -f.x)),
+                                   __builtin_amdgcn_exp2f(fmaf(sg[r1], c, -f.z)));
+            }
+            slot[64 * s2] = pk;      // P' for the dK wave of the same keys
+            pg[s2] = __builtin_bit_cast(bf16x8, pk);
           }
-          pg[s2] = __builtin_bit_cast(bf16x8, pk);
+          lds_sync();                // P'(g) published
+          tr_group<D>(dc, o, pg, g, acc);
+        } else {
+          const f32x16 dpg = brows_group<D>(dc, o, bop, g);
+          lds_sync();                // P'(g) published
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const float4* src = reinterpret_cast<const float4*>(&xc[32 * g + 16 * s2 + 8 * hl]);
+            const u32x4 pk = slot[64 * s2];
+            u32x4 dk4;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+              const float4 f = src[e2];
+              const int r0 = 8 * s2 + 2 * e2, r1 = r0 + 1;
+              const float p0 = __uint_as_float(pk[e2] << 16), p1 = __uint_as_float(pk[e2] & 0xffff0000u);
+              dk4[e2] = pack_bf16x2(p0 * (dpg[r0] - f.y), p1 * (dpg[r1] - f.w));
+            }
+            pg[s2] = __builtin_bit_cast(bf16x8, dk4);
+          }
+          tr_group<D>(qc, o, pg, g, acc);
         }
-        tr_group<D>(DK ? qc : dc, o, pg, g, acc);
       }
     };
     if (e0 < e1) copy(q0, d0, uni(row_idx[e0]));
