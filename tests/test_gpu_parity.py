@@ -237,7 +237,7 @@ def test_tile_plan_search(kind):
             assert choice[h] == ref_choice[h], h
 
 
-def _backward_case(w, seed):
+def _backward_case(w, seed, oracle=True):
     """GPU forward (permuted O and LSE), transposed lists and backward for a
     random upstream gradient; returns the GPU tensors and the oracle's fp64
     gradients on the same inputs."""
@@ -260,6 +260,8 @@ def _backward_case(w, seed):
     torch.cuda.synchronize()
     op = vo.Plan.from_workload(w)
     sel = _csr_to_selection(op, g["row_ptr"].cpu().numpy(), g["col_idx"].cpu().numpy())
+    if not oracle:
+        return op, sel, col_ptr, row_idx, {"inputs": (g["q_perm"], g["k_perm"], vp, dop), "grads": (dq, dk, dv)}, None
     ref = vo.block_sparse_attention_backward(op, gp.f64(g["q_perm"]), gp.f64(g["k_perm"]), gp.f64(vp), gp.f64(dop),
                                              sel, w.softmax_scale)
     return op, sel, col_ptr, row_idx, (dq, dk, dv), ref
@@ -334,6 +336,35 @@ def test_oracle_mask_mass_and_recall():
     heat_ref = vo.block_heat(op, qp, kp, L, w.softmax_scale)
     for h in range(w.num_heads):
         assert np.max(np.abs(heat_gpu[h] - heat_ref[h])) <= gp.HEAT_ABS
+
+
+def test_backward_config3_one_head():
+    """The bench's backward configuration (the 16x30x54 clip, 24 heads, full
+    size): transposed lists bit-exact on every head; dQ, dK, dV of one whole
+    head (all its rows, so every key tile's full column) against the fp64
+    oracle run on that head alone, from the same permuted inputs and mask."""
+    w = wl.workload(3)
+    op, sel, col_ptr, row_idx, got, _ = _backward_case(w, w.index, oracle=False)
+    tr = vo.mask_transpose(op, sel)
+    counts = [len(c) for rows in tr for c in rows]
+    cp = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    ri = np.concatenate([c for rows in tr for c in rows]).astype(np.int32)
+    assert np.array_equal(col_ptr.cpu().numpy(), cp) and np.array_equal(row_idx.cpu().numpy(), ri)
+    h = 7
+    sub = vo.Plan(w.segments, 1, w.head_dim, [w.tile_shapes[h]], w.budget_mode, w.keep_num, w.keep_den, w.fixed_k)
+    r0, L = op.row_offset[h], sub.total_rows
+    q, k, v, do = (gp.f64(t)[r0:r0 + L] for t in got["inputs"])
+    ref = vo.block_sparse_attention_backward(sub, q, k, v, do, [sel[h]], w.softmax_scale)
+    vr = gp.valid_rows(sub)
+    for name, a, b in zip(("dq", "dk", "dv"), got["grads"], ref):
+        a = gp.f64(a)[r0:r0 + L]
+        d = a[vr] - b[vr]
+        max_abs = float(np.max(np.abs(d)))
+        rel = float(np.linalg.norm(d) / np.linalg.norm(b[vr]))
+        print("config 3 head %d %s: max_abs %.3e (ref max %.3e) rel_l2 %.3e" % (h, name, max_abs,
+              np.max(np.abs(b[vr])), rel), flush=True)
+        assert rel <= gp.REL_L2 and max_abs <= gp.MAX_ABS * max(1.0, float(np.max(np.abs(b[vr]))))
+        assert not np.any(a[np.setdiff1d(np.arange(L), vr)]), name
 
 
 def _csr_to_selection(op, row_ptr, col):
