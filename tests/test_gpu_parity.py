@@ -141,6 +141,53 @@ def test_guard_large_late_logits():
     check_attention(w, inp, g, op, qp, kp, sel)
 
 
+def test_rows_longer_than_the_staged_list():
+    """Rows of more than 2048 key blocks (a dense 1-D segment of 2051 tiles,
+    the last one partial; one head, D = 64): the attention kernel stages a
+    row's block list in LDS 2048 entries at a time and refills it mid-row.
+    The plain inputs run the fast pass; with the keys of tile 2049 (past the
+    refill point) scaled by 64 every row exceeds the fast pass's bound and
+    the exact fallback pass, with its own refill, runs instead.  Sampled
+    query tiles against the oracle over all 2051 key tiles."""
+    n_tok = 128 * 2050 + 37
+    w = wl.Workload(97, "long_rows_2051_tiles", (wl.Segment(wl.DENSE1D, (1, 1, n_tok), 0),), 1, 64,
+                    ((2, 8, 8),), wl.KEEP_RATIO, 1, 10)
+    base = wl.make_inputs(w, seed=w.index)
+    op = vo.Plan.from_workload(w)
+    n = op.heads[0].num_tiles
+    assert n == 2051
+    perm = op.heads[0].perm()
+    for scaled in (False, True):
+        inp = dict(base)
+        if scaled:
+            k = base["k"].float()
+            toks = perm[128 * 2049: 128 * 2050]
+            k[torch.from_numpy(toks[toks >= 0].astype(np.int64)), 0, :] *= 64.0   # exact in bf16
+            inp["k"] = k.to(torch.bfloat16)
+        g = gp.gpu_path(w, inp, dense_mask=False)
+        rp, col = g["row_ptr"].cpu().numpy(), g["col_idx"].cpu().numpy()
+        for i in range(n):      # a dense segment keeps every key tile, ascending
+            assert np.array_equal(col[rp[i]:rp[i + 1]], np.arange(n))
+        assert int(g["visited"].item()) == n * n
+        qp, kp, vp = (vo.permute_forward(op, gp.f64(inp[x])) for x in ("q", "k", "v"))
+        if scaled:   # precondition: tile 2049's logits exceed the first key group's maximum by > 70 (log2 units)
+            c = w.softmax_scale / np.log(2.0)
+            q0 = qp[:128]
+            excess = (q0 @ kp[128 * 2049: 128 * 2050].T).max(1) - (q0 @ kp[:32].T).max(1)
+            assert float(np.max(excess)) * c > 70.0
+        o_nat, lse = gp.f64(g["o_nat"]), g["lse"].cpu().numpy().astype(np.float64)
+        for i in (0, 1024, n - 1):
+            O, L = vo.attention_row_tile(op, 0, i, qp, kp, vp, range(n), w.softmax_scale)
+            nv = op.heads[0].tiles[i].valid
+            got = o_nat[perm[128 * i: 128 * i + nv], 0]
+            max_abs = float(np.max(np.abs(got - O)))
+            rel = float(np.linalg.norm(got - O) / np.linalg.norm(O))
+            lerr = float(np.max(np.abs(lse[128 * i: 128 * i + nv] - L)))
+            print("long rows scaled=%s tile %d: max_abs %.3e rel_l2 %.3e lse %.3e" % (scaled, i, max_abs, rel, lerr),
+                  flush=True)
+            assert max_abs <= gp.MAX_ABS and rel <= gp.REL_L2 and lerr <= gp.LSE_ABS
+
+
 def test_guard_padding_mass():
     """Rows whose valid logits all sit far below zero while their key tiles
     have padding slots (logit exactly 0): the padding mass the fast pass
