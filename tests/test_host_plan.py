@@ -131,6 +131,8 @@ V = wl.VIDEO3D
     (dict(budget_mode=9), 1),
     (dict(budget_mode=wl.FIXED_K, fixed_k=-1), 1),
     (dict(segments=[(V, (4, 0, 8), 0)]), 2),
+    (dict(segments=[(wl.DENSE1D, (1, 1, 128 * 16384 + 1), 0)]), 3),    # 16385 tiles in one head
+    (dict(num_heads=1025, tile_shapes=[(2, 8, 8)] * 1025), 3),
 ])
 def test_plan_validation(case, status):
     args = dict(segments=[(V, (4, 8, 8), 0)], num_heads=1, head_dim=64, tile_shapes=[(2, 8, 8)],
@@ -140,6 +142,16 @@ def test_plan_validation(case, status):
         args["num_heads"] = len(args["tile_shapes"])
     assert _status_of(vb.veda_plan_create, **args) == status
     assert vb.veda_last_error()
+
+
+def test_largest_head_is_accepted():
+    """A head of exactly 16384 tiles (the kernels' largest) builds a plan;
+    one more tile is refused (above)."""
+    h = vb.veda_plan_create([(wl.DENSE1D, (1, 1, 128 * 16384), 0)], 1, 64, [(2, 8, 8)], wl.KEEP_RATIO, 1, 10, 0)
+    try:
+        assert vb.veda_plan_query(h)["max_tiles_per_head"] == 16384
+    finally:
+        vb.veda_plan_destroy(h)
 
 
 def test_compute_calls_check_on_host_before_any_launch():
@@ -157,6 +169,11 @@ def test_compute_calls_check_on_host_before_any_launch():
         assert lib.veda_permute_qkv(h, fake, fake, fake, fake, fake, fake, None, 0, None) == 6
         assert lib.veda_score_pooled(h, fake, fake, fake, fake, 1 << 20, None) == 6
         assert lib.veda_block_heat(h, fake, fake, fake, ctypes.c_float(0.125), fake, None) == 6
+        assert lib.veda_mask_mass(h, fake, fake, fake, fake, None) == 6
+        assert lib.veda_output_error(h, fake, fake, fake, None) == 6
+        assert lib.veda_mask_transpose(h, fake, fake, fake, fake, fake, 1 << 30, None) == 6
+        assert lib.veda_block_sparse_attn_bwd(h, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                              ctypes.c_float(0.125), fake, fake, fake, fake, 1 << 30, None) == 6
         assert "upload" in vb.veda_last_error()
         # null plan
         assert lib.veda_permute_tiles(None, fake, fake, 0, None) == 1
