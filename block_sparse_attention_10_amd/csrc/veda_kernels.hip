@@ -619,69 +619,6 @@ __device__ __forceinline__ int pi_row(int m) {  // swap bits 2 and 3
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-template <int D>
-struct AttnTiles {
-  static constexpr int CH = D / 8;           // 16-byte chunks per K row
-  static constexpr int KB = kTile * D;       // bf16 elements of one K / V^T tile
-};
-
-// Stage a K tile (rows in pi order, swizzled) and a V^T tile into LDS.
-template <int D>
-__device__ __forceinline__ void load_kv_tile(uint16_t* __restrict__ ks, uint16_t* __restrict__ vs,
-                                             const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg) {
-  constexpr int CH = D / 8;
-  constexpr int KCH = kTile * CH;  // chunks per K tile
-  constexpr int PER = KCH / kThreads;
-  {
-    u32x4 kr[PER];
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int q = it * kThreads + threadIdx.x;
-      const int m = q / CH, pc = q % CH;
-      const int c = pc ^ (m & (CH - 1));
-      const int key = (m & ~31) | pi_row(m & 31);
-      kr[it] = ld16(kg + (int64_t)key * D + 8 * c);
-    }
-#pragma unroll
-    for (int it = 0; it < PER; ++it) st16(ks + 8 * (it * kThreads + threadIdx.x), kr[it]);
-  }
-  if (vs) {
-    u32x4 vr[PER];
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int q = it * kThreads + threadIdx.x;
-      const int d = q / 16, pc = q % 16;
-      const int c = pc ^ (d & 15);
-      vr[it] = ld16(vg + (int64_t)d * kTile + 8 * c);
-    }
-#pragma unroll
-    for (int it = 0; it < PER; ++it) st16(vs + 8 * (it * kThreads + threadIdx.x), vr[it]);
-  }
-}
-
-// S^T for one 128-key block: sacc[kt] covers keys 32kt.. in MFMA row order.
-template <int D>
-__device__ __forceinline__ void qk_block(const uint16_t* __restrict__ ks, const bf16x8 (&qf)[D / 16],
-                                         f32x16 (&sacc)[4]) {
-  constexpr int CH = D / 8;
-  const int lane = lane_id();
-  const int ln = lane & 31, hl = lane >> 5;
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    f32x16 acc = {};
-    const int m = 32 * kt + ln;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      const int c = 2 * s + hl;
-      const u32x4 raw = ld16(ks + m * D + 8 * (c ^ (m & (CH - 1))));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, raw);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc, 0, 0, 0);
-    }
-    sacc[kt] = acc;
-    __builtin_amdgcn_sched_barrier(0);   // keep operand reads of one group together
-  }
-}
-
 // Key index (0..127 inside the block) held by S^T register r of key group kt.
 __device__ __forceinline__ int sacc_key(int kt, int r, int hl) {
   return 32 * kt + 16 * (r >> 3) + 8 * hl + (r & 7);
@@ -868,10 +805,7 @@ __device__ __forceinline__ float exp_group(const f32x16& sg, float c, float m, b
 // the softmax work is spread between the MFMAs and an MFMA's operand has
 // usually arrived when it issues (a wave issues in order: an operand wait
 // also holds back the VALU work behind it).
-#ifndef VEDA_LDS_AHEAD
-#define VEDA_LDS_AHEAD 2
-#endif
-constexpr int kLdsAhead = VEDA_LDS_AHEAD;
+constexpr int kLdsAhead = 2;
 template <int NMFMA, int VALU>
 __device__ __forceinline__ void interleave_step() {
   __builtin_amdgcn_sched_group_barrier(0x100, kLdsAhead, 0);  // DS read
@@ -1695,25 +1629,6 @@ __device__ __forceinline__ void tr_group(const uint16_t* __restrict__ tile, cons
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pg[s2], acc[db], 0, 0, 0);
     }
   }
-}
-
-// Scheduling pattern of one backward pipeline step: NMFMA MFMAs, each
-// followed by DS reads (alternately R0 and R1 of them, operands of later
-// MFMAs) and VALU instructions of the softmax step.
-template <int NMFMA, int R0, int R1, int VALU>
-__device__ __forceinline__ void bwd_interleave() {
-#ifndef VEDA_BWD_NO_INTERLEAVE
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // DS read
-#pragma unroll
-  for (int i = 0; i < NMFMA / 2; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, R0, 0);
-    if (VALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, R1, 0);
-    if (VALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
-  }
-#endif
 }
 
 // The wave's B operand for 32 rows of a permuted tile: lane (ln, hl) holds
