@@ -1358,10 +1358,12 @@ __global__ void __launch_bounds__(512) output_error_kernel(int64_t num_tokens, i
 // backward: transposed lists
 // ---------------------------------------------------------------------------
 //
-// The per-key-tile lists come from a byte matrix per head (m[i][j] = 1 iff
-// key tile j is in query tile i's row): scatter the CSR into it, then one
-// thread per key tile walks its column twice, counting and then listing the
-// query tiles in ascending order.  No atomics, so the order is fixed.
+// The per-key-tile lists come from a byte matrix per head, stored key tile
+// major (m[j][i] = 1 iff key tile j is in query tile i's row, so a column of
+// the mask is contiguous): scatter the CSR into it, then one wave per key
+// tile walks its column twice, 64 query tiles per ballot, counting and then
+// listing the query tiles in ascending order (ballot ranks give each its
+// position).  No atomics, so the order is fixed.
 __global__ void __launch_bounds__(kThreads) fill_u32_kernel(uint32_t* __restrict__ x, int64_t n, uint32_t v) {
   for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += (int64_t)gridDim.x * kThreads) x[e] = v;
 }
@@ -1373,33 +1375,34 @@ __global__ void __launch_bounds__(64) csc_scatter_kernel(DevPlan p, const int32_
   const int h = p.row_head[t];
   const int n = p.shape[p.head_shape[h]].num_tiles;
   const int i = t - p.head_tile_off[h];
-  uint8_t* m = bitmap + p.head_pair_off[h] + (int64_t)i * n;
+  uint8_t* m = bitmap + p.head_pair_off[h] + i;
   for (int e = row_ptr[t] + (int)threadIdx.x; e < row_ptr[t + 1]; e += 64) {
     const int j = col_idx[e];
-    if (j >= 0 && j < n) m[j] = 1;
+    if (j >= 0 && j < n) m[(int64_t)j * n] = 1;
   }
 }
 
 template <bool FILL>
-__global__ void __launch_bounds__(kThreads) csc_column_kernel(DevPlan p, const uint8_t* __restrict__ bitmap,
-                                                             int32_t* __restrict__ counts,
-                                                             const int32_t* __restrict__ col_ptr,
-                                                             int32_t* __restrict__ row_idx) {
-  const int64_t tc = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (tc >= p.total_tiles) return;
-  const int h = p.row_head[tc];
-  const int n = p.shape[p.head_shape[h]].num_tiles;
-  const int j = (int)(tc - p.head_tile_off[h]);
-  const uint8_t* m = bitmap + p.head_pair_off[h] + j;
-  if (!FILL) {
-    int c = 0;
-    for (int i = 0; i < n; ++i) c += m[(int64_t)i * n];
-    counts[tc] = c;
-  } else {
-    int32_t pos = col_ptr[tc];
-    for (int i = 0; i < n; ++i)
-      if (m[(int64_t)i * n]) row_idx[pos++] = i;
+__global__ void __launch_bounds__(64) csc_column_kernel(DevPlan p, const uint8_t* __restrict__ bitmap,
+                                                       int32_t* __restrict__ counts,
+                                                       const int32_t* __restrict__ col_ptr,
+                                                       int32_t* __restrict__ row_idx) {
+  const int64_t tc = blockIdx.x;           // one wave per key tile
+  const int h = uni(p.row_head[tc]);
+  const int n = uni(p.shape[uni(p.head_shape[h])].num_tiles);
+  const int j = (int)(tc - uni(p.head_tile_off[h]));
+  const uint8_t* m = bitmap + uni64(p.head_pair_off[h]) + (int64_t)j * n;
+  const int lane = lane_id();
+  const uint64_t below = lanes_below();
+  int32_t pos = FILL ? col_ptr[tc] : 0;
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int i = i0 + lane;
+    const bool set = i < n && m[i] != 0;
+    const uint64_t bal = __ballot(set);
+    if (FILL && set) row_idx[pos + __popcll(bal & below)] = i;
+    pos += __popcll(bal);
   }
+  if (!FILL && lane == 0) counts[tc] = pos;
 }
 
 // Exclusive scan of counts[0..n) into col_ptr[0..n]; one workgroup, chunks
@@ -2057,10 +2060,10 @@ hipError_t launch_mask_transpose(const DevPlan& p, const int32_t* row_ptr, const
   hipLaunchKernelGGL(fill_u32_kernel, dim3(std::max(fill_blocks, 1u)), dim3(kThreads), 0, s,
                      reinterpret_cast<uint32_t*>(bitmap), words, 0u);
   hipLaunchKernelGGL(csc_scatter_kernel, dim3((unsigned)p.total_tiles), dim3(64), 0, s, p, row_ptr, col_idx, bitmap);
-  const dim3 gcol((unsigned)((p.total_tiles + kThreads - 1) / kThreads));
-  hipLaunchKernelGGL(csc_column_kernel<false>, gcol, dim3(kThreads), 0, s, p, bitmap, counts, nullptr, nullptr);
+  const dim3 gcol((unsigned)p.total_tiles);
+  hipLaunchKernelGGL(csc_column_kernel<false>, gcol, dim3(64), 0, s, p, bitmap, counts, nullptr, nullptr);
   hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(1024), 0, s, counts, (int64_t)p.total_tiles, col_ptr);
-  hipLaunchKernelGGL(csc_column_kernel<true>, gcol, dim3(kThreads), 0, s, p, bitmap, counts, col_ptr, row_idx);
+  hipLaunchKernelGGL(csc_column_kernel<true>, gcol, dim3(64), 0, s, p, bitmap, counts, col_ptr, row_idx);
   return hipGetLastError();
 }
 
