@@ -9,8 +9,14 @@
 //   select    per-row radix top-k on order-preserving 32-bit keys, ties to the
 //             lowest key tile, ascending CSR by wavefront ballot compaction
 //   attn_fwd  block-sparse flash attention over the CSR, bf16 MFMA
-//             (32x32x16), fp32 online softmax in the log2 domain
+//             (32x32x16), fp32 softmax in the log2 domain against a fixed
+//             per-row reference point (exact online-softmax fallback)
 //   heat      block heat from the dense LSE, same QK^T machinery, no PV
+//   mass      attention mass a block mask keeps (fp64, fixed order)
+//   error     relative output error of two outputs per head (fp64)
+//   backward  transposed (per key tile) block lists; dV and dK per key tile
+//             (dV and dK waves, P' handed over in LDS), dQ per query tile,
+//             both with LDS transpose reads and no atomics
 //
 // The method is the Veda sparse attention of the Miowtion project page
 // ("Sparse acceleration (Veda)"; Key Features > "Veda sparse attention") and
