@@ -155,8 +155,8 @@ def _cpu_model():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the Veda path shards by heads with no exchange, and multi-GPU "
-              "runs are not part of this build (got --gpus %d)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU: the Veda path shards by heads with no exchange, and the library "
+              "has no multi-GPU path (got --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     from block_sparse_attention_10_amd import binding as vb
     ok, why = vb.veda_available(0)
