@@ -47,7 +47,7 @@ KEEP_RATIO = 0
 FIXED_K = 1
 ALL_BLOCKS = 2
 
-TILE_TOKENS = 128   # tokens per tile ("3D tiles of 128 tokens")
+TILE_TOKENS = 128   # tokens per tile (Miowtion page, "Sparse acceleration (Veda)": 3-D tiles of 128 tokens)
 
 
 def ceil_div(a: int, b: int) -> int:
