@@ -71,7 +71,6 @@ class Layer:
             self.dense = vb.Plan.from_workload(w, budget_mode=wl.ALL_BLOCKS)
             self.d_row_ptr = torch.empty(p.T + 1, dtype=torch.int32, device=dev)
             self.d_col = torch.empty(self.dense.info["nnz"], dtype=torch.int32, device=dev)
-            self.d_o = p.empty_perm()
             self.d_lse = torch.empty(p.R, dtype=torch.float32, device=dev)
             self.heat = torch.empty(p.info["total_pairs"], dtype=torch.float32, device=dev)
             # oracle mask (selection on the heat) and the attention mass of both masks
@@ -98,8 +97,8 @@ class Layer:
         if self.dense is not None:
             d = self.dense
             d.select(self.scores, self.d_row_ptr, self.d_col)
-            d.attention(self.qp, self.kp, self.vt, self.d_row_ptr, self.d_col, w.softmax_scale, self.d_o,
-                        self.d_lse)
+            d.attention(self.qp, self.kp, self.vt, self.d_row_ptr, self.d_col, w.softmax_scale, None,
+                        self.d_lse)   # the dense LSE only
             p.heat(self.qp, self.kp, self.d_lse, w.softmax_scale, self.heat)
             p.select(self.heat, self.o_row_ptr, self.o_col)
             p.mask_mass(self.heat, self.row_ptr, self.col, self.m_pred)

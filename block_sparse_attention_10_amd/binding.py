@@ -436,7 +436,10 @@ class Plan:
         self._expect(row_ptr, (self.T + 1,), torch.int32, "row_ptr")
         if col_idx is None or col_idx.dtype != torch.int32 or not col_idx.is_cuda:
             raise ValueError("col_idx must be an int32 CUDA tensor")
-        if o_layout == VEDA_LAYOUT_NATURAL:
+        if o is None:          # only the LSE
+            if lse is None:
+                raise ValueError("attention: o and lse are both None")
+        elif o_layout == VEDA_LAYOUT_NATURAL:
             self._expect(o, (self.N, self.H, self.D), bf, "o")
         else:
             self._expect(o, (self.R, self.D), bf, "o")

@@ -669,16 +669,18 @@ veda_status veda_block_sparse_attn_fwd(const veda_plan* p, const void* q, const 
   veda_status st = check_plan_ready(p);
   if (st) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v_t, "v_t")) ||
-      (st = check_ptr(row_ptr, "row_ptr")) || (st = check_ptr(col_idx, "col_idx")) || (st = check_ptr(o, "o")))
+      (st = check_ptr(row_ptr, "row_ptr")) || (st = check_ptr(col_idx, "col_idx")))
     return st;
+  if (o && (st = check_ptr(o, "o"))) return st;
   if (lse && (st = check_ptr(lse, "lse"))) return st;
+  if (!o && !lse) return fail(VEDA_ERR_INVALID_ARG, "o and lse are both NULL: nothing to compute");
   if (blocks_visited && (reinterpret_cast<uintptr_t>(blocks_visited) & 3))
     return fail(VEDA_ERR_INVALID_ARG, "blocks_visited is not 4-byte aligned");
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
     return fail(VEDA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if (o_layout != VEDA_LAYOUT_PERMUTED && o_layout != VEDA_LAYOUT_NATURAL)
     return fail(VEDA_ERR_INVALID_ARG, "unknown o_layout %d", o_layout);
-  if (o == q || o == k || o == v_t) return fail(VEDA_ERR_INVALID_ARG, "o aliases an input");
+  if (o && (o == q || o == k || o == v_t)) return fail(VEDA_ERR_INVALID_ARG, "o aliases an input");
   return launched(launch_attn_fwd(p->dev, q, k, v_t, row_ptr, col_idx, softmax_scale, o,
                                   o_layout == VEDA_LAYOUT_NATURAL, lse, blocks_visited, (hipStream_t)stream),
                   "block-sparse attention");

@@ -713,10 +713,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
-// Synchronous copy (plain loads and LDS stores) of one K tile and one V^T
-// tile into the four half arrays in the layouts the asynchronous copies
-// produce.
-template <int D>
+// Synchronous copy (plain loads and LDS stores) of one K tile and (with V)
+// one V^T tile into the four half arrays in the layouts the asynchronous
+// copies produce.
+template <int D, bool V>
 __device__ __forceinline__ void copy_kv_halves(uint16_t* __restrict__ kh0, uint16_t* __restrict__ kh1,
                                                uint16_t* __restrict__ vh0, uint16_t* __restrict__ vh1,
                                                const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg) {
@@ -729,6 +729,7 @@ __device__ __forceinline__ void copy_kv_halves(uint16_t* __restrict__ kh0, uint1
     uint16_t* dst = (m < 64 ? kh0 : kh1) + (m & 63) * D + 8 * pos;
     st16(dst, ld16(kg + (int64_t)key * D + 8 * cc));
   }
+  if (!V) return;
 #pragma unroll 1
   for (int q = threadIdx.x; q < D * 16; q += kThreads) {
     const int d = q / 16, pc = q % 16;                // V^T row and 16-byte chunk position in LDS
@@ -876,7 +877,7 @@ __device__ __forceinline__ int half_pads(int nv, int hh) {
 // every wave has done QK of group 1, K rows of groups 2-3 and V^T keys 0-63
 // once every wave has done QK of group 3 and PV of group 1, V^T keys 64-127
 // after the block.  Two workgroups share a CU (72 KB of LDS each).
-template <int D>
+template <int D, bool PV>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ vt,
@@ -969,36 +970,40 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
       pin(p0);
       interleave_step<8, 6>();
     }
-    dma_sync<H>();                    // V^T(b) keys 0-63 have landed; K rows 0-63 are free
+    // V^T(b) keys 0-63 have landed (without PV: K rows 64-127 have); K rows
+    // 0-63 are free
+    dma_sync<PV ? H : 0>();
     if (more) dma_k_half<D>(kh0, rk, jn * kTile * D * 2, koff, wave, 0);
     __builtin_amdgcn_sched_barrier(0);
     if (compute) {
       s2 = qk_group<D>(kh1, qf, 2, zero16);
-      pv_group<D>(vh0, p0, 0, oacc);
+      if constexpr (PV) pv_group<D>(vh0, p0, 0, oacc);
       l_run += exp_group<true>(s1, c, m_run, p1);
       pin(p1);
-      interleave_step<16, 3>();
+      interleave_step<PV ? 16 : 8, 3>();
       __builtin_amdgcn_sched_barrier(0);
       s3 = qk_group<D>(kh1, qf, 3, zero16);
-      pv_group<D>(vh0, p1, 1, oacc);
+      if constexpr (PV) pv_group<D>(vh0, p1, 1, oacc);
       l_run += exp_group<true>(s2, c, m_run, p2);
       pin(p2);
-      interleave_step<16, 3>();
+      interleave_step<PV ? 16 : 8, 3>();
     }
     if (more) dma_sync<H>(); else dma_sync<0>();   // V^T(b) keys 64-127 have landed; K, V^T keys 0-63 free
     if (more) {
       dma_k_half<D>(kh1, rk, jn * kTile * D * 2, koff, wave, 1);
-      dma_vt_half<D>(vh0, rv, jn * kTile * D * 2, voff, wave, 0);
+      if constexpr (PV) dma_vt_half<D>(vh0, rv, jn * kTile * D * 2, voff, wave, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (compute) {
-      pv_group<D>(vh1, p2, 2, oacc);
+      if constexpr (PV) pv_group<D>(vh1, p2, 2, oacc);
       l_run += exp_group<true>(s3, c, m_run, p3);
       pin(p3);
-      interleave_step<8, 6>();
+      interleave_step<PV ? 8 : 0, 6>();
       __builtin_amdgcn_sched_barrier(0);
-      pv_group<D>(vh1, p3, 3, oacc);
-      interleave_step<8, 0>();
+      if constexpr (PV) {
+        pv_group<D>(vh1, p3, 3, oacc);
+        interleave_step<8, 0>();
+      }
       npad += ((ent >> 7) & 127) + (ent & 127);
     }
   };
@@ -1027,8 +1032,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
       const int jn = en >> 14;
       block(b >= beg, b == beg, ent, more, jn);
       if (more) {
-        dma_sync<H>();                // K(b+1) has landed; every wave is done with V^T(b)
-        dma_vt_half<D>(vh1, rv, jn * kTile * D * 2, voff, wave, 1);
+        dma_sync<H>();                // K(b+1) has landed (without PV: its rows 0-63); every wave is done with V^T(b)
+        if constexpr (PV) dma_vt_half<D>(vh1, rv, jn * kTile * D * 2, voff, wave, 1);
       }
       ent = en;
       if (b + 2 < end) {
@@ -1058,8 +1063,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
       const int j = ent >> 14;
       const int nj = kTile - ((ent >> 7) & 127) - (ent & 127);
       lds_sync();                     // every wave is done with the previous tiles
-      copy_kv_halves<D>(kh0, kh1, vh0, vh1, k + (hrow + (int64_t)kTile * j) * D,
-                        vt + (htile + j) * D * kTile);
+      copy_kv_halves<D, PV>(kh0, kh1, vh0, vh1, k + (hrow + (int64_t)kTile * j) * D,
+                            vt + (htile + j) * D * kTile);
       lds_sync();
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
@@ -1078,7 +1083,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
         }
         bf16x8 pg[2];
         l_run += exp_group<true>(sg, c, m_run, pg);
-        pv_group<D>(kt < 2 ? vh0 : vh1, pg, kt, oacc);
+        if constexpr (PV) pv_group<D>(kt < 2 ? vh0 : vh1, pg, kt, oacc);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1096,31 +1101,33 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
     l_all = l_run + __shfl_xor(l_run, 32, 64);
   }
 
-  // epilogue: normalise, store
-  const float inv = 1.0f / l_all;
-  // permuted: row row0 + slot; natural: the slot's token, padding dropped
-  uint16_t* orow = o + (row0 + 32 * w + ln) * D;
-  bool store = true;
-  if (o_natural) {
-    const int slot = 32 * w + ln;
-    const int32_t tok = sh.perm[(int64_t)kTile * i + slot];
-    store = tok >= 0;
-    orow = o + ((int64_t)(store ? tok : 0) * p.num_heads + h) * D;
-  }
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      bf16x2 lo, hi;
-      lo[0] = (__bf16)(oacc[db][4 * jj + 0] * inv);
-      lo[1] = (__bf16)(oacc[db][4 * jj + 1] * inv);
-      hi[0] = (__bf16)(oacc[db][4 * jj + 2] * inv);
-      hi[1] = (__bf16)(oacc[db][4 * jj + 3] * inv);
-      uint2 v;
-      v.x = __builtin_bit_cast(uint32_t, lo);
-      v.y = __builtin_bit_cast(uint32_t, hi);
-      if (store) *reinterpret_cast<uint2*>(orow + 32 * db + 8 * jj + 4 * hl) = v;
+  // epilogue: normalise, store (without PV only the LSE)
+  if constexpr (PV) {
+    const float inv = 1.0f / l_all;
+    // permuted: row row0 + slot; natural: the slot's token, padding dropped
+    uint16_t* orow = o + (row0 + 32 * w + ln) * D;
+    bool store = true;
+    if (o_natural) {
+      const int slot = 32 * w + ln;
+      const int32_t tok = sh.perm[(int64_t)kTile * i + slot];
+      store = tok >= 0;
+      orow = o + ((int64_t)(store ? tok : 0) * p.num_heads + h) * D;
     }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        bf16x2 lo, hi;
+        lo[0] = (__bf16)(oacc[db][4 * jj + 0] * inv);
+        lo[1] = (__bf16)(oacc[db][4 * jj + 1] * inv);
+        hi[0] = (__bf16)(oacc[db][4 * jj + 2] * inv);
+        hi[1] = (__bf16)(oacc[db][4 * jj + 3] * inv);
+        uint2 v;
+        v.x = __builtin_bit_cast(uint32_t, lo);
+        v.y = __builtin_bit_cast(uint32_t, hi);
+        if (store) *reinterpret_cast<uint2*>(orow + 32 * db + 8 * jj + 4 * hl) = v;
+      }
+  }
   if (lse && hl == 0) lse[row0 + 32 * w + ln] = m_run * 0.69314718055994531f + logf(l_all);
   if (visited && threadIdx.x == 0) atomicAdd(visited, (uint32_t)(end - beg));
 }
@@ -2014,12 +2021,21 @@ hipError_t launch_attn_fwd(const DevPlan& p, const void* q, const void* k, const
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(vt);
   uint16_t* oo = static_cast<uint16_t*>(o);
+  // o == nullptr: only the LSE (no PV products, no V^T copies)
   if (p.head_dim == 128) {
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
-                       scale_log2, oo, o_natural, lse, visited);
+    if (oo)
+      hipLaunchKernelGGL((attn_fwd_kernel<128, true>), grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
+                         scale_log2, oo, o_natural, lse, visited);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<128, false>), grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
+                         scale_log2, oo, o_natural, lse, visited);
   } else {
-    hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
-                       scale_log2, oo, o_natural, lse, visited);
+    if (oo)
+      hipLaunchKernelGGL((attn_fwd_kernel<64, true>), grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
+                         scale_log2, oo, o_natural, lse, visited);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<64, false>), grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
+                         scale_log2, oo, o_natural, lse, visited);
   }
   return hipGetLastError();
 }

@@ -246,8 +246,11 @@ veda_status veda_select_blocks(const veda_plan* plan, const float* scores, int32
  *           padding slots unspecified (finite); VEDA_LAYOUT_NATURAL:
  *           [N, H, D], every token of head h written at its natural place
  *           (the inverse permutation fused into the epilogue), padding
- *           slots dropped
- *   lse:    device fp32 [R] natural log, permuted row order, or NULL
+ *           slots dropped.  Or NULL: then only the LSE is computed (no PV
+ *           products; v_t is not read), bitwise equal to the LSE of a call
+ *           with o, e.g. the dense LSE that veda_block_heat takes.
+ *   lse:    device fp32 [R] natural log, permuted row order, or NULL (not
+ *           both o and lse NULL: VEDA_ERR_INVALID_ARG)
  *   blocks_visited: device uint32 counter the kernel adds the number of
  *           blocks it computed to (caller zeroes it), or NULL.
  * softmax_scale must be finite and > 0 (1/sqrt(D) for the usual scale). */

@@ -188,6 +188,34 @@ def test_rows_longer_than_the_staged_list():
             assert max_abs <= gp.MAX_ABS and rel <= gp.REL_L2 and lerr <= gp.LSE_ABS
 
 
+@pytest.mark.parametrize("kind", ["small", "guard_all_blocks", "guard_late_logits"])
+def test_lse_only_equals_full_attention(kind):
+    """veda_block_sparse_attn_fwd with o = NULL computes only the LSE (no PV
+    products): bitwise equal to the LSE of the full call, on the fast pass
+    and on the fallback pass (forced by late logits)."""
+    ws = small_workloads() if kind == "small" else [_guard_workload()]
+    for w in ws:
+        inp = wl.make_inputs(w, seed=w.index)
+        if kind == "guard_late_logits":
+            op = vo.Plan.from_workload(w)
+            k = inp["k"].float()
+            for h in range(w.num_heads):
+                perm = op.heads[h].perm()
+                last = perm[(op.heads[h].num_tiles - 1) * 128:]
+                k[torch.from_numpy(last[last >= 0].astype(np.int64)), h, :] *= 64.0
+            inp["k"] = k.to(torch.bfloat16)
+        g = gp.gpu_path(w, inp, dense_mask=False)
+        plan = g["plan"]
+        lse2 = torch.full_like(g["lse"], float("nan"))
+        visited = torch.zeros(1, dtype=torch.int32, device="cuda")
+        plan.attention(g["q_perm"], g["k_perm"], g["v_t"], g["row_ptr"], g["col_idx"], w.softmax_scale, None, lse2,
+                       visited)
+        torch.cuda.synchronize()
+        a, b = g["lse"].cpu().numpy(), lse2.cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), w.name
+        assert int(visited.item()) == int(g["visited"].item())
+
+
 def test_guard_padding_mass():
     """Rows whose valid logits all sit far below zero while their key tiles
     have padding slots (logit exactly 0): the padding mass the fast pass
