@@ -807,6 +807,22 @@ __device__ __forceinline__ float exp_group(const f32x16& sg, float c, float m, b
   return SUM ? (acc[0] + acc[1]) + (acc[2] + acc[3]) : 0.0f;
 }
 
+// The lane's fp32 sum of p = exp2(s*c - m) over a group's 16 keys, in the
+// same order as exp_group<true> (so both give bitwise the same sum), without
+// packing p.
+__device__ __forceinline__ float exp_sum(const f32x16& sg, float c, float m) {
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sg[8 * s2 + 2 * e], c, -m));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sg[8 * s2 + 2 * e + 1], c, -m));
+      acc[e] += p0 + p1;
+    }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 // Scheduling pattern for one pipeline step: kLdsAhead LDS operand reads
 // ahead, then per MFMA one more read and up to `valu` vector instructions, so
 // the softmax work is spread between the MFMAs and an MFMA's operand has
@@ -951,6 +967,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
   // without VALU work and doubles the next step's.
   auto pin = [](bf16x8 (&pg)[2]) { asm volatile("" : "+v"(pg[0]), "+v"(pg[1])); };
 
+  // Without PV a group's softmax step is only the sum of p (pinned, so that
+  // it stays in its pipeline step like the packed p with PV).
+  auto pin_sum = [](float& l) { asm volatile("" : "+v"(l)); };
+
   // One key block of the fast pass.  Steps are separated by scheduling
   // barriers so that the compiler keeps each step's operand reads and MFMAs
   // together with that step's softmax work (and register lifetimes short).
@@ -966,8 +986,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
       if (first) m_run = group_max(s0) * c;   // finite: key 0 always exists
       __builtin_amdgcn_sched_barrier(0);
       s1 = qk_group<D>(kh0, qf, 1, zero16);
-      l_run += exp_group<true>(s0, c, m_run, p0);
-      pin(p0);
+      if constexpr (PV) {
+        l_run += exp_group<true>(s0, c, m_run, p0);
+        pin(p0);
+      } else {
+        l_run += exp_sum(s0, c, m_run);
+        pin_sum(l_run);
+      }
       interleave_step<8, 6>();
     }
     // V^T(b) keys 0-63 have landed (without PV: K rows 64-127 have); K rows
@@ -978,14 +1003,24 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
     if (compute) {
       s2 = qk_group<D>(kh1, qf, 2, zero16);
       if constexpr (PV) pv_group<D>(vh0, p0, 0, oacc);
-      l_run += exp_group<true>(s1, c, m_run, p1);
-      pin(p1);
+      if constexpr (PV) {
+        l_run += exp_group<true>(s1, c, m_run, p1);
+        pin(p1);
+      } else {
+        l_run += exp_sum(s1, c, m_run);
+        pin_sum(l_run);
+      }
       interleave_step<PV ? 16 : 8, 3>();
       __builtin_amdgcn_sched_barrier(0);
       s3 = qk_group<D>(kh1, qf, 3, zero16);
       if constexpr (PV) pv_group<D>(vh0, p1, 1, oacc);
-      l_run += exp_group<true>(s2, c, m_run, p2);
-      pin(p2);
+      if constexpr (PV) {
+        l_run += exp_group<true>(s2, c, m_run, p2);
+        pin(p2);
+      } else {
+        l_run += exp_sum(s2, c, m_run);
+        pin_sum(l_run);
+      }
       interleave_step<PV ? 16 : 8, 3>();
     }
     if (more) dma_sync<H>(); else dma_sync<0>();   // V^T(b) keys 64-127 have landed; K, V^T keys 0-63 free
@@ -996,8 +1031,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
     __builtin_amdgcn_sched_barrier(0);
     if (compute) {
       if constexpr (PV) pv_group<D>(vh1, p2, 2, oacc);
-      l_run += exp_group<true>(s3, c, m_run, p3);
-      pin(p3);
+      if constexpr (PV) {
+        l_run += exp_group<true>(s3, c, m_run, p3);
+        pin(p3);
+      } else {
+        l_run += exp_sum(s3, c, m_run);
+        pin_sum(l_run);
+      }
       interleave_step<PV ? 8 : 0, 6>();
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (PV) {
