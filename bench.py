@@ -308,7 +308,8 @@ def time_backward(layer, w, steps):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     flops = 10.0 * 128 * 128 * w.head_dim * p.info["nnz"]
-    return {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "flop_count": "10 * 128^2 * D per computed block (dV, dP, dK, dQ, recomputed S)",
             "includes": "transposed lists, per-row (lse, rowsum(dO*O)), key-tile dispatch order, dK/dV and dQ kernels"}
 
