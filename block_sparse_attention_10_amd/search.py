@@ -2,12 +2,14 @@
 tile-plan search by relative output MSE under the best mask, majority vote,
 at most two shapes per layer).
 
-For every sample (q, k, v of one layer) and every candidate (t, h, w) tile
-shape, run through libveda:
-  permute (veda_permute_qkv) -> all-blocks attention (dense output in natural
-  order and the dense LSE) -> block heat (veda_block_heat) -> oracle mask
-  (veda_select_blocks on the heat, the layer's budgets) -> block-sparse
-  attention over it -> relative output error per head (veda_output_error);
+For every sample (q, k, v of one layer) the dense output in natural token
+order is computed once (all-blocks attention under the first candidate's
+tiling; in natural order it does not depend on the tiling).  Then for every
+candidate (t, h, w) tile shape, through libveda:
+  permute (veda_permute_qkv) -> the dense LSE (all-blocks attention without o)
+  -> block heat (veda_block_heat) -> oracle mask (veda_select_blocks on the
+  heat, the layer's budgets) -> block-sparse attention over it -> relative
+  output error per head against the dense output (veda_output_error);
 then the vote over the error table (veda_tile_plan_vote).  This module only
 sequences library calls and owns the device buffers (torch allocations).
 """
@@ -24,29 +26,41 @@ def tile_plan_search(segments, num_heads, head_dim, candidates, budget_mode, kee
     S, C = len(samples), len(candidates)
     dev = "cuda"
     err = torch.empty((S, C, num_heads), dtype=torch.float64, device=dev)
-    for ci, shape in enumerate(candidates):
+
+    def plans(shape):
         shapes = [tuple(shape)] * num_heads
         p = vb.Plan(segments, num_heads, head_dim, shapes, budget_mode, keep_num, keep_den, fixed_k)
         pd = vb.Plan(segments, num_heads, head_dim, shapes, vb.VEDA_BUDGET_ALL)
-        qp, kp, vt, ws = p.empty_perm(), p.empty_perm(), p.empty_vt(), p.empty_workspace()
         pairs = p.info["total_pairs"]
-        heat = torch.empty(pairs, dtype=torch.float32, device=dev)
         d_rp = torch.empty(p.T + 1, dtype=torch.int32, device=dev)
         d_col = torch.empty(pd.info["nnz"], dtype=torch.int32, device=dev)
         pd.select(torch.zeros(pairs, dtype=torch.float32, device=dev), d_rp, d_col, stream=stream)
+        return p, pd, d_rp, d_col
+
+    # dense outputs, natural order, one per sample
+    p, pd, d_rp, d_col = plans(candidates[0])
+    qp, kp, vt, ws = p.empty_perm(), p.empty_perm(), p.empty_vt(), p.empty_workspace()
+    o_dense = []
+    for q, k, v in samples:
+        o = torch.empty_like(q)
+        p.permute_qkv(q, k, v, qp, kp, vt, ws, stream=stream)
+        pd.attention(qp, kp, vt, d_rp, d_col, scale, o, stream=stream, o_layout=vb.VEDA_LAYOUT_NATURAL)
+        o_dense.append(o)
+    for ci, shape in enumerate(candidates):
+        p, pd, d_rp, d_col = plans(shape)
+        qp, kp, vt, ws = p.empty_perm(), p.empty_perm(), p.empty_vt(), p.empty_workspace()
+        heat = torch.empty(p.info["total_pairs"], dtype=torch.float32, device=dev)
         rp = torch.empty(p.T + 1, dtype=torch.int32, device=dev)
         col = torch.empty(p.info["nnz"], dtype=torch.int32, device=dev)
         lse = torch.empty(p.R, dtype=torch.float32, device=dev)
         for si, (q, k, v) in enumerate(samples):
-            o_dense = torch.empty_like(q)
             o_sparse = torch.empty_like(q)
             p.permute_qkv(q, k, v, qp, kp, vt, ws, stream=stream)
-            pd.attention(qp, kp, vt, d_rp, d_col, scale, o_dense, lse, stream=stream,
-                         o_layout=vb.VEDA_LAYOUT_NATURAL)
+            pd.attention(qp, kp, vt, d_rp, d_col, scale, None, lse, stream=stream)   # the dense LSE only
             p.heat(qp, kp, lse, scale, heat, stream=stream)
             p.select(heat, rp, col, stream=stream)
             p.attention(qp, kp, vt, rp, col, scale, o_sparse, stream=stream, o_layout=vb.VEDA_LAYOUT_NATURAL)
-            p.output_error(o_sparse, o_dense, err[si, ci], stream=stream)
+            p.output_error(o_sparse, o_dense[si], err[si, ci], stream=stream)
     torch.cuda.synchronize()
     err_h = err.cpu().numpy()
     return err_h, vb.veda_tile_plan_vote(err_h, max_shapes)
