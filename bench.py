@@ -79,11 +79,18 @@ class Layer:
             self.m_pred = torch.empty(w.num_heads, dtype=torch.float64, device=dev)
             self.m_orc = torch.empty(w.num_heads, dtype=torch.float64, device=dev)
         self.attn_events = []
+        self.perm_events = []
 
     def step(self, s, time_attn=False):
         vb, p, w = self.vb, self.plan, self.w
         x = self.sets[s % len(self.sets)]
+        if time_attn:
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g0.record()
         p.permute_qkv(x["q"], x["k"], x["v"], self.qp, self.kp, self.vt, self.ws)
+        if time_attn:
+            g1.record()
+            self.perm_events.append((g0, g1))
         p.score_pooled(x["w_q"], x["w_k"], self.scores, self.ws)
         p.select(self.scores, self.row_ptr, self.col)
         if time_attn:
@@ -193,6 +200,7 @@ def main():
     attn_avg = float(np.mean(attn_ms))
     valid_flops = valid_only_flops(layer)
     cold = attention_cold(layer, 5)
+    perm = permute_rate(layer, w)
     attn_tflops = flops_attn / (attn_avg * 1e-3) / 1e12
     value = flops_attn / (ms_step * 1e-3) / 1e12
     traffic = None
@@ -219,6 +227,7 @@ def main():
                               "p90_ms": round(float(np.percentile(attn_ms, 90)), 4)},
         "attn_valid_only_tflops": round(valid_flops / (attn_avg * 1e-3) / 1e12, 2),
         "attn_cold_cache": cold,
+        "permute_qkv": perm,
     }
     if layer.dense is not None:
         mp, mo = layer.m_pred.cpu().numpy(), layer.m_orc.cpu().numpy()
@@ -253,6 +262,34 @@ def valid_only_flops(layer):
             total += nv[i] * float(nv[js].sum())
         t0 += n
     return 4.0 * w.head_dim * total
+
+
+def permute_rate(layer, w):
+    """The fused permutation + pooling of the timed steps (HIP events on the
+    launch stream) against its algorithmic HBM bytes: every valid natural row
+    of Q, K, V read once, every permuted row (padding included) written once,
+    and the pooled features written; next to it, the rate of a plain 1 GiB
+    device copy (1 GiB read + 1 GiB written) measured in the same run."""
+    p = layer.plan
+    ms = float(np.mean([a.elapsed_time(b) for a, b in layer.perm_events]))
+    d = w.head_dim
+    nbytes = (3 * w.num_tokens * w.num_heads * d * 2 + 3 * p.R * d * 2 + 2 * p.T * 3 * d * 4)
+    a = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_tbs = 2 * (1 << 30) / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
+    del a, b
+    tbs = nbytes / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "bytes": nbytes, "tb_per_s": round(tbs, 3),
+            "frac_of_hbm_peak": round(tbs * 1e3 / PEAK_HBM_GBS, 4), "copy_reference_tb_per_s": round(copy_tbs, 3),
+            "frac_of_copy_rate": round(tbs / copy_tbs, 4)}
 
 
 def attention_cold(layer, n):

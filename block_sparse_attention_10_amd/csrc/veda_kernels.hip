@@ -789,9 +789,11 @@ __device__ __forceinline__ void mask_group(f32x16& sg, int kt, int nj, int hl) {
 
 // p = exp2(s*c - m) for the lane's 16 keys of a group, packed to bf16 in key
 // order; with SUM, also returns the lane's fp32 sum of p.
+// (Partial sums start from the first pair rather than from 0: p >= 0, so
+// 0 + x == x and the order of the sum is unchanged, one add fewer per pair.)
 template <bool SUM>
 __device__ __forceinline__ float exp_group(const f32x16& sg, float c, float m, bf16x8 (&pg)[2]) {
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc[4];
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
     u32x4 pk;
@@ -800,7 +802,7 @@ __device__ __forceinline__ float exp_group(const f32x16& sg, float c, float m, b
       const float p0 = __builtin_amdgcn_exp2f(fmaf(sg[8 * s2 + 2 * e], c, -m));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(sg[8 * s2 + 2 * e + 1], c, -m));
       pk[e] = pack_bf16x2(p0, p1);
-      if (SUM) acc[e] += p0 + p1;
+      if (SUM) acc[e] = s2 == 0 ? p0 + p1 : acc[e] + (p0 + p1);
     }
     pg[s2] = __builtin_bit_cast(bf16x8, pk);
   }
@@ -811,14 +813,14 @@ __device__ __forceinline__ float exp_group(const f32x16& sg, float c, float m, b
 // same order as exp_group<true> (so both give bitwise the same sum), without
 // packing p.
 __device__ __forceinline__ float exp_sum(const f32x16& sg, float c, float m) {
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc[4];
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float p0 = __builtin_amdgcn_exp2f(fmaf(sg[8 * s2 + 2 * e], c, -m));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(sg[8 * s2 + 2 * e + 1], c, -m));
-      acc[e] += p0 + p1;
+      acc[e] = s2 == 0 ? p0 + p1 : acc[e] + (p0 + p1);
     }
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
