@@ -201,6 +201,7 @@ def main():
     valid_flops = valid_only_flops(layer)
     cold = attention_cold(layer, 5)
     perm = permute_rate(layer, w)
+    gemm = gemm_reference()
     attn_tflops = flops_attn / (attn_avg * 1e-3) / 1e12
     value = flops_attn / (ms_step * 1e-3) / 1e12
     traffic = None
@@ -228,6 +229,7 @@ def main():
         "attn_valid_only_tflops": round(valid_flops / (attn_avg * 1e-3) / 1e12, 2),
         "attn_cold_cache": cold,
         "permute_qkv": perm,
+        "bf16_gemm_reference": dict(gemm, attn_kernel_over_gemm=round(attn_tflops / gemm["tflops"], 4)),
     }
     if layer.dense is not None:
         mp, mo = layer.m_pred.cpu().numpy(), layer.m_orc.cpu().numpy()
@@ -290,6 +292,29 @@ def permute_rate(layer, w):
     return {"ms": round(ms, 4), "bytes": nbytes, "tb_per_s": round(tbs, 3),
             "frac_of_hbm_peak": round(tbs * 1e3 / PEAK_HBM_GBS, 4), "copy_reference_tb_per_s": round(copy_tbs, 3),
             "frac_of_copy_rate": round(tbs / copy_tbs, 4)}
+
+
+def gemm_reference(n=8192, reps=20):
+    """Rate of the vendor bf16 GEMM (torch.matmul of two contiguous n x n
+    matrices of N(0,1) values) in the same run: what the matrix cores sustain
+    on random operands on this machine, next to the nominal 2.5 PFLOP/s."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(5):
+        torch.matmul(a, b, out=c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    return {"shape": "%dx%dx%d" % (n, n, n), "ms": round(ms, 4), "tflops": round(tf, 1),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
 def attention_cold(layer, n):
