@@ -4,9 +4,9 @@ One step = one attention layer through the whole hot path on one batch of
 resident synthetic input: permute Q, K (rows) and V (tile-transposed) with the
 tile pooling fused in, project and score tile pairs, select blocks, and run
 block-sparse attention whose epilogue writes O back in natural token order
-(plus, for the packed workload, the all-blocks forward for the dense LSE, the
-block heat, the oracle mask selected on the heat and the attention mass of
-the predicted and the oracle mask).  Four seeded input
+(plus, for the packed workload, the dense LSE and the block heat in one pass
+over all blocks, the oracle mask selected on the heat and the attention mass
+of the predicted and the oracle mask).  Four seeded input
 sets rotate across steps, so each call sees a new block pattern.
 
 Prints one JSON line.  value = attention FLOP over computed blocks / layer
@@ -73,6 +73,8 @@ class Layer:
             self.d_col = torch.empty(self.dense.info["nnz"], dtype=torch.int32, device=dev)
             self.d_lse = torch.empty(p.R, dtype=torch.float32, device=dev)
             self.heat = torch.empty(p.info["total_pairs"], dtype=torch.float32, device=dev)
+            self.heat_ws = torch.empty(self.dense.info["heat_workspace_bytes"] // 4, dtype=torch.float32,
+                                       device=dev)
             # oracle mask (selection on the heat) and the attention mass of both masks
             self.o_row_ptr = torch.empty(p.T + 1, dtype=torch.int32, device=dev)
             self.o_col = torch.empty(p.info["nnz"], dtype=torch.int32, device=dev)
@@ -104,9 +106,9 @@ class Layer:
         if self.dense is not None:
             d = self.dense
             d.select(self.scores, self.d_row_ptr, self.d_col)
-            d.attention(self.qp, self.kp, self.vt, self.d_row_ptr, self.d_col, w.softmax_scale, None,
-                        self.d_lse)   # the dense LSE only
-            p.heat(self.qp, self.kp, self.d_lse, w.softmax_scale, self.heat)
+            # the dense LSE and the block heat in one pass over all blocks
+            d.lse_heat(self.qp, self.kp, self.d_row_ptr, self.d_col, w.softmax_scale, self.d_lse, self.heat,
+                       self.heat_ws)
             p.select(self.heat, self.o_row_ptr, self.o_col)
             p.mask_mass(self.heat, self.row_ptr, self.col, self.m_pred)
             p.mask_mass(self.heat, self.o_row_ptr, self.o_col, self.m_orc)

@@ -62,7 +62,8 @@ class PlanInfo(ctypes.Structure):
                 ("nnz", ctypes.c_int64), ("max_row_blocks", ctypes.c_int64),
                 ("device_table_bytes", ctypes.c_int64), ("score_workspace_bytes", ctypes.c_int64),
                 ("transpose_workspace_bytes", ctypes.c_int64), ("bwd_workspace_bytes", ctypes.c_int64),
-                ("max_tiles_per_head", ctypes.c_int32), ("uploaded", ctypes.c_int32)]
+                ("max_tiles_per_head", ctypes.c_int32), ("uploaded", ctypes.c_int32),
+                ("heat_workspace_bytes", ctypes.c_int64)]
 
 
 # name -> (restype, argtypes)
@@ -90,6 +91,7 @@ _SIGS = {
     "veda_select_blocks": (_I32, [_P, _P, _P, _P, _P, _P]),
     "veda_block_sparse_attn_fwd": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _P, _P, _P]),
     "veda_block_heat": (_I32, [_P, _P, _P, _P, ctypes.c_float, _P, _P]),
+    "veda_dense_lse_heat": (_I32, [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
     "veda_mask_mass": (_I32, [_P, _P, _P, _P, _P, _P]),
     "veda_output_error": (_I32, [_P, _P, _P, _P, _P]),
     "veda_mask_transpose": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -259,6 +261,12 @@ def veda_block_sparse_attn_fwd(plan: int, q, k, v_t, row_ptr, col_idx, softmax_s
 def veda_block_heat(plan: int, q, k, lse, softmax_scale: float, heat, stream=None) -> None:
     _check(lib().veda_block_heat(plan, _ptr(q), _ptr(k), _ptr(lse), float(softmax_scale), _ptr(heat),
                                  _stream(stream)))
+
+
+def veda_dense_lse_heat(plan: int, q, k, row_ptr, col_idx, softmax_scale: float, lse, heat, workspace,
+                        stream=None) -> None:
+    _check(lib().veda_dense_lse_heat(plan, _ptr(q), _ptr(k), _ptr(row_ptr), _ptr(col_idx), float(softmax_scale),
+                                     _ptr(lse), _ptr(heat), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def veda_mask_mass(plan: int, heat, row_ptr, col_idx, mass, stream=None) -> None:
@@ -457,6 +465,18 @@ class Plan:
         self._expect(lse, (self.R,), torch.float32, "lse")
         self._expect(heat, (self.info["total_pairs"],), torch.float32, "heat")
         veda_block_heat(self.handle, q, k, lse, scale, heat, stream)
+
+    def lse_heat(self, q, k, row_ptr, col_idx, scale, lse, heat, workspace, stream=None):
+        import torch
+        self._expect(q, (self.R, self.D), torch.bfloat16, "q")
+        self._expect(k, (self.R, self.D), torch.bfloat16, "k")
+        self._expect(row_ptr, (self.T + 1,), torch.int32, "row_ptr")
+        self._expect(col_idx, (self.info["nnz"],), torch.int32, "col_idx")
+        if lse is not None:
+            self._expect(lse, (self.R,), torch.float32, "lse")
+        self._expect(heat, (self.info["total_pairs"],), torch.float32, "heat")
+        self._check_ws(workspace, "heat_workspace_bytes")
+        veda_dense_lse_heat(self.handle, q, k, row_ptr, col_idx, scale, lse, heat, workspace, stream)
 
     def transpose(self, row_ptr, col_idx, col_ptr, row_idx, workspace, stream=None):
         import torch

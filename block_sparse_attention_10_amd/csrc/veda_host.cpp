@@ -502,6 +502,7 @@ veda_status veda_plan_create(const veda_plan_desc* d, veda_plan** out) {
   in.score_workspace_bytes = score_workspace_bytes(tiles, d->head_dim);
   in.transpose_workspace_bytes = transpose_workspace_bytes(in.total_pairs, in.total_tiles);
   in.bwd_workspace_bytes = bwd_workspace_bytes(in.total_rows, in.total_tiles);
+  in.heat_workspace_bytes = heat_workspace_bytes(in.nnz);
   build_attn_order(*p);
   build_staging(*p);
   in.device_table_bytes = (int64_t)p->staging.size();
@@ -698,6 +699,28 @@ veda_status veda_block_heat(const veda_plan* p, const void* q, const void* k, co
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
     return fail(VEDA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   return launched(launch_heat(p->dev, q, k, lse, softmax_scale, heat, (hipStream_t)stream), "block heat");
+}
+
+veda_status veda_dense_lse_heat(const veda_plan* p, const void* q, const void* k, const int32_t* row_ptr,
+                                const int32_t* col_idx, float softmax_scale, float* lse, float* heat,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  veda_status st = check_plan_ready(p);
+  if (st) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(row_ptr, "row_ptr")) ||
+      (st = check_ptr(col_idx, "col_idx")) || (st = check_ptr(heat, "heat")) ||
+      (st = check_ptr(workspace, "workspace")))
+    return st;
+  if (lse && (st = check_ptr(lse, "lse"))) return st;
+  if (p->budget_mode != VEDA_BUDGET_ALL)
+    return fail(VEDA_ERR_UNSUPPORTED, "the fused dense LSE and heat needs a plan with budget mode ALL");
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return fail(VEDA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if ((int64_t)workspace_bytes < p->info.heat_workspace_bytes)
+    return fail(VEDA_ERR_WORKSPACE, "workspace of %zu bytes, %lld needed", workspace_bytes,
+                (long long)p->info.heat_workspace_bytes);
+  return launched(launch_lse_heat(p->dev, q, k, row_ptr, col_idx, softmax_scale, lse, static_cast<float*>(workspace),
+                                  heat, (hipStream_t)stream),
+                  "dense LSE and heat");
 }
 
 veda_status veda_mask_mass(const veda_plan* p, const float* heat, const int32_t* row_ptr, const int32_t* col_idx,

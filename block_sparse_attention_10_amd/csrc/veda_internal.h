@@ -26,6 +26,8 @@ inline int64_t transpose_workspace_bytes(int64_t total_pairs, int64_t total_tile
 inline int64_t bwd_workspace_bytes(int64_t total_rows, int64_t total_tiles) {
   return align256(total_rows * 8) + align256(total_tiles * 4);
 }
+// One fp32 per (block, query slot): each block's sum of p per query.
+inline int64_t heat_workspace_bytes(int64_t nnz) { return align256(nnz * 128 * 4); }
 
 // Device view of the tables of one distinct tile shape.  Heads that share a
 // shape share these tables (tiling, valid counts, budgets, local CSR offsets).
@@ -73,6 +75,9 @@ hipError_t launch_select(const DevPlan& p, const float* scores, int32_t* row_ptr
 hipError_t launch_attn_fwd(const DevPlan& p, const void* q, const void* k, const void* vt,
                            const int32_t* row_ptr, const int32_t* col_idx, float scale,
                            void* o, int o_natural, float* lse, uint32_t* visited, hipStream_t s);
+hipError_t launch_lse_heat(const DevPlan& p, const void* q, const void* k, const int32_t* row_ptr,
+                           const int32_t* col_idx, float scale, float* lse, float* bsum, float* heat,
+                           hipStream_t s);
 hipError_t launch_heat(const DevPlan& p, const void* q, const void* k, const float* lse,
                        float scale, float* heat, hipStream_t s);
 hipError_t launch_mask_mass(const DevPlan& p, const float* heat, const int32_t* row_ptr, const int32_t* col_idx,

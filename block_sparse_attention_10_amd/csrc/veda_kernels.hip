@@ -895,14 +895,15 @@ __device__ __forceinline__ int half_pads(int nv, int hh) {
 // every wave has done QK of group 1, K rows of groups 2-3 and V^T keys 0-63
 // once every wave has done QK of group 3 and PV of group 1, V^T keys 64-127
 // after the block.  Two workgroups share a CU (72 KB of LDS each).
-template <int D, bool PV>
-__global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const uint16_t* __restrict__ q,
-                                                              const uint16_t* __restrict__ k,
-                                                              const uint16_t* __restrict__ vt,
-                                                              const int32_t* __restrict__ row_ptr,
-                                                              const int32_t* __restrict__ col_idx, float scale_log2,
-                                                              uint16_t* __restrict__ o, int o_natural,
-                                                              float* __restrict__ lse, uint32_t* __restrict__ visited) {
+template <int D, bool PV, bool HB>
+__device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* __restrict__ q,
+                                              const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
+                                              const int32_t* __restrict__ row_ptr,
+                                              const int32_t* __restrict__ col_idx, float scale_log2,
+                                              uint16_t* __restrict__ o, int o_natural, float* __restrict__ lse,
+                                              uint32_t* __restrict__ visited, float* __restrict__ bsum,
+                                              float* __restrict__ heat) {
+  static_assert(!(PV && HB), "the block heat is fused into the LSE-only pass");
   constexpr int H = D / 32;   // copy instructions per thread and half tile (K or V^T)
   constexpr int kRowList = 2048;
   // K and V^T halves as four separate arrays: the compiler then knows that
@@ -914,6 +915,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
   __shared__ __attribute__((aligned(16))) uint16_t vh1[64 * D];
   __shared__ int32_t rowlist[kRowList];
   __shared__ int32_t redo;
+  __shared__ float s_inv[HB ? kTile : 1];   // heat: per query, the factor of its block sums
+  __shared__ float s_pe[HB ? kTile : 1];    // heat: per query, one padding key's share of its row
   const int t = uni(p.attn_order[blockIdx.x]);
   if (t < 0) return;
   const int h = uni(p.row_head[t]);
@@ -942,6 +945,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
   f32x16 oacc[D / 32];
   float m_run, l_run;   // reference point (log2 units) and the lane's sum of p
   int npad;             // fast pass: padding keys over the row's blocks
+  float bs = 0.0f;      // heat: the lane's sum of p over the current block
+  float pend_b = 0.0f;  // heat: a finished block's sum per query, stored one block later
+  int pend_pos = -1;    // heat: its position in the CSR (-1: none pending)
 
   // The row's key tiles, staged in LDS as (tile << 14 | pads1 << 7 | pads0)
   // (padsX = half_pads of the tile's valid count) so the loop issues no
@@ -978,7 +984,19 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
   // together with that step's softmax work (and register lifetimes short).
   // It also issues the asynchronous copies of the next block; `compute` =
   // false runs only those (the pass's first iteration).
-  auto block = [&](bool compute, bool first, int ent, bool more, int jn) {
+  // With HB each finished block's sum of p per query (both lane halves) goes
+  // to bsum[position][query]; the store waits until the next block's first
+  // copy wait, where no copy is in flight, so the copy waits (which count
+  // stores too) keep their meaning.
+  auto flush_block_sum = [&]() {
+    if constexpr (HB) {
+      if (pend_pos >= 0) {
+        if (hl == 0) bsum[(int64_t)pend_pos * kTile + 32 * w + ln] = pend_b;
+        pend_pos = -1;
+      }
+    }
+  };
+  auto block = [&](bool compute, bool first, int ent, bool more, int jn, int bpos) {
     const f32x16 zero16 = {};
     f32x16 s0, s1, s2, s3;
     bf16x8 p0[2], p1[2], p2[2], p3[2];
@@ -992,14 +1010,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
         l_run += exp_group<true>(s0, c, m_run, p0);
         pin(p0);
       } else {
-        l_run += exp_sum(s0, c, m_run);
+        const float g = exp_sum(s0, c, m_run);
+        l_run += g;
         pin_sum(l_run);
+        if constexpr (HB) {
+          bs = g;
+          pin_sum(bs);
+        }
       }
       interleave_step<8, 6>();
     }
     // V^T(b) keys 0-63 have landed (without PV: K rows 64-127 have); K rows
     // 0-63 are free
     dma_sync<PV ? H : 0>();
+    flush_block_sum();
     if (more) dma_k_half<D>(kh0, rk, jn * kTile * D * 2, koff, wave, 0);
     __builtin_amdgcn_sched_barrier(0);
     if (compute) {
@@ -1009,8 +1033,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
         l_run += exp_group<true>(s1, c, m_run, p1);
         pin(p1);
       } else {
-        l_run += exp_sum(s1, c, m_run);
+        const float g = exp_sum(s1, c, m_run);
+        l_run += g;
         pin_sum(l_run);
+        if constexpr (HB) {
+          bs += g;
+          pin_sum(bs);
+        }
       }
       interleave_step<PV ? 16 : 8, 3>();
       __builtin_amdgcn_sched_barrier(0);
@@ -1020,12 +1049,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
         l_run += exp_group<true>(s2, c, m_run, p2);
         pin(p2);
       } else {
-        l_run += exp_sum(s2, c, m_run);
+        const float g = exp_sum(s2, c, m_run);
+        l_run += g;
         pin_sum(l_run);
+        if constexpr (HB) {
+          bs += g;
+          pin_sum(bs);
+        }
       }
       interleave_step<PV ? 16 : 8, 3>();
     }
-    if (more) dma_sync<H>(); else dma_sync<0>();   // V^T(b) keys 64-127 have landed; K, V^T keys 0-63 free
+    // V^T(b) keys 64-127 have landed; K, V^T keys 0-63 free.  (Without PV
+    // nothing needs to have landed here; with HB the block-sum store issued
+    // before the K copies is allowed to stay in flight too.)
+    if (more) dma_sync<HB ? H + 1 : H>(); else dma_sync<0>();
     if (more) {
       dma_k_half<D>(kh1, rk, jn * kTile * D * 2, koff, wave, 1);
       if constexpr (PV) dma_vt_half<D>(vh0, rv, jn * kTile * D * 2, voff, wave, 0);
@@ -1037,8 +1074,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
         l_run += exp_group<true>(s3, c, m_run, p3);
         pin(p3);
       } else {
-        l_run += exp_sum(s3, c, m_run);
+        const float g = exp_sum(s3, c, m_run);
+        l_run += g;
         pin_sum(l_run);
+        if constexpr (HB) {
+          bs += g;
+          pin_sum(bs);
+        }
       }
       interleave_step<PV ? 8 : 0, 6>();
       __builtin_amdgcn_sched_barrier(0);
@@ -1047,6 +1089,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
         interleave_step<8, 0>();
       }
       npad += ((ent >> 7) & 127) + (ent & 127);
+      if constexpr (HB) {
+        pend_b = bs + __shfl_xor(bs, 32, 64);
+        pend_pos = bpos;
+      }
     }
   };
 
@@ -1072,7 +1118,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
     for (int b = beg - 1; b < end; ++b) {
       const bool more = b + 1 < end;
       const int jn = en >> 14;
-      block(b >= beg, b == beg, ent, more, jn);
+      block(b >= beg, b == beg, ent, more, jn, b);
       if (more) {
         dma_sync<H>();                // K(b+1) has landed (without PV: its rows 0-63); every wave is done with V^T(b)
         if constexpr (PV) dma_vt_half<D>(vh1, rv, jn * kTile * D * 2, voff, wave, 1);
@@ -1088,6 +1134,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
         en = uni(rowlist[slot]);
       }
     }
+    flush_block_sum();
   };
 
   // Safe pass: per block a plain synchronous tile copy, then the four groups
@@ -1143,6 +1190,62 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
     l_all = l_run + __shfl_xor(l_run, 32, 64);
   }
 
+  // Block heat of this query tile (HB): heat(i, j) is the mean over the
+  // tile's valid queries of the probability mass on key tile j's valid keys.
+  // After the fast pass, bsum holds per (block, query) the sum of
+  // exp2(s*c - m) over the block's 128 key slots, so the mass is
+  // (bsum - pads(j) * exp2(-m)) / l with the row's final l.  After the safe
+  // pass those sums are not on one reference point, so every block is walked
+  // again with the final LSE and its exact masked mass stored instead.
+  if constexpr (HB) {
+    const bool exact = uni(redo) != 0;
+    if (exact) {
+      const float lse2 = m_run + __log2f(l_all);
+      for (int b = beg; b < end; ++b) {
+        const int j = min(max(col_idx[b], 0), nt - 1);
+        const int nj = sh.valid[j];
+        lds_sync();                     // every wave is done with the previous tile
+        copy_kv_halves<D, false>(kh0, kh1, vh0, vh1, k + (hrow + (int64_t)kTile * j) * D, vt);
+        lds_sync();
+        float acc = 0.0f;
+#pragma unroll 1
+        for (int kt = 0; kt < 4; ++kt) {
+          const f32x16 zero16 = {};
+          const f32x16 sg = qk_group<D>(kt < 2 ? kh0 : kh1, qf, kt, zero16);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(sg[r], c, -lse2));
+            acc += sacc_key(kt, r, hl) < nj ? e : 0.0f;
+          }
+        }
+        const float bq = acc + __shfl_xor(acc, 32, 64);
+        if (hl == 0) bsum[(int64_t)b * kTile + 32 * w + ln] = bq;
+      }
+    }
+    if (hl == 0) {
+      s_inv[32 * w + ln] = qvalid ? (exact ? 1.0f : 1.0f / l_all) : 0.0f;
+      s_pe[32 * w + ln] = (qvalid && !exact) ? __builtin_amdgcn_exp2f(-m_run) / l_all : 0.0f;
+    }
+    __syncthreads();                    // every wave's block sums and factors are visible
+    float pe = 0.0f;                    // one padding key's mass, summed over the queries
+#pragma unroll 4
+    for (int qq = 0; qq < kTile; ++qq) pe += s_pe[qq];
+    const float inv_nq = 1.0f / (float)sh.valid[i];
+    float* hrow_out = heat + p.head_pair_off[h] + (int64_t)i * nt;
+    for (int e = threadIdx.x; e < end - beg; e += kThreads) {
+      const int j = min(max(col_idx[beg + e], 0), nt - 1);
+      const float* bp = bsum + (int64_t)(beg + e) * kTile;
+      float acc = 0.0f;
+#pragma unroll 2
+      for (int q4 = 0; q4 < kTile; q4 += 4) {
+        const u32x4 bv = ld16(bp + q4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = fmaf(__uint_as_float(bv[u]), s_inv[q4 + u], acc);
+      }
+      hrow_out[j] = fmaf(-(float)(kTile - sh.valid[j]), pe, acc) * inv_nq;
+    }
+  }
+
   // epilogue: normalise, store (without PV only the LSE)
   if constexpr (PV) {
     const float inv = 1.0f / l_all;
@@ -1172,6 +1275,31 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
   }
   if (lse && hl == 0) lse[row0 + 32 * w + ln] = m_run * 0.69314718055994531f + logf(l_all);
   if (visited && threadIdx.x == 0) atomicAdd(visited, (uint32_t)(end - beg));
+}
+
+template <int D, bool PV>
+__global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ k,
+                                                              const uint16_t* __restrict__ vt,
+                                                              const int32_t* __restrict__ row_ptr,
+                                                              const int32_t* __restrict__ col_idx, float scale_log2,
+                                                              uint16_t* __restrict__ o, int o_natural,
+                                                              float* __restrict__ lse, uint32_t* __restrict__ visited) {
+  attn_fwd_body<D, PV, false>(p, q, k, vt, row_ptr, col_idx, scale_log2, o, o_natural, lse, visited, nullptr,
+                              nullptr);
+}
+
+// The dense LSE and the block heat in one pass over an all-blocks mask: the
+// LSE-only attention (no PV, no V^T) that also keeps every block's sum of p
+// per query in bsum and reduces them into the heat at the end of each row.
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2) lse_heat_kernel(DevPlan p, const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ k,
+                                                              const int32_t* __restrict__ row_ptr,
+                                                              const int32_t* __restrict__ col_idx, float scale_log2,
+                                                              float* __restrict__ lse, float* __restrict__ bsum,
+                                                              float* __restrict__ heat) {
+  attn_fwd_body<D, false, true>(p, q, k, k, row_ptr, col_idx, scale_log2, nullptr, 0, lse, nullptr, bsum, heat);
 }
 
 // ---------------------------------------------------------------------------
@@ -2079,6 +2207,21 @@ hipError_t launch_attn_fwd(const DevPlan& p, const void* q, const void* k, const
       hipLaunchKernelGGL((attn_fwd_kernel<64, false>), grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
                          scale_log2, oo, o_natural, lse, visited);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_heat(const DevPlan& p, const void* q, const void* k, const int32_t* row_ptr,
+                           const int32_t* col_idx, float scale, float* lse, float* bsum, float* heat, hipStream_t s) {
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const dim3 grid((unsigned)p.attn_grid);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL(lse_heat_kernel<128>, grid, dim3(kThreads), 0, s, p, qq, kk, row_ptr, col_idx, scale_log2, lse,
+                       bsum, heat);
+  else
+    hipLaunchKernelGGL(lse_heat_kernel<64>, grid, dim3(kThreads), 0, s, p, qq, kk, row_ptr, col_idx, scale_log2, lse,
+                       bsum, heat);
   return hipGetLastError();
 }
 

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define VEDA_ABI_VERSION 4
+#define VEDA_ABI_VERSION 5
 
 typedef int32_t veda_status;
 enum {
@@ -124,6 +124,7 @@ typedef struct veda_plan_info {
   int64_t bwd_workspace_bytes; /* bytes veda_block_sparse_attn_bwd needs       */
   int32_t max_tiles_per_head;
   int32_t uploaded;           /* 1 after a successful veda_plan_upload        */
+  int64_t heat_workspace_bytes; /* bytes veda_dense_lse_heat needs (nnz*512)   */
 } veda_plan_info;
 
 /* ABI version of the loaded library (VEDA_ABI_VERSION it was built with). */
@@ -271,6 +272,32 @@ veda_status veda_block_sparse_attn_fwd(const veda_plan* plan, const void* q, con
  * A head may have at most 4096 tiles. */
 veda_status veda_block_heat(const veda_plan* plan, const void* q, const void* k,
                             const float* lse, float softmax_scale, float* heat, void* stream);
+
+/* The dense LSE and the teacher block heat in one pass (Key Features > "Veda
+ * sparse attention": teacher block heat from the dense LSE, fused kernel).
+ * The plan must have budget mode VEDA_BUDGET_ALL (else
+ * VEDA_ERR_UNSUPPORTED) and row_ptr/col_idx its all-blocks CSR (from
+ * veda_select_blocks).  Computes the same LSE as veda_block_sparse_attn_fwd
+ * with o = NULL (bitwise equal) and the heat of veda_block_heat from that
+ * LSE: heat[i][j] = (1/valid(i)) * sum over valid query slots r of tile i
+ * and valid key slots c of tile j of exp(scale * q_r . k_c - lse[r]).  The
+ * heat is formed from each block's sum of exp(scale * q_r . k_c - m_r)
+ * against a fixed per-row reference m_r, divided by the row's final sum at
+ * the end of the row, so the key tiles are walked once instead of twice
+ * (rows that need the exact fallback pass are walked again with the final
+ * LSE).  The padding rows of k must hold zeros.
+ *   q, k:      device permuted bf16 [R, D]
+ *   lse:       device fp32 [R] natural log, or NULL (not stored)
+ *   heat:      device fp32 [sum_h n_h^2], layout of the scores; every pair
+ *              is written
+ *   workspace: device scratch of at least heat_workspace_bytes (the plan's
+ *              nnz x 128 x 4 bytes: one fp32 per block and query slot),
+ *              16-byte aligned; its contents on entry do not matter.
+ * Errors: VEDA_ERR_WORKSPACE if workspace_bytes is too small. */
+veda_status veda_dense_lse_heat(const veda_plan* plan, const void* q, const void* k,
+                                const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
+                                float* lse, float* heat, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* Attention mass a block mask keeps ("Deploying this checkpoint", section 4:
  * recall of a predicted mask against the oracle mask; section 6: the share

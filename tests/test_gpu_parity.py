@@ -538,6 +538,121 @@ def test_heat_config5_sampled_heads():
         assert np.max(np.abs(hg[h].sum(axis=1) - 1.0)) <= 1e-3
 
 
+def _late_logits(w, inp):
+    """Scale the keys of every head's last key tile by 64: logits there lie far
+    above the first key group's maximum, which forces the exact fallback pass."""
+    op = vo.Plan.from_workload(w)
+    k = inp["k"].float()
+    for h in range(w.num_heads):
+        perm = op.heads[h].perm()
+        last = perm[(op.heads[h].num_tiles - 1) * 128:]
+        k[torch.from_numpy(last[last >= 0].astype(np.int64)), h, :] *= 64.0
+    inp["k"] = k.to(torch.bfloat16)
+
+
+def _far_below_zero(inp, seed):
+    """Every logit about -400 * scale while key tiles have padding slots: the
+    padding mass the fast pass removes dwarfs the valid sum (fallback pass)."""
+    gen = torch.Generator().manual_seed(seed)
+    q = 0.1 * torch.randn(inp["q"].shape, generator=gen)
+    k = 0.1 * torch.randn(inp["k"].shape, generator=gen)
+    q[..., 0] += 20.0
+    k[..., 0] -= 20.0
+    inp["q"], inp["k"] = q.to(torch.bfloat16), k.to(torch.bfloat16)
+
+
+def _dense_lse_heat(g, w):
+    plan = g["plan"]
+    lse = torch.full_like(g["lse"], float("nan"))
+    heat = torch.full((plan.info["total_pairs"],), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((plan.info["heat_workspace_bytes"] // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    plan.lse_heat(g["q_perm"], g["k_perm"], g["row_ptr"], g["col_idx"], w.softmax_scale, lse, heat, ws)
+    torch.cuda.synchronize()
+    return lse, heat
+
+
+@pytest.mark.parametrize("kind", ["small", "guard_all_blocks", "guard_late_logits", "guard_far_below_zero"])
+def test_dense_lse_heat(kind):
+    """veda_dense_lse_heat (dense LSE and block heat in one pass): the LSE is
+    bitwise equal to the attention's over the same all-blocks CSR; the heat
+    matches the oracle's heat from its own dense LSE and veda_block_heat on
+    the same LSE (HEAT_ABS), on the fast pass and on the fallback pass (late
+    logits; logits far below zero with partial key tiles)."""
+    ws = small_workloads() if kind == "small" else [_guard_workload()]
+    for w in ws:
+        inp = wl.make_inputs(w, seed=w.index)
+        if kind == "guard_late_logits":
+            _late_logits(w, inp)
+        elif kind == "guard_far_below_zero":
+            _far_below_zero(inp, 9)
+        g = gp.gpu_path(w, inp, budget_mode=wl.ALL_BLOCKS, dense_mask=False)
+        plan = g["plan"]
+        lse, heat = _dense_lse_heat(g, w)
+        a, b = g["lse"].cpu().numpy(), lse.cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), w.name
+        heat2 = torch.empty_like(heat)
+        plan.heat(g["q_perm"], g["k_perm"], g["lse"], w.softmax_scale, heat2)
+        torch.cuda.synchronize()
+        op = vo.Plan.from_workload(w)
+        qp, kp, _ = gp.oracle_front(op, inp)
+        _, L = vo.block_sparse_attention(op, qp, kp, kp, vo.all_blocks_selection(op), w.softmax_scale)
+        ref = vo.block_heat(op, qp, kp, L, w.softmax_scale)
+        hg = gp.split_scores(None, op, heat.cpu().numpy())
+        h2 = gp.split_scores(None, op, heat2.cpu().numpy())
+        for h in range(w.num_heads):
+            err = float(np.max(np.abs(hg[h] - ref[h])))
+            print("%s %s head %d: heat max_abs %.3e (two-pass %.3e)" % (kind, w.name, h, err,
+                  float(np.max(np.abs(h2[h] - ref[h])))), flush=True)
+            assert err <= gp.HEAT_ABS, (w.name, h)
+            assert np.max(np.abs(hg[h] - h2[h])) <= gp.HEAT_ABS, (w.name, h)
+
+
+def test_dense_lse_heat_config5_sampled_heads():
+    """The fused dense LSE and heat at full size (packed sequence, the bench's
+    heat step): LSE bitwise equal to the all-blocks attention's, heat against
+    the oracle on two heads, every heat row summing to 1."""
+    w = wl.workload(5)
+    inp = wl.make_inputs(w)
+    g = gp.gpu_path(w, inp, budget_mode=wl.ALL_BLOCKS, dense_mask=False)
+    lse, heat = _dense_lse_heat(g, w)
+    a, b = g["lse"].cpu().numpy(), lse.cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    op = vo.Plan.from_workload(w)
+    qp = vo.permute_forward(op, gp.f64(inp["q"]))
+    kp = vo.permute_forward(op, gp.f64(inp["k"]))
+    hg = gp.split_scores(None, op, heat.cpu().numpy())
+    for h in (0, 13):
+        rows = [(h, i) for i in range(op.heads[h].num_tiles)]
+        _, L = vo.block_sparse_attention(op, qp, kp, kp, vo.all_blocks_selection(op), w.softmax_scale, rows=rows)
+        ref = vo.block_heat(op, qp, kp, L, w.softmax_scale, heads=[h])[h]
+        err = float(np.max(np.abs(hg[h] - ref)))
+        print("fused heat head %d max_abs %.3e" % (h, err), flush=True)
+        assert err <= gp.HEAT_ABS
+    for h in range(w.num_heads):
+        assert np.max(np.abs(hg[h].sum(axis=1) - 1.0)) <= 1e-3
+
+
+def test_dense_lse_heat_errors():
+    """The fused call refuses a plan that is not all-blocks (UNSUPPORTED) and a
+    short workspace (WORKSPACE) on the host, before any launch."""
+    w = _guard_workload()
+    inp = wl.make_inputs(w, seed=w.index)
+    g = gp.gpu_path(w, inp, budget_mode=wl.ALL_BLOCKS, dense_mask=False)
+    plan = g["plan"]
+    heat = torch.empty(plan.info["total_pairs"], dtype=torch.float32, device="cuda")
+    short = torch.empty(plan.info["heat_workspace_bytes"] // 4 - 64, dtype=torch.float32, device="cuda")
+    with pytest.raises(vb.VedaError) as e:
+        vb.veda_dense_lse_heat(plan.handle, g["q_perm"], g["k_perm"], g["row_ptr"], g["col_idx"], w.softmax_scale,
+                               g["lse"], heat, short)
+    assert e.value.status == 4          # VEDA_ERR_WORKSPACE
+    sparse = vb.Plan.from_workload(w, budget_mode=wl.KEEP_RATIO)
+    ws = torch.empty(plan.info["heat_workspace_bytes"] // 4, dtype=torch.float32, device="cuda")
+    with pytest.raises(vb.VedaError) as e:
+        vb.veda_dense_lse_heat(sparse.handle, g["q_perm"], g["k_perm"], g["row_ptr"], g["col_idx"],
+                               w.softmax_scale, g["lse"], heat, ws)
+    assert e.value.status == 3          # VEDA_ERR_UNSUPPORTED
+
+
 def test_config4_long_clip_sampled():
     """Full-size config 4 (two tile shapes): permutation bit-exact on all
     heads, scores and CSR bit-exact on sampled heads, attention on sampled
