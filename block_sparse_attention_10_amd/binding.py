@@ -393,11 +393,15 @@ class Plan:
         import torch
         bf = torch.bfloat16
         nat = (self.N, self.H, self.D)
-        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        for t, n in ((q, "q"), (k, "k")):
             self._expect(t, nat, bf, n)
         self._expect(q_perm, (self.R, self.D), bf, "q_perm")
         self._expect(k_perm, (self.R, self.D), bf, "k_perm")
-        self._expect(v_t, (self.T, self.D, 128), bf, "v_t")
+        if (v is None) != (v_t is None):
+            raise ValueError("permute_qkv: give both v and v_t, or neither")
+        if v is not None:
+            self._expect(v, nat, bf, "v")
+            self._expect(v_t, (self.T, self.D, 128), bf, "v_t")
         if workspace is not None:
             self._check_workspace(workspace)
         veda_permute_qkv(self.handle, q, k, v, q_perm, k_perm, v_t, workspace, stream)

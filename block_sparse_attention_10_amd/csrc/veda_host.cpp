@@ -620,13 +620,16 @@ veda_status veda_permute_qkv(const veda_plan* p, const void* q, const void* k, c
                              void* k_perm, void* v_t, void* workspace, size_t workspace_bytes, void* stream) {
   veda_status st = check_plan_ready(p);
   if (st) return st;
-  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
-      (st = check_ptr(q_perm, "q_perm")) || (st = check_ptr(k_perm, "k_perm")) || (st = check_ptr(v_t, "v_t")))
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(q_perm, "q_perm")) ||
+      (st = check_ptr(k_perm, "k_perm")))
     return st;
+  if ((v == nullptr) != (v_t == nullptr)) return fail(VEDA_ERR_INVALID_ARG, "v and v_t must both be given or both NULL");
+  if (v && ((st = check_ptr(v, "v")) || (st = check_ptr(v_t, "v_t")))) return st;
+  const int nt = v ? 3 : 2;   // without V: Q and K only
   const void* ins[3] = {q, k, v};
   void* outs[3] = {q_perm, k_perm, v_t};
-  for (int a = 0; a < 3; ++a)
-    for (int b = 0; b < 3; ++b)
+  for (int a = 0; a < nt; ++a)
+    for (int b = 0; b < nt; ++b)
       if (ins[a] == outs[b]) return fail(VEDA_ERR_INVALID_ARG, "an input aliases an output");
   if (workspace) {
     if ((st = check_ptr(workspace, "workspace"))) return st;

@@ -85,42 +85,6 @@ __global__ void __launch_bounds__(kThreads) permute_rows_kernel(DevPlan p, const
   }
 }
 
-// Forward permutation into the tile-transposed layout [T][D][128]: one
-// workgroup per tile gathers 128 rows into LDS and writes D rows of 128 slots.
-template <int D>
-__global__ void __launch_bounds__(kThreads) permute_vt_kernel(DevPlan p, const uint16_t* __restrict__ src,
-                                                             uint16_t* __restrict__ dst) {
-  constexpr int CH = D / 8;
-  constexpr int LD = D + 8;  // padded LDS row (bf16 elements)
-  __shared__ __attribute__((aligned(16))) uint16_t tileb[kTile * LD];
-  const int64_t t = blockIdx.x;
-  const int h = p.row_head[t];
-  const DevShape& sh = p.shape[p.head_shape[h]];
-  const int64_t s0 = t * kTile - p.head_row_off[h];  // first slot of the tile (head-local)
-  for (int q = threadIdx.x; q < kTile * CH; q += kThreads) {
-    const int r = q / CH, c = q % CH;
-    const int32_t tok = sh.perm[s0 + r];
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (tok >= 0) v = ld16(src + ((int64_t)tok * p.num_heads + h) * D + 8 * c);
-    *reinterpret_cast<u32x4*>(&tileb[r * LD + 8 * c]) = v;
-  }
-  __syncthreads();
-  // output row d holds 128 slots = 16 chunks of 8
-  uint16_t* out = dst + t * (int64_t)D * kTile;
-  for (int q = threadIdx.x; q < D * 16; q += kThreads) {
-    const int d = q / 16, c = q % 16;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = tileb[(8 * c + 2 * e) * LD + d];
-      const uint32_t hi = tileb[(8 * c + 2 * e + 1) * LD + d];
-      w[e] = lo | (hi << 16);
-    }
-    u32x4 v = {w[0], w[1], w[2], w[3]};
-    st16(out + (int64_t)d * kTile + 8 * c, v);
-  }
-}
-
 // Forward permutation of Q, K and V in one launch, with the pooling of Q and
 // K fused in.  Workgroup (tile t, tensor y); thread (cb, sb) owns channels
 // 8cb..8cb+7 of slots 8sb..8sb+7: it gathers those eight 16-byte pieces of
@@ -134,14 +98,15 @@ __global__ void __launch_bounds__(D * 2) permute_qkv_kernel(DevPlan p, const uin
                                                            const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v, uint16_t* __restrict__ qp,
                                                            uint16_t* __restrict__ kp, uint16_t* __restrict__ vt,
-                                                           float* __restrict__ feat_q, float* __restrict__ feat_k) {
+                                                           float* __restrict__ feat_q, float* __restrict__ feat_k,
+                                                           int y0) {
   constexpr int CB = D / 8;     // channel chunks
   constexpr int SB = 16;        // slot chunks of 8
   __shared__ double s_sum[SB][D];
   __shared__ float s_max[SB][D];
   __shared__ float s_min[SB][D];
   const int64_t t = blockIdx.x;
-  const int y = blockIdx.y;
+  const int y = y0 + (int)blockIdx.y;   // tensor: 0 Q, 1 K, 2 V
   const int cb = threadIdx.x % CB, sb = threadIdx.x / CB;
   const int h = uni(p.row_head[t]);
   const DevShape& sh = p.shape[uni(p.head_shape[h])];
@@ -2097,12 +2062,14 @@ __global__ void __launch_bounds__(kBwdThreads, 1) attn_bwd_dq_kernel(
 hipError_t launch_permute(const DevPlan& p, const void* src, void* dst, int direction, hipStream_t s) {
   const uint16_t* in = static_cast<const uint16_t*>(src);
   uint16_t* out = static_cast<uint16_t*>(dst);
-  if (direction == VEDA_PERMUTE_FORWARD_TRANSPOSED) {
-    const dim3 grid((unsigned)p.total_tiles);
+  if (direction == VEDA_PERMUTE_FORWARD_TRANSPOSED) {   // the V path of the fused permutation alone
+    const dim3 grid((unsigned)p.total_tiles, 1);
     if (p.head_dim == 128)
-      hipLaunchKernelGGL(permute_vt_kernel<128>, grid, dim3(kThreads), 0, s, p, in, out);
+      hipLaunchKernelGGL(permute_qkv_kernel<128>, grid, dim3(256), 0, s, p, in, in, in, nullptr, nullptr, out, nullptr,
+                         nullptr, 2);
     else
-      hipLaunchKernelGGL(permute_vt_kernel<64>, grid, dim3(kThreads), 0, s, p, in, out);
+      hipLaunchKernelGGL(permute_qkv_kernel<64>, grid, dim3(128), 0, s, p, in, in, in, nullptr, nullptr, out, nullptr,
+                         nullptr, 2);
     return hipGetLastError();
   }
   const int inverse = direction == VEDA_PERMUTE_INVERSE;
@@ -2121,7 +2088,7 @@ hipError_t launch_permute_qkv(const DevPlan& p, const void* q, const void* k, co
   const int64_t T = p.total_tiles;
   float* feat_q = ws ? static_cast<float*>(ws) : nullptr;
   float* feat_k = ws ? feat_q + T * 3 * D : nullptr;
-  const dim3 grid((unsigned)T, 3);
+  const dim3 grid((unsigned)T, v ? 3 : 2);   // blockIdx.y: Q, K, V
   auto cq = static_cast<const uint16_t*>(q);
   auto ck = static_cast<const uint16_t*>(k);
   auto cv = static_cast<const uint16_t*>(v);
@@ -2129,9 +2096,9 @@ hipError_t launch_permute_qkv(const DevPlan& p, const void* q, const void* k, co
   auto ok = static_cast<uint16_t*>(kp);
   auto ov = static_cast<uint16_t*>(vt);
   if (D == 128)
-    hipLaunchKernelGGL(permute_qkv_kernel<128>, grid, dim3(256), 0, s, p, cq, ck, cv, oq, ok, ov, feat_q, feat_k);
+    hipLaunchKernelGGL(permute_qkv_kernel<128>, grid, dim3(256), 0, s, p, cq, ck, cv, oq, ok, ov, feat_q, feat_k, 0);
   else
-    hipLaunchKernelGGL(permute_qkv_kernel<64>, grid, dim3(128), 0, s, p, cq, ck, cv, oq, ok, ov, feat_q, feat_k);
+    hipLaunchKernelGGL(permute_qkv_kernel<64>, grid, dim3(128), 0, s, p, cq, ck, cv, oq, ok, ov, feat_q, feat_k, 0);
   return hipGetLastError();
 }
 

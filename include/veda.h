@@ -190,7 +190,10 @@ veda_status veda_permute_tiles(const veda_plan* plan, const void* src, void* dst
  * are written to `workspace` (fp32 [T, 3D] for Q, then for K), where
  * veda_score_pooled picks them up.  Outputs are bit-identical to three
  * veda_permute_tiles calls.  workspace may be NULL (no pooling); otherwise it
- * must hold score_workspace_bytes. */
+ * must hold score_workspace_bytes.  v and v_t may both be NULL: then only Q
+ * and K are permuted (and pooled), e.g. so that V's permutation
+ * (veda_permute_tiles, FORWARD_TRANSPOSED) can run on another stream while
+ * the predictor scores; one NULL without the other is VEDA_ERR_INVALID_ARG. */
 veda_status veda_permute_qkv(const veda_plan* plan, const void* q, const void* k, const void* v,
                              void* q_perm, void* k_perm, void* v_t, void* workspace,
                              size_t workspace_bytes, void* stream);

@@ -479,6 +479,39 @@ def test_fused_equals_separate_bitwise():
         assert torch.equal(a[key], b[key]), key
 
 
+@pytest.mark.parametrize("idx", [2, 4])
+def test_permute_qk_only_and_side_stream_v(idx):
+    """veda_permute_qkv with v = v_t = NULL (Q and K only, with the pooling)
+    and V's tile-transposed permutation on a second stream, the way the bench
+    runs a layer: bitwise equal to the three-tensor fused call (permuted Q, K,
+    V^T and the pooled features); config 4 has two tile shapes."""
+    w = wl.workload(idx)
+    inp = wl.make_inputs(w)
+    plan = vb.Plan.from_workload(w)
+    dev = "cuda"
+    q, k, v = inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev)
+    ref = [plan.empty_perm(), plan.empty_perm(), plan.empty_vt(), plan.empty_workspace()]
+    plan.permute_qkv(q, k, v, *ref)
+    got = [torch.full_like(ref[0], -1), torch.full_like(ref[1], -1), torch.full_like(ref[2], -1),
+           torch.full_like(ref[3], float("nan"))]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan.permute(v, got[2], vb.VEDA_PERMUTE_FORWARD_TRANSPOSED, stream=side)
+    plan.permute_qkv(q, k, None, got[0], got[1], None, got[3])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    nf = 2 * plan.T * 3 * w.head_dim          # pooled features of Q, then K, at the workspace's start
+    ref[3], got[3] = ref[3][:nf], got[3][:nf]
+    for a, b, name in zip(ref, got, ("q_perm", "k_perm", "v_t", "pooled features")):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
+    with pytest.raises(ValueError):
+        plan.permute_qkv(q, k, v, got[0], got[1], None, got[3])
+    with pytest.raises(vb.VedaError) as e:
+        vb.veda_permute_qkv(plan.handle, q, k, v, got[0], got[1], None, got[3])
+    assert e.value.status == 1                   # VEDA_ERR_INVALID_ARG: v without v_t
+
+
 def test_config5_packed_sampled_rows():
     w = wl.workload(5)
     inp = wl.make_inputs(w)
