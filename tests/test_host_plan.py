@@ -203,3 +203,48 @@ def test_tile_plan_vote_matches_oracle():
             assert np.array_equal(vb.veda_tile_plan_vote(e, m), vo.vote_tile_shapes(e, m))
     with pytest.raises(vb.VedaError):
         vb.veda_tile_plan_vote(np.full((1, 2, 2), np.nan))
+
+
+def test_plans_and_errors_from_several_threads():
+    """Plans are host objects: several threads build, query and destroy their
+    own plans at once and get the same tables as a single thread; each
+    thread's last error message is its own (a failure in one thread is not
+    seen by another)."""
+    import threading
+    ref = {}
+    for idx in (1, 2, 3):
+        w = wl.workload(idx)
+        h = vb.veda_plan_create(w.segments, w.num_heads, w.head_dim, w.tile_shapes, w.budget_mode,
+                                w.keep_num, w.keep_den, w.fixed_k)
+        ref[idx] = (vb.veda_plan_query(h), vb.veda_plan_copy_row_ptr(h))
+        vb.veda_plan_destroy(h)
+    errors, msgs = [], {}
+
+    def work(tid):
+        try:
+            for rep in range(3):
+                idx = 1 + (tid + rep) % 3
+                w = wl.workload(idx)
+                h = vb.veda_plan_create(w.segments, w.num_heads, w.head_dim, w.tile_shapes, w.budget_mode,
+                                        w.keep_num, w.keep_den, w.fixed_k)
+                info, rp = vb.veda_plan_query(h), vb.veda_plan_copy_row_ptr(h)
+                vb.veda_plan_destroy(h)
+                assert info == ref[idx][0] and np.array_equal(rp, ref[idx][1])
+            if tid % 2:                          # odd threads fail on purpose, even ones do not
+                with pytest.raises(vb.VedaError):
+                    vb.veda_plan_create(w.segments, w.num_heads, 96, w.tile_shapes, w.budget_mode)
+            msgs[tid] = vb.veda_last_error()
+        except Exception as e:                   # reported on the main thread
+            errors.append((tid, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for tid, m in msgs.items():
+        if tid % 2:
+            assert "96" in m or "head" in m.lower(), m
+        else:
+            assert m == "", (tid, m)
