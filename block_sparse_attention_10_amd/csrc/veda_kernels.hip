@@ -88,7 +88,9 @@ __global__ void __launch_bounds__(kThreads) permute_rows_kernel(DevPlan p, const
 // Forward permutation of Q, K and V in one launch, with the pooling of Q and
 // K fused in.  Workgroup (tile t, tensor y); thread (cb, sb) owns channels
 // 8cb..8cb+7 of slots 8sb..8sb+7: it gathers those eight 16-byte pieces of
-// natural rows (the 16 threads sharing sb read whole 256-byte rows), then
+// natural rows (for Q and K the D/8 threads sharing sb are consecutive and
+// read whole rows; for V the 16 sharing cb are, so that each store writes
+// whole 256-byte V^T rows), then
 //  - Q, K: writes them as permuted rows and keeps fp64 sums / max / min of
 //    the valid ones, combined over sb through LDS in a fixed order;
 //  - V:    transposes the 8x8 block in registers and writes 8 rows of the
@@ -107,7 +109,11 @@ __global__ void __launch_bounds__(D * 2) permute_qkv_kernel(DevPlan p, const uin
   __shared__ float s_min[SB][D];
   const int64_t t = blockIdx.x;
   const int y = y0 + (int)blockIdx.y;   // tensor: 0 Q, 1 K, 2 V
-  const int cb = threadIdx.x % CB, sb = threadIdx.x / CB;
+  // Q, K: the D/8 threads of a slot chunk are consecutive (whole rows per
+  // load and store); V: the 16 threads of a channel chunk are (whole
+  // 256-byte V^T rows per store)
+  const int cb = y == 2 ? (int)threadIdx.x / SB : (int)threadIdx.x % CB;
+  const int sb = y == 2 ? (int)threadIdx.x % SB : (int)threadIdx.x / CB;
   const int h = uni(p.row_head[t]);
   const DevShape& sh = p.shape[uni(p.head_shape[h])];
   const int i = (int)(t - uni(p.head_tile_off[h]));
