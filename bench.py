@@ -299,7 +299,7 @@ def permute_rate(layer, w):
 def gemm_reference(n=8192, reps=20):
     """Rate of the vendor bf16 GEMM (torch.matmul of two contiguous n x n
     matrices of N(0,1) values) in the same run: what the matrix cores sustain
-    on random operands on this machine, next to the nominal 2.5 PFLOP/s."""
+    on random operands on this GPU, next to the nominal 2.5 PFLOP/s."""
     g = torch.Generator(device="cuda").manual_seed(7)
     a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
     b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
