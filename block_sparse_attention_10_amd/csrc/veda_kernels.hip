@@ -360,60 +360,65 @@ __global__ void __launch_bounds__(kThreads) project_kernel(DevPlan p, const floa
 }
 
 // s[i][j] = fp32(sum_d q_hat_i[d] k_hat_j[d]), d ascending in fp64; 64x64
-// output tile per workgroup, 4x4 per thread.
+// output tile per workgroup, 4x4 per thread.  q_hat and k_hat pass through
+// LDS 32 channels at a time, already widened to fp64 ([channel][row]), so
+// the inner loop is two 32-byte reads and 16 FMAs per channel.
+constexpr int kScoreChunk = 32;
+
 template <int D>
 __global__ void __launch_bounds__(kThreads) score_kernel(DevPlan p, const float* __restrict__ hat_q,
                                                         const float* __restrict__ hat_k, float* __restrict__ scores) {
-  __shared__ float qs[D][64];
-  __shared__ float ks[D][64];
+  static_assert(D % kScoreChunk == 0, "whole channel chunks");
+  __shared__ __attribute__((aligned(16))) double qs[kScoreChunk][64];
+  __shared__ __attribute__((aligned(16))) double ks[kScoreChunk][64];
   const int h = blockIdx.z;
   const DevShape& sh = p.shape[p.head_shape[h]];
   const int n = sh.num_tiles;
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
   if (i0 >= n || j0 >= n) return;
   const int64_t t0 = p.head_tile_off[h];
-  {   // 64 rows of q_hat and k_hat, 16-byte loads all in flight, stored [d][row]
-    constexpr int V4 = 64 * D / 4 / kThreads;
-    float4 bq[V4], bk[V4];
-#pragma unroll
-    for (int u = 0; u < V4; ++u) {
-      const int q4 = u * kThreads + threadIdx.x;
-      const int r = (4 * q4) / D, d = (4 * q4) % D;
-      // rows past the head's last tile read the last tile (in bounds) and are
-      // zeroed below, so every load is unconditional
-      bq[u] = *reinterpret_cast<const float4*>(hat_q + (t0 + min(i0 + r, n - 1)) * D + d);
-      bk[u] = *reinterpret_cast<const float4*>(hat_k + (t0 + min(j0 + r, n - 1)) * D + d);
-    }
-#pragma unroll
-    for (int u = 0; u < V4; ++u) {
-      const int r = (4 * (u * kThreads + threadIdx.x)) / D;
-      if (i0 + r >= n) bq[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j0 + r >= n) bk[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int u = 0; u < V4; ++u) {
-      const int q4 = u * kThreads + threadIdx.x;
-      const int r = (4 * q4) / D, d = (4 * q4) % D;
-      qs[d][r] = bq[u].x; qs[d + 1][r] = bq[u].y; qs[d + 2][r] = bq[u].z; qs[d + 3][r] = bq[u].w;
-      ks[d][r] = bk[u].x; ks[d + 1][r] = bk[u].y; ks[d + 2][r] = bk[u].z; ks[d + 3][r] = bk[u].w;
-    }
-  }
-  __syncthreads();
   const int ti = threadIdx.x / 16, tj = threadIdx.x % 16;
+  // staging: thread -> (row r, 8 consecutive channels) of the chunk; rows
+  // past the head's last tile read the last tile (in bounds) and are zeroed
+  constexpr int PER_ROW = kScoreChunk / 8;                 // threads per row
+  static_assert(64 * PER_ROW == kThreads, "one 8-channel piece per thread and matrix");
+  const int sr = threadIdx.x / PER_ROW, sc = 8 * (threadIdx.x % PER_ROW);
+  const bool qin = i0 + sr < n, kin = j0 + sr < n;
+  const float* qrow = hat_q + (t0 + min(i0 + sr, n - 1)) * D + sc;
+  const float* krow = hat_k + (t0 + min(j0 + sr, n - 1)) * D + sc;
   double acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-  for (int d = 0; d < D; ++d) {
-    const float4 qa = *reinterpret_cast<const float4*>(&qs[d][4 * ti]);
-    const float4 kb = *reinterpret_cast<const float4*>(&ks[d][4 * tj]);
-    const double qv[4] = {(double)qa.x, (double)qa.y, (double)qa.z, (double)qa.w};
-    const double kv[4] = {(double)kb.x, (double)kb.y, (double)kb.z, (double)kb.w};
+#pragma unroll 1
+  for (int c0 = 0; c0 < D; c0 += kScoreChunk) {
+    const float4 q0 = *reinterpret_cast<const float4*>(qrow + c0);
+    const float4 q1 = *reinterpret_cast<const float4*>(qrow + c0 + 4);
+    const float4 k0 = *reinterpret_cast<const float4*>(krow + c0);
+    const float4 k1 = *reinterpret_cast<const float4*>(krow + c0 + 4);
+    if (c0 > 0) __syncthreads();       // every thread is done with the previous chunk
+    const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int u = 0; u < 8; ++u) {
+      qs[sc + u][sr] = qin ? (double)qv[u] : 0.0;
+      ks[sc + u][sr] = kin ? (double)kv[u] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int d = 0; d < kScoreChunk; ++d) {
+      const double2 qa0 = *reinterpret_cast<const double2*>(&qs[d][4 * ti]);
+      const double2 qa1 = *reinterpret_cast<const double2*>(&qs[d][4 * ti + 2]);
+      const double2 kb0 = *reinterpret_cast<const double2*>(&ks[d][4 * tj]);
+      const double2 kb1 = *reinterpret_cast<const double2*>(&ks[d][4 * tj + 2]);
+      const double qd[4] = {qa0.x, qa0.y, qa1.x, qa1.y};
+      const double kd[4] = {kb0.x, kb0.y, kb1.x, kb1.y};
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = fma(qv[a], kv[b], acc[a][b]);
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = fma(qd[a], kd[b], acc[a][b]);
+    }
   }
   float* out = scores + p.head_pair_off[h];
 #pragma unroll
