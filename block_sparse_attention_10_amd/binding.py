@@ -63,7 +63,7 @@ class PlanInfo(ctypes.Structure):
                 ("device_table_bytes", ctypes.c_int64), ("score_workspace_bytes", ctypes.c_int64),
                 ("transpose_workspace_bytes", ctypes.c_int64), ("bwd_workspace_bytes", ctypes.c_int64),
                 ("max_tiles_per_head", ctypes.c_int32), ("uploaded", ctypes.c_int32),
-                ("heat_workspace_bytes", ctypes.c_int64)]
+                ("heat_workspace_bytes", ctypes.c_int64), ("reduce_workspace_bytes", ctypes.c_int64)]
 
 
 # name -> (restype, argtypes)
@@ -92,8 +92,8 @@ _SIGS = {
     "veda_block_sparse_attn_fwd": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _P, _P, _P]),
     "veda_block_heat": (_I32, [_P, _P, _P, _P, ctypes.c_float, _P, _P]),
     "veda_dense_lse_heat": (_I32, [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
-    "veda_mask_mass": (_I32, [_P, _P, _P, _P, _P, _P]),
-    "veda_output_error": (_I32, [_P, _P, _P, _P, _P]),
+    "veda_mask_mass": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "veda_output_error": (_I32, [_P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "veda_mask_transpose": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "veda_block_sparse_attn_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
                                           _P, ctypes.c_size_t, _P]),
@@ -269,12 +269,14 @@ def veda_dense_lse_heat(plan: int, q, k, row_ptr, col_idx, softmax_scale: float,
                                      _ptr(lse), _ptr(heat), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
-def veda_mask_mass(plan: int, heat, row_ptr, col_idx, mass, stream=None) -> None:
-    _check(lib().veda_mask_mass(plan, _ptr(heat), _ptr(row_ptr), _ptr(col_idx), _ptr(mass), _stream(stream)))
+def veda_mask_mass(plan: int, heat, row_ptr, col_idx, mass, workspace, stream=None) -> None:
+    _check(lib().veda_mask_mass(plan, _ptr(heat), _ptr(row_ptr), _ptr(col_idx), _ptr(mass), _ptr(workspace),
+                                _nbytes(workspace), _stream(stream)))
 
 
-def veda_output_error(plan: int, o, o_ref, err, stream=None) -> None:
-    _check(lib().veda_output_error(plan, _ptr(o), _ptr(o_ref), _ptr(err), _stream(stream)))
+def veda_output_error(plan: int, o, o_ref, err, workspace, stream=None) -> None:
+    _check(lib().veda_output_error(plan, _ptr(o), _ptr(o_ref), _ptr(err), _ptr(workspace), _nbytes(workspace),
+                                   _stream(stream)))
 
 
 def veda_mask_transpose(plan: int, row_ptr, col_idx, col_ptr, row_idx, workspace, stream=None) -> None:
@@ -514,22 +516,32 @@ class Plan:
         import torch
         return torch.empty(max(self.info[key], 1), dtype=torch.uint8, device="cuda")
 
-    def output_error(self, o, o_ref, err, stream=None):
+    def _reduce_ws(self, workspace):
+        # the two-launch reductions' partial sums: a given buffer, else one
+        # torch buffer kept with the plan (calls on one stream reuse it)
+        if workspace is not None:
+            self._check_ws(workspace, "reduce_workspace_bytes")
+            return workspace
+        if getattr(self, "_rws", None) is None:
+            self._rws = self.empty_bytes("reduce_workspace_bytes")
+        return self._rws
+
+    def output_error(self, o, o_ref, err, workspace=None, stream=None):
         import torch
         nat = (self.N, self.H, self.D)
         self._expect(o, nat, torch.bfloat16, "o")
         self._expect(o_ref, nat, torch.bfloat16, "o_ref")
         self._expect(err, (self.H,), torch.float64, "err")
-        veda_output_error(self.handle, o, o_ref, err, stream)
+        veda_output_error(self.handle, o, o_ref, err, self._reduce_ws(workspace), stream)
 
-    def mask_mass(self, heat, row_ptr, col_idx, mass, stream=None):
+    def mask_mass(self, heat, row_ptr, col_idx, mass, workspace=None, stream=None):
         import torch
         self._expect(heat, (self.info["total_pairs"],), torch.float32, "heat")
         self._expect(row_ptr, (self.T + 1,), torch.int32, "row_ptr")
         if col_idx is None or col_idx.dtype != torch.int32 or not col_idx.is_cuda:
             raise ValueError("col_idx must be a device int32 tensor")
         self._expect(mass, (self.H,), torch.float64, "mass")
-        veda_mask_mass(self.handle, heat, row_ptr, col_idx, mass, stream)
+        veda_mask_mass(self.handle, heat, row_ptr, col_idx, mass, self._reduce_ws(workspace), stream)
 
     # allocation helpers (torch: device memory only)
     def empty_perm(self):

@@ -503,6 +503,7 @@ veda_status veda_plan_create(const veda_plan_desc* d, veda_plan** out) {
   in.transpose_workspace_bytes = transpose_workspace_bytes(in.total_pairs, in.total_tiles);
   in.bwd_workspace_bytes = bwd_workspace_bytes(in.total_rows, in.total_tiles);
   in.heat_workspace_bytes = heat_workspace_bytes(in.nnz);
+  in.reduce_workspace_bytes = reduce_workspace_bytes(H, maxtiles);
   build_attn_order(*p);
   build_staging(*p);
   in.device_table_bytes = (int64_t)p->staging.size();
@@ -726,21 +727,38 @@ veda_status veda_dense_lse_heat(const veda_plan* p, const void* q, const void* k
                   "dense LSE and heat");
 }
 
+namespace {
+veda_status check_reduce_ws(const veda_plan* p, void* workspace, size_t workspace_bytes) {
+  veda_status st = check_ptr(workspace, "workspace");
+  if (st) return st;
+  if ((int64_t)workspace_bytes < p->info.reduce_workspace_bytes)
+    return fail(VEDA_ERR_WORKSPACE, "workspace of %zu bytes, %lld needed", workspace_bytes,
+                (long long)p->info.reduce_workspace_bytes);
+  return ok();
+}
+}  // namespace
+
 veda_status veda_mask_mass(const veda_plan* p, const float* heat, const int32_t* row_ptr, const int32_t* col_idx,
-                           double* mass, void* stream) {
+                           double* mass, void* workspace, size_t workspace_bytes, void* stream) {
   veda_status st = check_plan_ready(p);
   if (st) return st;
   if ((st = check_ptr(heat, "heat")) || (st = check_ptr(row_ptr, "row_ptr")) ||
-      (st = check_ptr(col_idx, "col_idx")) || (st = check_ptr(mass, "mass")))
+      (st = check_ptr(col_idx, "col_idx")) || (st = check_ptr(mass, "mass")) ||
+      (st = check_reduce_ws(p, workspace, workspace_bytes)))
     return st;
-  return launched(launch_mask_mass(p->dev, heat, row_ptr, col_idx, mass, (hipStream_t)stream), "mask mass");
+  return launched(launch_mask_mass(p->dev, p->info.max_tiles_per_head, heat, row_ptr, col_idx, mass, workspace,
+                                   (hipStream_t)stream),
+                  "mask mass");
 }
 
-veda_status veda_output_error(const veda_plan* p, const void* o, const void* o_ref, double* err, void* stream) {
+veda_status veda_output_error(const veda_plan* p, const void* o, const void* o_ref, double* err, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   veda_status st = check_plan_ready(p);
   if (st) return st;
-  if ((st = check_ptr(o, "o")) || (st = check_ptr(o_ref, "o_ref")) || (st = check_ptr(err, "err"))) return st;
-  return launched(launch_output_error(p->dev, p->info.num_tokens, o, o_ref, err, (hipStream_t)stream),
+  if ((st = check_ptr(o, "o")) || (st = check_ptr(o_ref, "o_ref")) || (st = check_ptr(err, "err")) ||
+      (st = check_reduce_ws(p, workspace, workspace_bytes)))
+    return st;
+  return launched(launch_output_error(p->dev, p->info.num_tokens, o, o_ref, err, workspace, (hipStream_t)stream),
                   "output error");
 }
 

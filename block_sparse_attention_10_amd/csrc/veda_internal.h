@@ -28,6 +28,13 @@ inline int64_t bwd_workspace_bytes(int64_t total_rows, int64_t total_tiles) {
 }
 // One fp32 per (block, query slot): each block's sum of p per query.
 inline int64_t heat_workspace_bytes(int64_t nnz) { return align256(nnz * 128 * 4); }
+// Per-head partial sums of the two-launch reductions (mask mass: one per 16
+// rows; output error: 32 token chunks), two fp64 each.
+inline int mass_chunks(int32_t max_tiles) { return (max_tiles + 15) / 16; }
+inline int64_t reduce_workspace_bytes(int32_t num_heads, int32_t max_tiles) {
+  const int64_t c = mass_chunks(max_tiles) > 32 ? mass_chunks(max_tiles) : 32;
+  return align256((int64_t)num_heads * c * 16);
+}
 
 // Device view of the tables of one distinct tile shape.  Heads that share a
 // shape share these tables (tiling, valid counts, budgets, local CSR offsets).
@@ -80,10 +87,10 @@ hipError_t launch_lse_heat(const DevPlan& p, const void* q, const void* k, const
                            hipStream_t s);
 hipError_t launch_heat(const DevPlan& p, const void* q, const void* k, const float* lse,
                        float scale, float* heat, hipStream_t s);
-hipError_t launch_mask_mass(const DevPlan& p, const float* heat, const int32_t* row_ptr, const int32_t* col_idx,
-                            double* mass, hipStream_t s);
+hipError_t launch_mask_mass(const DevPlan& p, int32_t max_tiles, const float* heat, const int32_t* row_ptr,
+                            const int32_t* col_idx, double* mass, void* ws, hipStream_t s);
 hipError_t launch_output_error(const DevPlan& p, int64_t num_tokens, const void* o, const void* o_ref, double* err,
-                               hipStream_t s);
+                               void* ws, hipStream_t s);
 hipError_t launch_mask_transpose(const DevPlan& p, const int32_t* row_ptr, const int32_t* col_idx, int32_t* col_ptr,
                                  int32_t* row_idx, void* workspace, int64_t total_pairs, hipStream_t s);
 hipError_t launch_attn_bwd(const DevPlan& p, const void* q, const void* k, const void* v, const void* o,

@@ -1432,65 +1432,92 @@ __global__ void __launch_bounds__(kThreads, 2) heat_kernel(DevPlan p, const uint
 // attention mass of a block mask
 // ---------------------------------------------------------------------------
 //
-// One workgroup per head.  Thread x takes the head's rows x, x + 256, ...;
-// each row's heat over its listed key tiles is summed in fp64 and weighted by
-// the row tile's valid query count; the partial sums and counts are combined
-// by a fixed-order tree in LDS, so the result does not depend on timing.
-__global__ void __launch_bounds__(kThreads) mask_mass_kernel(DevPlan p, const float* __restrict__ heat,
-                                                            const int32_t* __restrict__ row_ptr,
-                                                            const int32_t* __restrict__ col_idx,
-                                                            double* __restrict__ mass) {
-  __shared__ double kept_s[kThreads];
-  __shared__ double cnt_s[kThreads];
-  const int h = blockIdx.x;
+// Two launches, both in a fixed order (the result does not depend on
+// timing).  Part: workgroup (chunk c, head h) takes rows 16c .. 16c+15 of the
+// head, 16 threads per row; each thread sums its share of the row's listed
+// heat in list order, the row's 16 partials are combined by a fixed shuffle
+// tree, weighted by the row tile's valid query count, and the 16 rows by a
+// fixed tree in LDS; (kept, count) go to part[h][c].  Final: thread h sums
+// its chunks in ascending order.
+constexpr int kMassRows = 16;
+
+__global__ void __launch_bounds__(kThreads) mask_mass_part_kernel(DevPlan p, const float* __restrict__ heat,
+                                                                 const int32_t* __restrict__ row_ptr,
+                                                                 const int32_t* __restrict__ col_idx,
+                                                                 double2* __restrict__ part, int chunks) {
+  __shared__ double kept_s[kMassRows];
+  __shared__ double cnt_s[kMassRows];
+  const int c = blockIdx.x, h = blockIdx.y;
   const DevShape& sh = p.shape[p.head_shape[h]];
   const int n = sh.num_tiles;
   const int64_t t0 = p.head_tile_off[h];
   const float* hm = heat + p.head_pair_off[h];
-  double kept = 0.0, cnt = 0.0;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    double row = 0.0;
-    for (int e = row_ptr[t0 + i]; e < row_ptr[t0 + i + 1]; ++e) {
+  const int rr = threadIdx.x / 16, sub = threadIdx.x % 16;
+  const int i = c * kMassRows + rr;
+  double row = 0.0;
+  if (i < n) {
+    const int e1 = row_ptr[t0 + i + 1];
+    for (int e = row_ptr[t0 + i] + sub; e < e1; e += 16) {
       const int j = col_idx[e];
       if (j >= 0 && j < n) row += (double)hm[(int64_t)i * n + j];
     }
-    const double v = (double)sh.valid[i];
-    kept += v * row;
-    cnt += v;
   }
-  kept_s[threadIdx.x] = kept;
-  cnt_s[threadIdx.x] = cnt;
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) row += __shfl_xor(row, off, 16);
+  if (sub == 0) {
+    const double v = i < n ? (double)sh.valid[i] : 0.0;
+    kept_s[rr] = v * row;
+    cnt_s[rr] = v;
+  }
   __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) {
-      kept_s[threadIdx.x] += kept_s[threadIdx.x + w];
-      cnt_s[threadIdx.x] += cnt_s[threadIdx.x + w];
+  if (threadIdx.x == 0) {
+    double kept = 0.0, cnt = 0.0;
+    for (int r = 0; r < kMassRows; ++r) {
+      kept += kept_s[r];
+      cnt += cnt_s[r];
     }
-    __syncthreads();
+    part[(int64_t)h * chunks + c] = make_double2(kept, cnt);
   }
-  if (threadIdx.x == 0) mass[h] = kept_s[0] / cnt_s[0];
+}
+
+__global__ void __launch_bounds__(kThreads) mask_mass_final_kernel(int num_heads, const double2* __restrict__ part,
+                                                                  int chunks, double* __restrict__ mass) {
+  const int h = blockIdx.x * kThreads + threadIdx.x;
+  if (h >= num_heads) return;
+  double kept = 0.0, cnt = 0.0;
+  for (int c = 0; c < chunks; ++c) {
+    const double2 v = part[(int64_t)h * chunks + c];
+    kept += v.x;
+    cnt += v.y;
+  }
+  mass[h] = kept / cnt;
 }
 
 // ---------------------------------------------------------------------------
 // relative output error of two natural-order outputs
 // ---------------------------------------------------------------------------
 //
-// One workgroup of 512 threads per head.  Thread x takes the 16-byte chunks
-// x, x + 512, ... of the head's N x D values (strided by H*D between
-// tokens), accumulates (o - o_ref)^2 and o_ref^2 in fp64, and the partials
-// are combined by a fixed-order tree in LDS.
+// Two launches in a fixed order.  Part: workgroup (chunk c, head h) takes
+// tokens [c N / C, (c+1) N / C) of the head; thread x takes the 16-byte
+// pieces x, x + 256, ... of that range (strided by H*D between tokens),
+// accumulates (o - o_ref)^2 and o_ref^2 in fp64, and the partials meet in a
+// fixed-order tree in LDS.  Final: thread h sums its C chunks in ascending
+// order and divides.
+constexpr int kErrChunks = 32;
+
 template <int D>
-__global__ void __launch_bounds__(512) output_error_kernel(int64_t num_tokens, int num_heads,
-                                                          const uint16_t* __restrict__ o,
-                                                          const uint16_t* __restrict__ o_ref,
-                                                          double* __restrict__ err) {
+__global__ void __launch_bounds__(kThreads) output_error_part_kernel(int64_t num_tokens, int num_heads,
+                                                                    const uint16_t* __restrict__ o,
+                                                                    const uint16_t* __restrict__ o_ref,
+                                                                    double2* __restrict__ part) {
   constexpr int CH = D / 8;
-  __shared__ double num_s[512];
-  __shared__ double den_s[512];
-  const int h = blockIdx.x;
+  __shared__ double num_s[kThreads];
+  __shared__ double den_s[kThreads];
+  const int c = blockIdx.x, h = blockIdx.y;
+  const int64_t q0 = num_tokens * c / kErrChunks * CH, q1 = num_tokens * (c + 1) / kErrChunks * CH;
   double num = 0.0, den = 0.0;
-  for (int64_t c = threadIdx.x; c < num_tokens * CH; c += 512) {
-    const int64_t n = c / CH, off = (n * num_heads + h) * D + 8 * (c % CH);
+  for (int64_t q = q0 + threadIdx.x; q < q1; q += kThreads) {
+    const int64_t n = q / CH, off = (n * num_heads + h) * D + 8 * (q % CH);
     const u32x4 a = ld16(o + off), b = ld16(o_ref + off);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1503,14 +1530,27 @@ __global__ void __launch_bounds__(512) output_error_kernel(int64_t num_tokens, i
   num_s[threadIdx.x] = num;
   den_s[threadIdx.x] = den;
   __syncthreads();
-  for (int w = 256; w > 0; w >>= 1) {
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
     if ((int)threadIdx.x < w) {
       num_s[threadIdx.x] += num_s[threadIdx.x + w];
       den_s[threadIdx.x] += den_s[threadIdx.x + w];
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) err[h] = num_s[0] / den_s[0];
+  if (threadIdx.x == 0) part[(int64_t)h * kErrChunks + c] = make_double2(num_s[0], den_s[0]);
+}
+
+__global__ void __launch_bounds__(kThreads) output_error_final_kernel(int num_heads, const double2* __restrict__ part,
+                                                                     double* __restrict__ err) {
+  const int h = blockIdx.x * kThreads + threadIdx.x;
+  if (h >= num_heads) return;
+  double num = 0.0, den = 0.0;
+  for (int c = 0; c < kErrChunks; ++c) {
+    const double2 v = part[(int64_t)h * kErrChunks + c];
+    num += v.x;
+    den += v.y;
+  }
+  err[h] = num / den;
 }
 
 // ---------------------------------------------------------------------------
@@ -2216,23 +2256,29 @@ hipError_t launch_heat(const DevPlan& p, const void* q, const void* k, const flo
   return hipGetLastError();
 }
 
-hipError_t launch_mask_mass(const DevPlan& p, const float* heat, const int32_t* row_ptr, const int32_t* col_idx,
-                            double* mass, hipStream_t s) {
-  hipLaunchKernelGGL(mask_mass_kernel, dim3((unsigned)p.num_heads), dim3(kThreads), 0, s, p, heat, row_ptr, col_idx,
-                     mass);
+hipError_t launch_mask_mass(const DevPlan& p, int32_t max_tiles, const float* heat, const int32_t* row_ptr,
+                            const int32_t* col_idx, double* mass, void* ws, hipStream_t s) {
+  const int chunks = mass_chunks(max_tiles);
+  double2* part = static_cast<double2*>(ws);
+  hipLaunchKernelGGL(mask_mass_part_kernel, dim3((unsigned)chunks, (unsigned)p.num_heads), dim3(kThreads), 0, s, p,
+                     heat, row_ptr, col_idx, part, chunks);
+  hipLaunchKernelGGL(mask_mass_final_kernel, dim3((unsigned)((p.num_heads + kThreads - 1) / kThreads)), dim3(kThreads),
+                     0, s, p.num_heads, part, chunks, mass);
   return hipGetLastError();
 }
 
 hipError_t launch_output_error(const DevPlan& p, int64_t num_tokens, const void* o, const void* o_ref, double* err,
-                               hipStream_t s) {
+                               void* ws, hipStream_t s) {
   const uint16_t* a = static_cast<const uint16_t*>(o);
   const uint16_t* b = static_cast<const uint16_t*>(o_ref);
+  double2* part = static_cast<double2*>(ws);
+  const dim3 grid(kErrChunks, (unsigned)p.num_heads);
   if (p.head_dim == 128)
-    hipLaunchKernelGGL(output_error_kernel<128>, dim3((unsigned)p.num_heads), dim3(512), 0, s, num_tokens,
-                       p.num_heads, a, b, err);
+    hipLaunchKernelGGL(output_error_part_kernel<128>, grid, dim3(kThreads), 0, s, num_tokens, p.num_heads, a, b, part);
   else
-    hipLaunchKernelGGL(output_error_kernel<64>, dim3((unsigned)p.num_heads), dim3(512), 0, s, num_tokens,
-                       p.num_heads, a, b, err);
+    hipLaunchKernelGGL(output_error_part_kernel<64>, grid, dim3(kThreads), 0, s, num_tokens, p.num_heads, a, b, part);
+  hipLaunchKernelGGL(output_error_final_kernel, dim3((unsigned)((p.num_heads + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, p.num_heads, part, err);
   return hipGetLastError();
 }
 

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define VEDA_ABI_VERSION 5
+#define VEDA_ABI_VERSION 6
 
 typedef int32_t veda_status;
 enum {
@@ -125,6 +125,8 @@ typedef struct veda_plan_info {
   int32_t max_tiles_per_head;
   int32_t uploaded;           /* 1 after a successful veda_plan_upload        */
   int64_t heat_workspace_bytes; /* bytes veda_dense_lse_heat needs (nnz*512)   */
+  int64_t reduce_workspace_bytes; /* bytes veda_mask_mass / veda_output_error
+                                     need (per-head partial sums)             */
 } veda_plan_info;
 
 /* ABI version of the loaded library (VEDA_ABI_VERSION it was built with). */
@@ -315,9 +317,14 @@ veda_status veda_dense_lse_heat(const veda_plan* plan, const void* q, const void
  *   row_ptr, col_idx: device CSR of this plan's shape (as veda_select_blocks
  *            writes it); out-of-range columns are skipped
  *   mass:    device fp64 [num_heads]
- * fp64 accumulation in a fixed order: bitwise reproducible. */
+ *   workspace: device scratch of at least reduce_workspace_bytes (per-head
+ *            partial sums; contents on entry do not matter); too small is
+ *            VEDA_ERR_WORKSPACE
+ * fp64 accumulation in a fixed order (partial sums over 16-row chunks, then
+ * the chunks in ascending order): bitwise reproducible. */
 veda_status veda_mask_mass(const veda_plan* plan, const float* heat, const int32_t* row_ptr,
-                           const int32_t* col_idx, double* mass, void* stream);
+                           const int32_t* col_idx, double* mass, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* Relative output error of a sparse attention output against a reference
  * (Miowtion project page, Key Features: oracle tile-plan search by relative
@@ -326,8 +333,12 @@ veda_status veda_mask_mass(const veda_plan* plan, const float* heat, const int32
  *   o, o_ref: device bf16 [N, H, D] (natural token order, as
  *             veda_block_sparse_attn_fwd writes with VEDA_LAYOUT_NATURAL)
  *   err:      device fp64 [num_heads]
+ *   workspace: device scratch of at least reduce_workspace_bytes (per-head
+ *             partial sums over 32 token chunks); too small is
+ *             VEDA_ERR_WORKSPACE
  * fp64 accumulation in a fixed order: bitwise reproducible. */
 veda_status veda_output_error(const veda_plan* plan, const void* o, const void* o_ref, double* err,
+                              void* workspace, size_t workspace_bytes,
                               void* stream);
 
 /* Transposed block lists for the backward (Miowtion project page: the

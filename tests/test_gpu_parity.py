@@ -756,5 +756,11 @@ def test_error_paths_on_device():
                                           buf.data_ptr() + 8192, 7, None, None, None) == 1
     assert lib.veda_score_tiles(plan.handle, buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(),
                                 buf.data_ptr(), buf.data_ptr(), 16, None) == 4
+    # the two-launch reductions refuse a short workspace (WORKSPACE) on the host
+    short = plan.info["reduce_workspace_bytes"] - 16
+    assert lib.veda_mask_mass(plan.handle, buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(),
+                              buf.data_ptr(), short, None) == 4
+    assert lib.veda_output_error(plan.handle, buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(),
+                                 short, None) == 4
     with pytest.raises(vb.VedaError):
         vb.veda_plan_upload(plan.handle, plan.tables)   # uploaded twice

@@ -37,7 +37,7 @@ def test_abi_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert vb.veda_abi_version() == 5
+    assert vb.veda_abi_version() == 6
 
 
 def test_available_reports_reason_without_gpu():
@@ -86,6 +86,7 @@ def _compare_plan(w):
         assert np.array_equal(vb.veda_plan_copy_row_ptr(h), rp)
         assert info["nnz"] == rp[-1]
         assert info["heat_workspace_bytes"] >= info["nnz"] * 128 * 4
+        assert info["reduce_workspace_bytes"] >= w.num_heads * max(32, -(-info["max_tiles_per_head"] // 16)) * 16
     finally:
         vb.veda_plan_destroy(h)
 
@@ -172,8 +173,8 @@ def test_compute_calls_check_on_host_before_any_launch():
         assert lib.veda_block_heat(h, fake, fake, fake, ctypes.c_float(0.125), fake, None) == 6
         assert lib.veda_dense_lse_heat(h, fake, fake, fake, fake, ctypes.c_float(0.125), fake, fake, fake,
                                        1 << 30, None) == 6
-        assert lib.veda_mask_mass(h, fake, fake, fake, fake, None) == 6
-        assert lib.veda_output_error(h, fake, fake, fake, None) == 6
+        assert lib.veda_mask_mass(h, fake, fake, fake, fake, fake, 1 << 20, None) == 6
+        assert lib.veda_output_error(h, fake, fake, fake, fake, 1 << 20, None) == 6
         assert lib.veda_mask_transpose(h, fake, fake, fake, fake, fake, 1 << 30, None) == 6
         assert lib.veda_block_sparse_attn_bwd(h, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
                                               ctypes.c_float(0.125), fake, fake, fake, fake, 1 << 30, None) == 6
