@@ -537,11 +537,14 @@ def block_sparse_attention_backward(plan: Plan, q_perm, k_perm, v_perm, do_perm,
 # ---------------------------------------------------------------------------
 
 def block_heat(plan: Plan, q_perm, k_perm, lse: np.ndarray, scale: float,
-               heads: Optional[Sequence[int]] = None) -> List[Optional[np.ndarray]]:
+               heads: Optional[Sequence[int]] = None,
+               rows: Optional[Sequence[int]] = None) -> List[Optional[np.ndarray]]:
     """Teacher block heat (A16): heat[i, j] = mean over the valid queries r of
     tile i of the attention probability mass on the valid keys of tile j,
     exp(scale q_r.k_c - LSE_r) summed over c, with LSE the dense attention's
-    log-sum-exp over all valid keys.  Each row is a distribution.
+    log-sum-exp over all valid keys.  Each row is a distribution.  `rows`
+    restricts the work to those query tiles of each head (the other rows of
+    the returned matrices are NaN); only their LSE entries are read.
     """
     out: List[Optional[np.ndarray]] = [None] * plan.num_heads
     heads = range(plan.num_heads) if heads is None else heads
@@ -552,7 +555,9 @@ def block_heat(plan: Plan, q_perm, k_perm, lse: np.ndarray, scale: float,
         Kall = np.asarray(k_perm[base:base + ht.rows], dtype=np.float64)
         valid = ht.valid_counts()
         heat = np.zeros((n, n), dtype=np.float64)
-        for i in range(n):
+        if rows is not None:
+            heat[:] = np.nan
+        for i in (range(n) if rows is None else rows):
             nq = int(valid[i])
             r0 = base + TILE_TOKENS * i
             q = np.asarray(q_perm[r0:r0 + nq], dtype=np.float64)

@@ -188,6 +188,48 @@ def test_rows_longer_than_the_staged_list():
             assert max_abs <= gp.MAX_ABS and rel <= gp.REL_L2 and lerr <= gp.LSE_ABS
 
 
+def test_dense_lse_heat_rows_longer_than_the_staged_list():
+    """The one-pass dense LSE and heat on rows of 2051 key blocks (a dense
+    1-D segment, one head, D = 64; the staged block list refills mid-row and
+    the heat reduction reads the rest of the row's list from memory), on the
+    fast pass and, with tile 2049's keys scaled by 64, on the exact fallback
+    pass with its re-walk: sampled query tiles' LSE and heat rows against the
+    oracle, every heat row summing to 1."""
+    n_tok = 128 * 2050 + 37
+    w = wl.Workload(97, "long_rows_2051_tiles", (wl.Segment(wl.DENSE1D, (1, 1, n_tok), 0),), 1, 64,
+                    ((2, 8, 8),), wl.ALL_BLOCKS)
+    base = wl.make_inputs(w, seed=w.index)
+    op = vo.Plan.from_workload(w)
+    n = op.heads[0].num_tiles
+    perm = op.heads[0].perm()
+    for scaled in (False, True):
+        inp = dict(base)
+        if scaled:
+            k = base["k"].float()
+            toks = perm[128 * 2049: 128 * 2050]
+            k[torch.from_numpy(toks[toks >= 0].astype(np.int64)), 0, :] *= 64.0
+            inp["k"] = k.to(torch.bfloat16)
+        g = gp.gpu_path(w, inp, dense_mask=False)
+        lse, heat = _dense_lse_heat(g, w)
+        a, b = g["lse"].cpu().numpy(), lse.cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+        hg = heat.cpu().numpy().reshape(n, n)
+        assert np.max(np.abs(hg.sum(axis=1) - 1.0)) <= 1e-3
+        qp, kp, vp = (vo.permute_forward(op, gp.f64(inp[x])) for x in ("q", "k", "v"))
+        sampled = (0, 1024, n - 1)
+        L = np.full(op.total_rows, np.nan)
+        for i in sampled:
+            _, Li = vo.attention_row_tile(op, 0, i, qp, kp, vp, range(n), w.softmax_scale)
+            nv = op.heads[0].tiles[i].valid
+            L[128 * i: 128 * i + nv] = Li
+            assert np.max(np.abs(b[128 * i: 128 * i + nv] - Li)) <= gp.LSE_ABS
+        ref = vo.block_heat(op, qp, kp, L, w.softmax_scale, rows=sampled)[0]
+        for i in sampled:
+            err = float(np.max(np.abs(hg[i] - ref[i])))
+            print("long rows scaled=%s tile %d: heat max_abs %.3e" % (scaled, i, err), flush=True)
+            assert err <= gp.HEAT_ABS
+
+
 @pytest.mark.parametrize("kind", ["small", "guard_all_blocks", "guard_late_logits"])
 def test_lse_only_equals_full_attention(kind):
     """veda_block_sparse_attn_fwd with o = NULL computes only the LSE (no PV
