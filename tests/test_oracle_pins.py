@@ -635,6 +635,33 @@ def test_heat_packed():
     check_heat(_small_packed_workload())
 
 
+def test_heat_row_subset():
+    """block_heat restricted to some query tiles computes exactly those rows
+    (pinned above against library softmax probabilities), reading the LSE of
+    those rows only (NaN elsewhere), and leaves the other rows NaN."""
+    w = _small_packed_workload()
+    plan = vo.Plan.from_workload(w)
+    N, H, D = w.num_tokens, w.num_heads, w.head_dim
+    q = _f64(_random_bf16((N, H, D), 7))
+    k = _f64(_random_bf16((N, H, D), 8))
+    qp, kp = vo.permute_forward(plan, q), vo.permute_forward(plan, k)
+    _, L = vo.block_sparse_attention(plan, qp, kp, kp, vo.all_blocks_selection(plan), w.softmax_scale)
+    full = vo.block_heat(plan, qp, kp, L, w.softmax_scale)
+    n = plan.heads[0].num_tiles
+    rows = [0, n - 1]
+    Lsub = np.full_like(L, np.nan)
+    for i in rows:
+        r0 = plan.row_offset[0] + 128 * i
+        Lsub[r0:r0 + 128] = L[r0:r0 + 128]
+    sub = vo.block_heat(plan, qp, kp, Lsub, w.softmax_scale, heads=[0], rows=rows)
+    assert sub[1] is None if H > 1 else True
+    for i in range(n):
+        if i in rows:
+            assert np.array_equal(sub[0][i], full[0][i])
+        else:
+            assert np.all(np.isnan(sub[0][i]))
+
+
 # ---------------------------------------------------------------------------
 # P10: attention mass of a mask, oracle mask, recall
 # ---------------------------------------------------------------------------
