@@ -170,34 +170,34 @@ size_t append_table(std::vector<uint8_t>& img, const std::vector<T>& v) {
 
 // Order in which attention workgroups take query tiles.  Rows of equal cost
 // keep head-major order so neighbouring query tiles of one head (which keep
-// overlapping key tiles) run close in time; when row costs differ widely (the
-// dense audio rows of a packed sequence) the longest rows go first.
+// overlapping key tiles) run close in time; when some rows cost far more
+// than the typical row (the dense audio rows of a packed sequence) those go
+// first, longest first, and the rest keep the head-major order.
 void build_attn_order(veda_plan& p) {
   const int64_t T = p.info.total_tiles;
-  std::vector<int32_t> order(T);
-  for (int64_t t = 0; t < T; ++t) order[t] = (int32_t)t;
-  int32_t mx = 0, mn = INT32_MAX;
-  for (auto& s : p.shapes) {
-    mx = std::max(mx, s.max_row);
-    mn = std::min(mn, s.min_row);
-  }
-  if (mx > 2 * mn + 2) {
-    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
-      return (p.row_ptr[x + 1] - p.row_ptr[x]) > (p.row_ptr[y + 1] - p.row_ptr[y]);
-    });
-    p.attn_order = order;
-    return;
-  }
-  // Workgroup b runs on XCD b % 8 (8 XCDs, each with its own L2).  Give each
-  // XCD one contiguous run of the head-major order, so the query tiles that
-  // are resident together on an XCD are spatial neighbours of one head and
-  // share most of their key tiles in that XCD's L2.
+  std::vector<int32_t> len(T);
+  for (int64_t t = 0; t < T; ++t) len[t] = p.row_ptr[t + 1] - p.row_ptr[t];
+  std::vector<int32_t> sorted(len);
+  std::nth_element(sorted.begin(), sorted.begin() + T / 2, sorted.end());
+  const int32_t median = T > 0 ? sorted[T / 2] : 0;
+  std::vector<int32_t> longs, rest;
+  for (int64_t t = 0; t < T; ++t) (len[t] > 2 * median + 2 ? longs : rest).push_back((int32_t)t);
+  std::stable_sort(longs.begin(), longs.end(), [&](int32_t x, int32_t y) { return len[x] > len[y]; });
+  // Workgroup b runs on XCD b % 8 (8 XCDs, each with its own L2).  The long
+  // rows take the first workgroups (spread over the XCDs); after them each
+  // XCD gets one contiguous run of the head-major order, so the query tiles
+  // that are resident together on an XCD are spatial neighbours of one head
+  // and share most of their key tiles in that XCD's L2.
   constexpr int64_t kXcds = 8;
-  const int64_t per = (T + kXcds - 1) / kXcds;
-  p.attn_order.assign(per * kXcds, -1);
+  const int64_t L = (int64_t)longs.size();
+  const int64_t L8 = (L + kXcds - 1) / kXcds * kXcds;   // the rest starts on XCD 0
+  const int64_t R = (int64_t)rest.size();
+  const int64_t per = (R + kXcds - 1) / kXcds;
+  p.attn_order.assign(L8 + per * kXcds, -1);
+  for (int64_t b = 0; b < L; ++b) p.attn_order[b] = longs[b];
   for (int64_t b = 0; b < per * kXcds; ++b) {
     const int64_t logical = (b % kXcds) * per + b / kXcds;
-    if (logical < T) p.attn_order[b] = order[logical];
+    if (logical < R) p.attn_order[L8 + b] = rest[logical];
   }
 }
 
