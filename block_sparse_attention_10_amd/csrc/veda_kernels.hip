@@ -268,12 +268,21 @@ __global__ void __launch_bounds__(kThreads) pool_kernel(DevPlan p, const uint16_
   }
 }
 
-// x_hat[t][d] = fp32(mean[d] + sum_e W[h][d][e] f[t][e]), e ascending, fp64.
-// Workgroup = (16-tile chunk of one head, head, tensor).  The chunk's
-// features sit in LDS as fp64 laid out [e][tile], so one 16-byte broadcast
-// read feeds two tiles; thread d streams W[h][d][:] in 16-byte chunks (the
-// next chunk in flight) and keeps the sums of kProjTiles / (256 / D) tiles.
-constexpr int kProjTiles = 16;
+// x_hat[t][d] = fp32(mean[d] + sum_e W[h][d][e] f[t][e]), e ascending, fp64
+// (a product of two fp32 values is exact in fp64, so fma = multiply + add).
+//
+// A register-blocked product.  Workgroup = (prj_tiles<D>() tiles of one head,
+// head, tensor); thread (tg, dg) keeps the sums of 4 tiles (4tg .. 4tg + 3)
+// x 4 channels (2dg, 2dg + 1, D/2 + 2dg, D/2 + 2dg + 1).  Both operands pass
+// through LDS as fp64 in chunks of kPrjE feature channels, W transposed to
+// [e][d] and the features to [e][tile], so per e a thread reads 32 bytes of
+// each (the W reads of a wave are contiguous, the feature reads broadcasts)
+// and does 16 FMAs.  The next chunk is loaded into registers while the
+// current one is summed.
+constexpr int kPrjE = 16;   // feature channels per LDS chunk
+
+template <int D>
+constexpr int prj_tiles() { return 4 * (kThreads / (D / 4)); }   // D = 128: 32 tiles, D = 64: 64
 
 template <int D>
 __global__ void __launch_bounds__(kThreads) project_kernel(DevPlan p, const float* __restrict__ wq,
@@ -282,80 +291,89 @@ __global__ void __launch_bounds__(kThreads) project_kernel(DevPlan p, const floa
                                                           const float* __restrict__ feat_k, float* __restrict__ hat_q,
                                                           float* __restrict__ hat_k) {
   constexpr int E = 3 * D;
-  constexpr int G = kThreads / D;           // tile groups
-  constexpr int TPT = kProjTiles / G;       // tiles per thread
-  static_assert(TPT % 2 == 0, "pairs of tiles per LDS read");
-  __shared__ __attribute__((aligned(16))) double f[E][kProjTiles];
-  const int h = blockIdx.y;
-  const DevShape& sh = p.shape[p.head_shape[h]];
-  const int n = sh.num_tiles;
-  const int i0 = blockIdx.x * kProjTiles;
+  constexpr int NDG = D / 4;                        // channel groups = threads per tile group
+  constexpr int TB = prj_tiles<D>();                // tiles per workgroup
+  constexpr int P4 = kPrjE / 4;                     // 16-byte pieces per chunk row
+  constexpr int WP = D * P4 / kThreads;             // W pieces per thread per chunk
+  constexpr int FP = TB * P4;                       // feature pieces per chunk (at most one per thread)
+  static_assert(E % kPrjE == 0 && WP >= 1 && FP <= kThreads, "chunking");
+  __shared__ __attribute__((aligned(16))) double ws[kPrjE][D];
+  __shared__ __attribute__((aligned(16))) double fs[kPrjE][TB];
+  const int h = blockIdx.y, y = blockIdx.z;
+  const int n = p.shape[p.head_shape[h]].num_tiles;
+  const int i0 = (int)blockIdx.x * TB;
   if (i0 >= n) return;
-  const int cnt = min(kProjTiles, n - i0);
-  const float* W = (blockIdx.z ? wk : wq) + (int64_t)h * D * E;
-  const float* feat = blockIdx.z ? feat_k : feat_q;
-  float* hat = blockIdx.z ? hat_k : hat_q;
+  const int cnt = min(TB, n - i0);
   const int64_t t0 = p.head_tile_off[h] + i0;
-  {   // features of the chunk's tiles, 16-byte loads all in flight together
-    constexpr int V4 = kProjTiles * E / 4 / kThreads;
-    float4 buf[V4];
+  const float* W = (y ? wk : wq) + (int64_t)h * D * E;
+  const float* feat = y ? feat_k : feat_q;
+  float* hat = y ? hat_k : hat_q;
+  const int tid = threadIdx.x, dg = tid % NDG, tg = tid / NDG;
+  const int chn[4] = {2 * dg, 2 * dg + 1, D / 2 + 2 * dg, D / 2 + 2 * dg + 1};
+  // the residual: the tiles' means (features 0 .. D-1)
+  double acc[4][4];
 #pragma unroll
-    for (int u = 0; u < V4; ++u) {
-      const int q4 = u * kThreads + threadIdx.x;
-      const int r = (4 * q4) / E;
-      buf[u] = r < cnt ? *reinterpret_cast<const float4*>(feat + (t0 + r) * E + (4 * q4) % E)
-                       : float4{0.f, 0.f, 0.f, 0.f};
-    }
+  for (int a = 0; a < 4; ++a) {
+    const int64_t row = t0 + min(4 * tg + a, cnt - 1);
 #pragma unroll
-    for (int u = 0; u < V4; ++u) {
-      const int q4 = u * kThreads + threadIdx.x;
-      const int r = (4 * q4) / E, e = (4 * q4) % E;
-      f[e + 0][r] = (double)buf[u].x;
-      f[e + 1][r] = (double)buf[u].y;
-      f[e + 2][r] = (double)buf[u].z;
-      f[e + 3][r] = (double)buf[u].w;
-    }
+    for (int b = 0; b < 4; ++b) acc[a][b] = (double)feat[row * E + chn[b]];
   }
-  __syncthreads();
-  const int d = threadIdx.x % D, grp = threadIdx.x / D;
-  double acc[TPT];
+  // piece q of W: row d = q / P4 (4 lanes read 64 contiguous bytes of a row)
+  float4 wb[WP], fb = float4{0.f, 0.f, 0.f, 0.f};
+  auto load = [&](int c0) {
 #pragma unroll
-  for (int u = 0; u < TPT; ++u) acc[u] = f[d][grp * TPT + u];
-  // W[h][d][:] streamed in 16-float chunks, the next chunk in flight while
-  // the current one is used; the sum order stays e = 0, 1, ..., 3D-1.
-  const float4* wr = reinterpret_cast<const float4*>(W + (int64_t)d * E);
-  float4 cur[4], nxt[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) cur[u] = wr[u];
+    for (int r = 0; r < WP; ++r) {
+      const int q = r * kThreads + tid;
+      wb[r] = *reinterpret_cast<const float4*>(W + (int64_t)(q / P4) * E + c0 + 4 * (q % P4));
+    }
+    if (tid < FP) {
+      const int tl = tid / P4;
+      fb = tl < cnt ? *reinterpret_cast<const float4*>(feat + (t0 + tl) * E + c0 + 4 * (tid % P4))
+                    : float4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  load(0);
 #pragma unroll 1
-  for (int e0 = 0; e0 < E; e0 += 16) {
-    if (e0 + 16 < E) {
+  for (int c0 = 0; c0 < E; c0 += kPrjE) {
+    __syncthreads();   // every thread is done with the previous chunk
 #pragma unroll
-      for (int u = 0; u < 4; ++u) nxt[u] = wr[(e0 + 16) / 4 + u];
+    for (int r = 0; r < WP; ++r) {
+      const int q = r * kThreads + tid;
+      const int d = q / P4, e = 4 * (q % P4);
+      ws[e][d] = (double)wb[r].x;
+      ws[e + 1][d] = (double)wb[r].y;
+      ws[e + 2][d] = (double)wb[r].z;
+      ws[e + 3][d] = (double)wb[r].w;
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float wv[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int e = e0 + 4 * u + c;
-        const double wd = (double)wv[c];
-        const double2* fe = reinterpret_cast<const double2*>(&f[e][grp * TPT]);
-#pragma unroll
-        for (int tt = 0; tt < TPT / 2; ++tt) {
-          const double2 fv = fe[tt];
-          acc[2 * tt] = fma(wd, fv.x, acc[2 * tt]);
-          acc[2 * tt + 1] = fma(wd, fv.y, acc[2 * tt + 1]);
-        }
-      }
+    if (tid < FP) {
+      const int tl = tid / P4, e = 4 * (tid % P4);
+      fs[e][tl] = (double)fb.x;
+      fs[e + 1][tl] = (double)fb.y;
+      fs[e + 2][tl] = (double)fb.z;
+      fs[e + 3][tl] = (double)fb.w;
     }
+    __syncthreads();
+    if (c0 + kPrjE < E) load(c0 + kPrjE);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+    for (int e = 0; e < kPrjE; ++e) {
+      const double2 f01 = *reinterpret_cast<const double2*>(&fs[e][4 * tg]);
+      const double2 f23 = *reinterpret_cast<const double2*>(&fs[e][4 * tg + 2]);
+      const double2 w01 = *reinterpret_cast<const double2*>(&ws[e][2 * dg]);
+      const double2 w23 = *reinterpret_cast<const double2*>(&ws[e][D / 2 + 2 * dg]);
+      const double fv[4] = {f01.x, f01.y, f23.x, f23.y};
+      const double wv[4] = {w01.x, w01.y, w23.x, w23.y};
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = fma(wv[b], fv[a], acc[a][b]);
+    }
   }
 #pragma unroll
-  for (int u = 0; u < TPT; ++u) {
-    const int r = grp * TPT + u;
-    if (r < cnt) hat[(t0 + r) * D + d] = (float)acc[u];
+  for (int a = 0; a < 4; ++a) {
+    if (4 * tg + a >= cnt) continue;
+    float* out = hat + (t0 + 4 * tg + a) * D;
+    *reinterpret_cast<float2*>(out + 2 * dg) = float2{(float)acc[a][0], (float)acc[a][1]};
+    *reinterpret_cast<float2*>(out + D / 2 + 2 * dg) = float2{(float)acc[a][2], (float)acc[a][3]};
   }
 }
 
@@ -2163,7 +2181,8 @@ hipError_t launch_score_pooled(const DevPlan& p, const float* wq, const float* w
   float* hat_k = hat_q + T * D;
   int maxn = 0;
   for (int g = 0; g < p.num_shapes; ++g) maxn = maxn > p.shape[g].num_tiles ? maxn : p.shape[g].num_tiles;
-  const dim3 gproj((unsigned)((maxn + kProjTiles - 1) / kProjTiles), (unsigned)p.num_heads, 2);
+  const int tb = D == 128 ? prj_tiles<128>() : prj_tiles<64>();
+  const dim3 gproj((unsigned)((maxn + tb - 1) / tb), (unsigned)p.num_heads, 2);
   const dim3 gscore((unsigned)((maxn + 63) / 64), (unsigned)((maxn + 63) / 64), (unsigned)p.num_heads);
   if (D == 128) {
     hipLaunchKernelGGL(project_kernel<128>, gproj, dim3(kThreads), 0, s, p, wq, wk, feat_q, feat_k, hat_q, hat_k);
