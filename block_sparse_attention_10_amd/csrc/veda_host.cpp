@@ -717,6 +717,9 @@ veda_status veda_dense_lse_heat(const veda_plan* p, const void* q, const void* k
   if (lse && (st = check_ptr(lse, "lse"))) return st;
   if (p->budget_mode != VEDA_BUDGET_ALL)
     return fail(VEDA_ERR_UNSUPPORTED, "the fused dense LSE and heat needs a plan with budget mode ALL");
+  if (heat == workspace || (lse && ((const void*)lse == workspace || lse == heat)) || heat == q || heat == k ||
+      (lse && ((const void*)lse == q || (const void*)lse == k)))
+    return fail(VEDA_ERR_INVALID_ARG, "lse, heat and workspace must be distinct from each other and the inputs");
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
     return fail(VEDA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if ((int64_t)workspace_bytes < p->info.heat_workspace_bytes)
@@ -793,6 +796,16 @@ veda_status veda_block_sparse_attn_bwd(const veda_plan* p, const void* q, const 
     return st;
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
     return fail(VEDA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  {
+    const void* ins[7] = {q, k, v, o, d_o, lse, workspace};
+    const void* outs[3] = {dq, dk, dv};
+    for (int a = 0; a < 3; ++a) {
+      for (int b = 0; b < 7; ++b)
+        if (outs[a] == ins[b]) return fail(VEDA_ERR_INVALID_ARG, "dq, dk or dv aliases an input or the workspace");
+      for (int b = a + 1; b < 3; ++b)
+        if (outs[a] == outs[b]) return fail(VEDA_ERR_INVALID_ARG, "dq, dk and dv must be distinct buffers");
+    }
+  }
   if ((int64_t)workspace_bytes < p->info.bwd_workspace_bytes)
     return fail(VEDA_ERR_WORKSPACE, "backward needs %lld workspace bytes", (long long)p->info.bwd_workspace_bytes);
   return launched(launch_attn_bwd(p->dev, q, k, v, o, d_o, lse, row_ptr, col_idx, col_ptr, row_idx, softmax_scale, dq,

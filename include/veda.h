@@ -298,7 +298,9 @@ veda_status veda_block_heat(const veda_plan* plan, const void* q, const void* k,
  *   workspace: device scratch of at least heat_workspace_bytes (the plan's
  *              nnz x 128 x 4 bytes: one fp32 per block and query slot),
  *              16-byte aligned; its contents on entry do not matter.
- * Errors: VEDA_ERR_WORKSPACE if workspace_bytes is too small. */
+ * Errors: VEDA_ERR_WORKSPACE if workspace_bytes is too small;
+ * VEDA_ERR_INVALID_ARG if lse, heat and workspace are not three different
+ * buffers or one of them is q or k. */
 veda_status veda_dense_lse_heat(const veda_plan* plan, const void* q, const void* k,
                                 const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
                                 float* lse, float* heat, void* workspace, size_t workspace_bytes,
@@ -369,7 +371,10 @@ veda_status veda_mask_transpose(const veda_plan* plan, const int32_t* row_ptr, c
  *   row_ptr, col_idx: the forward's CSR; col_ptr, row_idx: its transpose
  *             (veda_mask_transpose)
  *   dq, dk, dv: device permuted bf16 [R, D]; rows of padding slots are zero
- *   workspace: device, bwd_workspace_bytes (contents overwritten) */
+ *   workspace: device, bwd_workspace_bytes (contents overwritten)
+ * Errors: VEDA_ERR_INVALID_ARG if dq, dk, dv are not three different buffers
+ * or one of them is an input or the workspace; VEDA_ERR_WORKSPACE if
+ * workspace_bytes is too small. */
 veda_status veda_block_sparse_attn_bwd(const veda_plan* plan, const void* q, const void* k, const void* v,
                                        const void* o, const void* d_o, const float* lse, const int32_t* row_ptr,
                                        const int32_t* col_idx, const int32_t* col_ptr, const int32_t* row_idx,

@@ -804,5 +804,13 @@ def test_error_paths_on_device():
                               buf.data_ptr(), short, None) == 4
     assert lib.veda_output_error(plan.handle, buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(),
                                  short, None) == 4
+    # the backward refuses an output that aliases an input (INVALID_ARG), before any launch
+    p_ = buf.data_ptr()
+    assert lib.veda_block_sparse_attn_bwd(plan.handle, p_, p_ + 4096, p_ + 8192, p_ + 12288, p_ + 16384,
+                                          p_ + 20480, p_, p_, p_, p_, ctypes.c_float(0.125), p_, p_ + 24576,
+                                          p_ + 28672, p_ + 32768, 1 << 40, None) == 1
+    assert lib.veda_block_sparse_attn_bwd(plan.handle, p_, p_ + 4096, p_ + 8192, p_ + 12288, p_ + 16384,
+                                          p_ + 20480, p_, p_, p_, p_, ctypes.c_float(0.125), p_ + 24576,
+                                          p_ + 24576, p_ + 28672, p_ + 32768, 1 << 40, None) == 1
     with pytest.raises(vb.VedaError):
         vb.veda_plan_upload(plan.handle, plan.tables)   # uploaded twice
