@@ -271,18 +271,24 @@ __global__ void __launch_bounds__(kThreads) pool_kernel(DevPlan p, const uint16_
 // x_hat[t][d] = fp32(mean[d] + sum_e W[h][d][e] f[t][e]), e ascending, fp64
 // (a product of two fp32 values is exact in fp64, so fma = multiply + add).
 //
-// A register-blocked product.  Workgroup = (prj_tiles<D>() tiles of one head,
-// head, tensor); thread (tg, dg) keeps the sums of 4 tiles (4tg .. 4tg + 3)
-// x 4 channels (2dg, 2dg + 1, D/2 + 2dg, D/2 + 2dg + 1).  Both operands pass
-// through LDS as fp64 in chunks of kPrjE feature channels, W transposed to
-// [e][d] and the features to [e][tile], so per e a thread reads 32 bytes of
-// each (the W reads of a wave are contiguous, the feature reads broadcasts)
-// and does 16 FMAs.  The next chunk is loaded into registers while the
-// current one is summed.
-constexpr int kPrjE = 16;   // feature channels per LDS chunk
-
-template <int D>
-constexpr int prj_tiles() { return 4 * (kThreads / (D / 4)); }   // D = 128: 32 tiles, D = 64: 64
+// On the fp64 matrix cores: v_mfma_f64_16x16x4_f64 adds its four products
+// to the accumulator one after another in k order, each rounded as an fma
+// (checked on gfx950 against sequential fmas over 128-step chains, all
+// 65,536 outputs bit-equal), so a chain of them over e = 0, 1, ..., 3D-1 with
+// the accumulator starting at the mean is exactly the sequential sum.
+// Operand layout of that instruction: A (16 x 4) lane l holds A[l % 16][l / 16],
+// B (4 x 16) lane l holds B[l / 16][l % 16], the accumulator's element r of
+// lane l is D[l / 16 + 4r][l % 16].  Here rows are tiles, k runs over feature
+// channels e and columns are output channels d.
+// Workgroup = (16 tiles of one head, head, tensor), 4 waves; wave w owns the
+// D/4 output channels from w D/4 on (D/64 16x16 blocks).  W (transposed to
+// [e][d]) and the features ([e][tile]) pass through LDS as fp64 in chunks of
+// kPrjE channels; the next chunk is loaded into registers while the current
+// one is used.  Row strides are odd numbers of doubles, so the transposing
+// LDS writes spread over the banks.
+typedef __attribute__((ext_vector_type(4))) double f64x4;
+constexpr int kPrjE = 32;    // feature channels per LDS chunk
+constexpr int kPrjTB = 16;   // tiles per workgroup
 
 template <int D>
 __global__ void __launch_bounds__(kThreads) project_kernel(DevPlan p, const float* __restrict__ wq,
@@ -291,34 +297,36 @@ __global__ void __launch_bounds__(kThreads) project_kernel(DevPlan p, const floa
                                                           const float* __restrict__ feat_k, float* __restrict__ hat_q,
                                                           float* __restrict__ hat_k) {
   constexpr int E = 3 * D;
-  constexpr int NDG = D / 4;                        // channel groups = threads per tile group
-  constexpr int TB = prj_tiles<D>();                // tiles per workgroup
-  constexpr int P4 = kPrjE / 4;                     // 16-byte pieces per chunk row
-  constexpr int WP = D * P4 / kThreads;             // W pieces per thread per chunk
-  constexpr int FP = TB * P4;                       // feature pieces per chunk (at most one per thread)
-  static_assert(E % kPrjE == 0 && WP >= 1 && FP <= kThreads, "chunking");
-  __shared__ __attribute__((aligned(16))) double ws[kPrjE][D];
-  __shared__ __attribute__((aligned(16))) double fs[kPrjE][TB];
+  constexpr int NB = D / 64;               // 16-channel blocks per wave
+  constexpr int WS = D + 1;                // doubles per LDS row of W^T
+  constexpr int FS = kPrjTB + 1;           // doubles per LDS row of the features
+  constexpr int P4 = kPrjE / 4;            // 16-byte pieces per chunk row
+  constexpr int WP = D * P4 / kThreads;    // W pieces per thread per chunk
+  constexpr int FP = kPrjTB * P4;          // feature pieces per chunk (one per thread at most)
+  static_assert(E % kPrjE == 0 && WP >= 1 && FP <= kThreads && NB >= 1, "chunking");
+  __shared__ double ws[kPrjE * WS];
+  __shared__ double fs[kPrjE * FS];
   const int h = blockIdx.y, y = blockIdx.z;
   const int n = p.shape[p.head_shape[h]].num_tiles;
-  const int i0 = (int)blockIdx.x * TB;
+  const int i0 = (int)blockIdx.x * kPrjTB;
   if (i0 >= n) return;
-  const int cnt = min(TB, n - i0);
+  const int cnt = min(kPrjTB, n - i0);
   const int64_t t0 = p.head_tile_off[h] + i0;
   const float* W = (y ? wk : wq) + (int64_t)h * D * E;
   const float* feat = y ? feat_k : feat_q;
   float* hat = y ? hat_k : hat_q;
-  const int tid = threadIdx.x, dg = tid % NDG, tg = tid / NDG;
-  const int chn[4] = {2 * dg, 2 * dg + 1, D / 2 + 2 * dg, D / 2 + 2 * dg + 1};
-  // the residual: the tiles' means (features 0 .. D-1)
-  double acc[4][4];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int lr = lane & 15, lk = lane >> 4;
+  const int dw = wave * (D / 4);
+  // the accumulators start at the tiles' means (features 0 .. D-1)
+  f64x4 acc[NB];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int64_t row = t0 + min(4 * tg + a, cnt - 1);
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = (double)feat[row * E + chn[b]];
-  }
-  // piece q of W: row d = q / P4 (4 lanes read 64 contiguous bytes of a row)
+    for (int r = 0; r < 4; ++r)
+      acc[b][r] = (double)feat[(t0 + min(lk + 4 * r, cnt - 1)) * E + dw + 16 * b + lr];
+  // piece q of W: row d = q / P4, channels 4 (q % P4) .. + 3 of the chunk
+  // (P4 lanes read one row's chunk, 128 contiguous bytes)
   float4 wb[WP], fb = float4{0.f, 0.f, 0.f, 0.f};
   auto load = [&](int c0) {
 #pragma unroll
@@ -335,46 +343,39 @@ __global__ void __launch_bounds__(kThreads) project_kernel(DevPlan p, const floa
   load(0);
 #pragma unroll 1
   for (int c0 = 0; c0 < E; c0 += kPrjE) {
-    __syncthreads();   // every thread is done with the previous chunk
+    __syncthreads();   // every wave is done with the previous chunk
 #pragma unroll
     for (int r = 0; r < WP; ++r) {
       const int q = r * kThreads + tid;
       const int d = q / P4, e = 4 * (q % P4);
-      ws[e][d] = (double)wb[r].x;
-      ws[e + 1][d] = (double)wb[r].y;
-      ws[e + 2][d] = (double)wb[r].z;
-      ws[e + 3][d] = (double)wb[r].w;
+      ws[(e + 0) * WS + d] = (double)wb[r].x;
+      ws[(e + 1) * WS + d] = (double)wb[r].y;
+      ws[(e + 2) * WS + d] = (double)wb[r].z;
+      ws[(e + 3) * WS + d] = (double)wb[r].w;
     }
     if (tid < FP) {
       const int tl = tid / P4, e = 4 * (tid % P4);
-      fs[e][tl] = (double)fb.x;
-      fs[e + 1][tl] = (double)fb.y;
-      fs[e + 2][tl] = (double)fb.z;
-      fs[e + 3][tl] = (double)fb.w;
+      fs[(e + 0) * FS + tl] = (double)fb.x;
+      fs[(e + 1) * FS + tl] = (double)fb.y;
+      fs[(e + 2) * FS + tl] = (double)fb.z;
+      fs[(e + 3) * FS + tl] = (double)fb.w;
     }
     __syncthreads();
     if (c0 + kPrjE < E) load(c0 + kPrjE);
 #pragma unroll
-    for (int e = 0; e < kPrjE; ++e) {
-      const double2 f01 = *reinterpret_cast<const double2*>(&fs[e][4 * tg]);
-      const double2 f23 = *reinterpret_cast<const double2*>(&fs[e][4 * tg + 2]);
-      const double2 w01 = *reinterpret_cast<const double2*>(&ws[e][2 * dg]);
-      const double2 w23 = *reinterpret_cast<const double2*>(&ws[e][D / 2 + 2 * dg]);
-      const double fv[4] = {f01.x, f01.y, f23.x, f23.y};
-      const double wv[4] = {w01.x, w01.y, w23.x, w23.y};
+    for (int s4 = 0; s4 < kPrjE / 4; ++s4) {
+      const int e = 4 * s4 + lk;
+      const double a = fs[e * FS + lr];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fma(wv[b], fv[a], acc[a][b]);
+      for (int b = 0; b < NB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, ws[e * WS + dw + 16 * b + lr], acc[b], 0, 0, 0);
     }
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    if (4 * tg + a >= cnt) continue;
-    float* out = hat + (t0 + 4 * tg + a) * D;
-    *reinterpret_cast<float2*>(out + 2 * dg) = float2{(float)acc[a][0], (float)acc[a][1]};
-    *reinterpret_cast<float2*>(out + D / 2 + 2 * dg) = float2{(float)acc[a][2], (float)acc[a][3]};
-  }
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (lk + 4 * r < cnt) hat[(t0 + lk + 4 * r) * D + dw + 16 * b + lr] = (float)acc[b][r];
 }
 
 // s[i][j] = fp32(sum_d q_hat_i[d] k_hat_j[d]), d ascending in fp64; 64x64
@@ -2181,8 +2182,7 @@ hipError_t launch_score_pooled(const DevPlan& p, const float* wq, const float* w
   float* hat_k = hat_q + T * D;
   int maxn = 0;
   for (int g = 0; g < p.num_shapes; ++g) maxn = maxn > p.shape[g].num_tiles ? maxn : p.shape[g].num_tiles;
-  const int tb = D == 128 ? prj_tiles<128>() : prj_tiles<64>();
-  const dim3 gproj((unsigned)((maxn + tb - 1) / tb), (unsigned)p.num_heads, 2);
+  const dim3 gproj((unsigned)((maxn + kPrjTB - 1) / kPrjTB), (unsigned)p.num_heads, 2);
   const dim3 gscore((unsigned)((maxn + 63) / 64), (unsigned)((maxn + 63) / 64), (unsigned)p.num_heads);
   if (D == 128) {
     hipLaunchKernelGGL(project_kernel<128>, gproj, dim3(kThreads), 0, s, p, wq, wk, feat_q, feat_k, hat_q, hat_k);
