@@ -378,25 +378,30 @@ __global__ void __launch_bounds__(kThreads) project_kernel(DevPlan p, const floa
       if (lk + 4 * r < cnt) hat[(t0 + lk + 4 * r) * D + dw + 16 * b + lr] = (float)acc[b][r];
 }
 
-// s[i][j] = fp32(sum_d q_hat_i[d] k_hat_j[d]), d ascending in fp64; 64x64
-// output tile per workgroup, 4x4 per thread.  q_hat and k_hat pass through
-// LDS 32 channels at a time, already widened to fp64 ([channel][row]), so
-// the inner loop is two 32-byte reads and 16 FMAs per channel.
+// s[i][j] = fp32(sum_d q_hat_i[d] k_hat_j[d]), d ascending in fp64, -0
+// written as +0.  On the fp64 matrix cores like the projection: a chain of
+// v_mfma_f64_16x16x4_f64 from a zero accumulator over d = 0, 1, ..., D-1 is
+// the sequential sum.  Workgroup = 64 x 64 scores of one head; wave w owns
+// query rows 16w .. 16w + 15 against all 64 key columns (four 16x16 blocks
+// sharing the A operand of each step).  q_hat and k_hat pass through LDS
+// kScoreChunk channels at a time, widened to fp64 and transposed to
+// [channel][row] with an odd row stride.
 constexpr int kScoreChunk = 32;
 
 template <int D>
 __global__ void __launch_bounds__(kThreads) score_kernel(DevPlan p, const float* __restrict__ hat_q,
                                                         const float* __restrict__ hat_k, float* __restrict__ scores) {
   static_assert(D % kScoreChunk == 0, "whole channel chunks");
-  __shared__ __attribute__((aligned(16))) double qs[kScoreChunk][64];
-  __shared__ __attribute__((aligned(16))) double ks[kScoreChunk][64];
+  constexpr int RS = 64 + 1;   // doubles per LDS row
+  __shared__ double qs[kScoreChunk * RS];
+  __shared__ double ks[kScoreChunk * RS];
   const int h = blockIdx.z;
   const DevShape& sh = p.shape[p.head_shape[h]];
   const int n = sh.num_tiles;
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
   if (i0 >= n || j0 >= n) return;
   const int64_t t0 = p.head_tile_off[h];
-  const int ti = threadIdx.x / 16, tj = threadIdx.x % 16;
+  const int lane = lane_id(), wave = threadIdx.x >> 6, lr = lane & 15, lk = lane >> 4;
   // staging: thread -> (row r, 8 consecutive channels) of the chunk; rows
   // past the head's last tile read the last tile (in bounds) and are zeroed
   constexpr int PER_ROW = kScoreChunk / 8;                 // threads per row
@@ -405,50 +410,42 @@ __global__ void __launch_bounds__(kThreads) score_kernel(DevPlan p, const float*
   const bool qin = i0 + sr < n, kin = j0 + sr < n;
   const float* qrow = hat_q + (t0 + min(i0 + sr, n - 1)) * D + sc;
   const float* krow = hat_k + (t0 + min(j0 + sr, n - 1)) * D + sc;
-  double acc[4][4];
+  f64x4 acc[4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  for (int b = 0; b < 4; ++b) acc[b] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll 1
   for (int c0 = 0; c0 < D; c0 += kScoreChunk) {
     const float4 q0 = *reinterpret_cast<const float4*>(qrow + c0);
     const float4 q1 = *reinterpret_cast<const float4*>(qrow + c0 + 4);
     const float4 k0 = *reinterpret_cast<const float4*>(krow + c0);
     const float4 k1 = *reinterpret_cast<const float4*>(krow + c0 + 4);
-    if (c0 > 0) __syncthreads();       // every thread is done with the previous chunk
+    if (c0 > 0) __syncthreads();       // every wave is done with the previous chunk
     const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
     const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      qs[sc + u][sr] = qin ? (double)qv[u] : 0.0;
-      ks[sc + u][sr] = kin ? (double)kv[u] : 0.0;
+      qs[(sc + u) * RS + sr] = qin ? (double)qv[u] : 0.0;
+      ks[(sc + u) * RS + sr] = kin ? (double)kv[u] : 0.0;
     }
     __syncthreads();
-#pragma unroll 4
-    for (int d = 0; d < kScoreChunk; ++d) {
-      const double2 qa0 = *reinterpret_cast<const double2*>(&qs[d][4 * ti]);
-      const double2 qa1 = *reinterpret_cast<const double2*>(&qs[d][4 * ti + 2]);
-      const double2 kb0 = *reinterpret_cast<const double2*>(&ks[d][4 * tj]);
-      const double2 kb1 = *reinterpret_cast<const double2*>(&ks[d][4 * tj + 2]);
-      const double qd[4] = {qa0.x, qa0.y, qa1.x, qa1.y};
-      const double kd[4] = {kb0.x, kb0.y, kb1.x, kb1.y};
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+    for (int s4 = 0; s4 < kScoreChunk / 4; ++s4) {
+      const int d = 4 * s4 + lk;
+      const double a = qs[d * RS + 16 * wave + lr];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fma(qd[a], kd[b], acc[a][b]);
+      for (int b = 0; b < 4; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, ks[d * RS + 16 * b + lr], acc[b], 0, 0, 0);
     }
   }
   float* out = scores + p.head_pair_off[h];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = i0 + 4 * ti + a;
-    if (i >= n) continue;
+  for (int b = 0; b < 4; ++b) {
+    const int j = j0 + 16 * b + lr;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int j = j0 + 4 * tj + b;
-      if (j >= n) continue;
-      uint32_t u = __float_as_uint((float)acc[a][b]);
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + 16 * wave + lk + 4 * r;
+      if (i >= n || j >= n) continue;
+      uint32_t u = __float_as_uint((float)acc[b][r]);
       if ((u & 0x7fffffffu) == 0u) u = 0u;  // -0 -> +0
       out[(int64_t)i * n + j] = __uint_as_float(u);
     }
