@@ -512,6 +512,76 @@ def test_config2_separate_calls():
     check_attention(w, inp, g, op, qp, kp, sel)
 
 
+def _order_sensitive_inputs(w):
+    """Inputs whose projections depend on the order of the fp64 sum: channel
+    5 of Q and channel 9 of K are constant (so a tile's mean, max and min of
+    that channel are equal), and W gives the mean column +2^40 and the min
+    column -2^40 of that channel.  Summed in ascending e, the big term enters
+    at e = c, every term up to e = 2D + c is rounded against it (ulp 2^-12),
+    and it cancels exactly at e = 2D + c; another order rounds differently."""
+    inp = wl.make_inputs(w)
+    D = w.head_dim
+    inp["q"][:, :, 5] = 0.75
+    inp["k"][:, :, 9] = -1.25
+    for key, c in (("w_q", 5), ("w_k", 9)):
+        wt = inp[key].clone()
+        wt[:, :, c] = 2.0 ** 40
+        wt[:, :, 2 * D + c] = -(2.0 ** 40)
+        inp[key] = wt
+    return inp
+
+
+def _project_blocked(op, feats, w):
+    """The projection with each step's four products summed first (the
+    alternative order a matrix instruction could take), for the check that
+    the inputs above tell the orders apart."""
+    H, D, E = w.shape
+    out = np.zeros((op.total_tiles, D), dtype=np.float32)
+    for h in range(H):
+        t0, t1 = op.tile_offset[h], op.tile_offset[h + 1]
+        f = feats[t0:t1].astype(np.float64)
+        wh = w[h].astype(np.float64)
+        acc = f[:, 0:D].copy()
+        for e in range(0, E, 4):
+            p = [f[:, e + u:e + u + 1] * wh[:, e + u][None, :] for u in range(4)]
+            acc += (p[0] + p[1]) + (p[2] + p[3])
+        out[t0:t1] = acc.astype(np.float32)
+    return out
+
+
+def test_predictor_sums_follow_the_sequential_order():
+    """Projections and scores bit-exact against the oracle's ascending-order
+    fp64 sums on inputs where the summation order shows in the fp32 result."""
+    w = wl.workload(2)
+    inp = _order_sensitive_inputs(w)
+    op = vo.Plan.from_workload(w)
+    qn, kn = gp.f64(inp["q"]), gp.f64(inp["k"])
+    fq = vo.pool_tiles(op, vo.permute_forward(op, qn))
+    fk = vo.pool_tiles(op, vo.permute_forward(op, kn))
+    qh = vo.project(op, fq, inp["w_q"].numpy())
+    kh = vo.project(op, fk, inp["w_k"].numpy())
+    scores = vo.score_pairs(op, qh, kh)
+    # the inputs separate the orders: a blocked sum gives other fp32 values
+    assert np.count_nonzero(_project_blocked(op, fq, inp["w_q"].numpy()) != qh) > qh.size // 10
+    plan = vb.Plan.from_workload(w)
+    dev = "cuda"
+    q, k, v = (inp[x].to(dev).to(torch.bfloat16) for x in ("q", "k", "v"))
+    qp, kp, vt, ws = plan.empty_perm(), plan.empty_perm(), plan.empty_vt(), plan.empty_workspace()
+    sc = torch.empty(plan.info["total_pairs"], dtype=torch.float32, device=dev)
+    plan.permute_qkv(q, k, v, qp, kp, vt, ws)
+    plan.score_pooled(inp["w_q"].to(dev), inp["w_k"].to(dev), sc, ws)
+    torch.cuda.synchronize()
+    T, D = op.total_tiles, w.head_dim
+    wsh = ws.cpu().numpy()
+    hq = wsh[6 * T * D:7 * T * D].reshape(T, D)
+    hk = wsh[7 * T * D:8 * T * D].reshape(T, D)
+    assert np.array_equal(hq.view(np.uint32), qh.view(np.uint32))
+    assert np.array_equal(hk.view(np.uint32), kh.view(np.uint32))
+    sg = gp.split_scores(None, op, sc.cpu().numpy())
+    for h in range(w.num_heads):
+        assert np.array_equal(sg[h].view(np.uint32), scores[h].view(np.uint32)), "scores head %d" % h
+
+
 def test_fused_equals_separate_bitwise():
     w = wl.workload(3)
     inp = wl.make_inputs(w)
