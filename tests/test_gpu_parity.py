@@ -624,17 +624,6 @@ def test_permute_qk_only_and_side_stream_v(idx):
     assert e.value.status == 1                   # VEDA_ERR_INVALID_ARG: v without v_t
 
 
-def test_config5_packed_sampled_rows():
-    w = wl.workload(5)
-    inp = wl.make_inputs(w)
-    g = gp.gpu_path(w, inp)
-    op, qp, kp, sel = check_front(w, inp, g)
-    rng = np.random.default_rng(5)
-    rows = [(h, i) for h in (0, 23) for i in range(op.heads[h].num_tiles) if op.heads[h].tiles[i].segment == 2]
-    rows += [(int(h), int(i)) for h, i in zip(rng.integers(0, 24, 40), rng.integers(0, 248, 40))]
-    check_attention(w, inp, g, op, qp, kp, sel, rows=rows)
-
-
 def test_all_mask_equals_dense_attention():
     """The ALL budget through the same kernels is dense attention (library fp64 SDPA)."""
     w = wl.Workload(95, "dense_small", (wl.Segment(wl.VIDEO3D, (4, 10, 12), 0),), 2, 128, ((2, 8, 8),) * 2,
@@ -655,32 +644,6 @@ def test_deterministic_bitwise():
     b = gp.gpu_path(w, inp)
     for key in ("scores", "col_idx", "o_nat", "lse"):
         assert torch.equal(a[key], b[key]), key
-
-
-def test_heat_config5_sampled_heads():
-    """Block heat from the dense LSE of the all-blocks forward, against the
-    oracle's heat computed from its own dense LSE."""
-    w = wl.workload(5)
-    inp = wl.make_inputs(w)
-    g = gp.gpu_path(w, inp, budget_mode=wl.ALL_BLOCKS, dense_mask=False)
-    plan = g["plan"]
-    heat = torch.empty(plan.info["total_pairs"], dtype=torch.float32, device="cuda")
-    plan.heat(g["q_perm"], g["k_perm"], g["lse"], w.softmax_scale, heat)
-    torch.cuda.synchronize()
-    op = vo.Plan.from_workload(w)
-    qp = vo.permute_forward(op, gp.f64(inp["q"]))
-    kp = vo.permute_forward(op, gp.f64(inp["k"]))
-    hg = gp.split_scores(None, op, heat.cpu().numpy())
-    for h in (0, 13):
-        rows = [(h, i) for i in range(op.heads[h].num_tiles)]
-        _, L = vo.block_sparse_attention(op, qp, kp, kp, vo.all_blocks_selection(op), w.softmax_scale, rows=rows)
-        ref = vo.block_heat(op, qp, kp, L, w.softmax_scale, heads=[h])[h]
-        err = float(np.max(np.abs(hg[h] - ref)))
-        print("heat head %d max_abs %.3e" % (h, err), flush=True)
-        assert err <= gp.HEAT_ABS
-    sums = heat.view(-1).cpu().numpy()
-    for h in range(w.num_heads):
-        assert np.max(np.abs(hg[h].sum(axis=1) - 1.0)) <= 1e-3
 
 
 def _late_logits(w, inp):
@@ -752,31 +715,6 @@ def test_dense_lse_heat(kind):
             assert np.max(np.abs(hg[h] - h2[h])) <= gp.HEAT_ABS, (w.name, h)
 
 
-def test_dense_lse_heat_config5_sampled_heads():
-    """The fused dense LSE and heat at full size (packed sequence, the bench's
-    heat step): LSE bitwise equal to the all-blocks attention's, heat against
-    the oracle on two heads, every heat row summing to 1."""
-    w = wl.workload(5)
-    inp = wl.make_inputs(w)
-    g = gp.gpu_path(w, inp, budget_mode=wl.ALL_BLOCKS, dense_mask=False)
-    lse, heat = _dense_lse_heat(g, w)
-    a, b = g["lse"].cpu().numpy(), lse.cpu().numpy()
-    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
-    op = vo.Plan.from_workload(w)
-    qp = vo.permute_forward(op, gp.f64(inp["q"]))
-    kp = vo.permute_forward(op, gp.f64(inp["k"]))
-    hg = gp.split_scores(None, op, heat.cpu().numpy())
-    for h in (0, 13):
-        rows = [(h, i) for i in range(op.heads[h].num_tiles)]
-        _, L = vo.block_sparse_attention(op, qp, kp, kp, vo.all_blocks_selection(op), w.softmax_scale, rows=rows)
-        ref = vo.block_heat(op, qp, kp, L, w.softmax_scale, heads=[h])[h]
-        err = float(np.max(np.abs(hg[h] - ref)))
-        print("fused heat head %d max_abs %.3e" % (h, err), flush=True)
-        assert err <= gp.HEAT_ABS
-    for h in range(w.num_heads):
-        assert np.max(np.abs(hg[h].sum(axis=1) - 1.0)) <= 1e-3
-
-
 def test_dense_lse_heat_errors():
     """The fused call refuses a plan that is not all-blocks (UNSUPPORTED) and a
     short workspace (WORKSPACE) on the host, before any launch."""
@@ -796,58 +734,6 @@ def test_dense_lse_heat_errors():
         vb.veda_dense_lse_heat(sparse.handle, g["q_perm"], g["k_perm"], g["row_ptr"], g["col_idx"],
                                w.softmax_scale, g["lse"], heat, ws)
     assert e.value.status == 3          # VEDA_ERR_UNSUPPORTED
-
-
-def test_config4_long_clip_sampled():
-    """Full-size config 4 (two tile shapes): permutation bit-exact on all
-    heads, scores and CSR bit-exact on sampled heads, attention on sampled
-    query tiles."""
-    w = wl.workload(4)
-    inp = wl.make_inputs(w)
-    g = gp.gpu_path(w, inp, dense_mask=False)
-    op = vo.Plan.from_workload(w)
-    assert np.array_equal(gp.i16(g["q_perm"]), vo.permute_forward(op, gp.i16(inp["q"])))
-    heads = [0, 11, 12, 23]
-    sub = vo.Plan(w.segments, len(heads), w.head_dim, [w.tile_shapes[h] for h in heads], w.budget_mode,
-                  w.keep_num, w.keep_den, w.fixed_k)
-    qn = gp.f64(inp["q"])[:, heads]
-    kn = gp.f64(inp["k"])[:, heads]
-    vn = gp.f64(inp["v"])[:, heads]
-    qp, kp, vp = vo.permute_forward(sub, qn), vo.permute_forward(sub, kn), vo.permute_forward(sub, vn)
-    qh = vo.project(sub, vo.pool_tiles(sub, qp), inp["w_q"].numpy()[heads])
-    kh = vo.project(sub, vo.pool_tiles(sub, kp), inp["w_k"].numpy()[heads])
-    scores = vo.score_pairs(sub, qh, kh)
-    plan = g["plan"]
-    flat = g["scores"].cpu().numpy()
-    rp_g = g["row_ptr"].cpu().numpy()
-    col_g = g["col_idx"].cpu().numpy()
-    for a, h in enumerate(heads):
-        n, r0, t0, p0 = vb.veda_plan_head(plan.handle, h)
-        assert np.array_equal(flat[p0:p0 + n * n].reshape(n, n).view(np.uint32), scores[a].view(np.uint32))
-    rng = np.random.default_rng(4)
-    sel_rows = {a: sorted(set(rng.integers(0, sub.heads[a].num_tiles, 6).tolist())) for a in range(len(heads))}
-    sel = vo.select_blocks(sub, scores)
-    rows = []
-    for a, h in enumerate(heads):
-        n, r0, t0, p0 = vb.veda_plan_head(plan.handle, h)
-        for i in range(n):
-            assert np.array_equal(col_g[rp_g[t0 + i]:rp_g[t0 + i + 1]], sel[a][i])
-        rows += [(a, i) for i in sel_rows[a]]
-    O, L = vo.block_sparse_attention(sub, qp, kp, vp, sel, w.softmax_scale, rows=rows)
-    o_nat = gp.f64(g["o_nat"])
-    lse_gpu = g["lse"].cpu().numpy()
-    for a, i in rows:
-        h = heads[a]
-        n, r0, t0, p0 = vb.veda_plan_head(plan.handle, h)
-        nv = sub.heads[a].tiles[i].valid
-        ref = O[sub.row_offset[a] + 128 * i: sub.row_offset[a] + 128 * i + nv]
-        toks = sub.heads[a].perm()[128 * i: 128 * i + nv]
-        got = o_nat[toks, h]
-        assert np.max(np.abs(got - ref)) <= gp.MAX_ABS
-        assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= gp.REL_L2
-        lref = L[sub.row_offset[a] + 128 * i: sub.row_offset[a] + 128 * i + nv]
-        assert np.max(np.abs(lse_gpu[r0 + 128 * i: r0 + 128 * i + nv] - lref)) <= gp.LSE_ABS
-    assert int(g["visited"].item()) == 2288520
 
 
 def test_error_paths_on_device():

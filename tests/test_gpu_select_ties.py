@@ -1,0 +1,108 @@
+"""veda_select_blocks on crafted, heavily tied scores, against the oracle's
+selection (Miowtion project page, Key Features > "Veda sparse attention":
+per-row budgets with a forced diagonal; ties go to the lowest key tile index
+and -0 equals +0, as the oracle's sort key (score descending, index ascending)
+fixes them).
+
+Random fp32 scores essentially never tie, so the parity tests on generated
+inputs never reach the kernel's tie path (equal keys ranked by ballot order
+across 64-column chunks) or its -0/+0 canonicalisation.  Here the scores are
+written directly and passed through the C ABI; CSR and dense mask must be
+bit-exact against the oracle.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import veda_workloads as wl
+from oracle import veda_oracle as vo
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from block_sparse_attention_10_amd import binding as vb  # noqa: E402
+
+
+def _plans():
+    V, DN = wl.VIDEO3D, wl.DENSE1D
+    return [
+        wl.workload(1),      # FIXED_K = 2, 8 tiles per head
+        wl.workload(2),      # 64 tiles: one 64-column chunk per row
+        wl.workload(3),      # 224 tiles: four chunks, the last partial
+        wl.workload(5),      # segmented reference / target budgets plus dense audio
+        wl.Workload(91, "small_packed_2shapes", (wl.Segment(V, (2, 8, 12), 0), wl.Segment(V, (4, 10, 12), 192),
+                                                 wl.Segment(DN, (1, 1, 200), 672)),
+                    4, 128, ((2, 8, 8), (4, 4, 8), (2, 8, 8), (4, 4, 8)), wl.KEEP_RATIO, 1, 3),
+        wl.Workload(99, "three_video_segments", (wl.Segment(V, (2, 8, 16), 0), wl.Segment(V, (4, 16, 16), 256),
+                                                 wl.Segment(V, (2, 24, 16), 1280)),
+                    2, 64, ((1, 8, 16), (2, 8, 8)), wl.KEEP_RATIO, 1, 4),
+    ]
+
+
+def _kinds():
+    return ["all_zero_mixed_sign", "small_integers", "runs_across_chunks", "signed_zeros_and_ones",
+            "diagonal_lowest", "equal_to_threshold_tail"]
+
+
+def _scores(kind, n, rng):
+    """One head's n x n score matrix (fp32) of the given kind."""
+    if kind == "all_zero_mixed_sign":
+        # every score is a zero of random sign: each row keeps its lowest key tiles
+        s = np.zeros((n, n), dtype=np.float32)
+        s[rng.random((n, n)) < 0.5] = np.float32(-0.0)
+    elif kind == "small_integers":
+        # four values only: the k-th place falls inside a long run of equal keys
+        s = rng.integers(-1, 3, size=(n, n)).astype(np.float32)
+    elif kind == "runs_across_chunks":
+        # equal values in runs of 50 columns, so runs straddle the 64-column chunks
+        s = (np.arange(n)[None, :] // 50).astype(np.float32) * np.float32(0.5)
+        s = np.broadcast_to(s, (n, n)).copy()
+        s[:, ::3] += np.float32(1.0)
+        s = s[:, ::-1].copy() if n % 2 else s
+    elif kind == "signed_zeros_and_ones":
+        s = rng.choice(np.array([-1.0, -0.0, 0.0, 1.0], dtype=np.float32), size=(n, n))
+    elif kind == "diagonal_lowest":
+        # the diagonal scores lowest; everything else ties
+        s = np.full((n, n), 2.5, dtype=np.float32)
+        np.fill_diagonal(s, -7.0)
+    elif kind == "equal_to_threshold_tail":
+        # distinct large values for a few columns, then a long tie: the tie must be
+        # cut by key index at the budget
+        s = np.full((n, n), 3.0, dtype=np.float32)
+        for i in range(n):
+            top = rng.choice(n, size=min(3, n), replace=False)
+            s[i, top] = np.float32(5.0) + rng.random(len(top)).astype(np.float32)
+    else:
+        raise ValueError(kind)
+    return s
+
+
+@pytest.mark.parametrize("kind", _kinds())
+@pytest.mark.parametrize("w", _plans(), ids=lambda w: w.name)
+def test_select_ties_bit_exact(w, kind):
+    op = vo.Plan.from_workload(w)
+    plan = vb.Plan.from_workload(w)
+    rng = np.random.default_rng(zlib.crc32((w.name + '/' + kind).encode()))
+    scores = [_scores(kind, op.heads[h].num_tiles, rng) for h in range(w.num_heads)]
+    flat = np.concatenate([s.reshape(-1) for s in scores])
+    assert flat.size == plan.info["total_pairs"]
+    dev = "cuda"
+    s_dev = torch.from_numpy(flat).to(dev)
+    row_ptr = torch.full((plan.T + 1,), -1, dtype=torch.int32, device=dev)
+    col = torch.full((plan.info["nnz"],), -1, dtype=torch.int32, device=dev)
+    dm = torch.full((plan.info["total_pairs"],), 7, dtype=torch.uint8, device=dev)
+    plan.select(s_dev, row_ptr, col, dm)
+    torch.cuda.synchronize()
+    sel = vo.select_blocks(op, scores)
+    rp, ci = vo.to_csr(op, sel)
+    ref_dm = np.concatenate([m.reshape(-1) for m in vo.to_dense_mask(op, sel)])
+    got_rp, got_col, got_dm = row_ptr.cpu().numpy(), col.cpu().numpy(), dm.cpu().numpy()
+    assert np.array_equal(got_rp, rp), (w.name, kind)
+    bad = np.nonzero(got_col != ci)[0]
+    assert bad.size == 0, (w.name, kind, "first differing col_idx entry", int(bad[0]) if bad.size else None)
+    assert np.array_equal(got_dm, ref_dm), (w.name, kind)
