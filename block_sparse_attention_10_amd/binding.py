@@ -16,9 +16,9 @@ from typing import Dict, Optional, Sequence, Tuple
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# VEDA_LIB may point at another build of the same library (e.g. a variant
-# being compared); by default the in-tree build is loaded.
-LIB_PATH = os.environ.get("VEDA_LIB") or os.path.join(_PKG, "libveda.so")
+# Only the in-tree build is ever loaded (no override): tests, smoke and bench
+# run exactly the library built from this source tree.
+LIB_PATH = os.path.join(_PKG, "libveda.so")
 
 VEDA_OK = 0
 VEDA_SEG_VIDEO3D = 0
@@ -118,6 +118,11 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = args
         _lib = l
     return _lib
+
+
+def loaded_library() -> str:
+    """Absolute path of the libveda.so this process loaded (loads it)."""
+    return os.path.realpath(lib()._name)
 
 
 def _check(status: int) -> None:
