@@ -98,6 +98,7 @@ _SIGS = {
     "veda_block_sparse_attn_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
                                           _P, ctypes.c_size_t, _P]),
     "veda_tile_plan_vote": (_I32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P]),
+    "veda_score_tiles_noalloc": (_I32, [_P, _P, _P, _P, _P, _P, _P]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -234,6 +235,11 @@ def veda_score_tiles(plan: int, q_perm, k_perm, w_q, w_k, scores, workspace, str
     _check(lib().veda_score_tiles(plan, _ptr(q_perm), _ptr(k_perm), _ptr(w_q), _ptr(w_k), _ptr(scores),
                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _stream(stream)))
+
+
+def veda_score_tiles_noalloc(plan: int, q_perm, k_perm, w_q, w_k, scores, stream=None) -> None:
+    _check(lib().veda_score_tiles_noalloc(plan, _ptr(q_perm), _ptr(k_perm), _ptr(w_q), _ptr(w_k), _ptr(scores),
+                                          _stream(stream)))
 
 
 def _nbytes(t):
@@ -435,6 +441,16 @@ class Plan:
         self._expect(scores, (self.info["total_pairs"],), torch.float32, "scores")
         self._check_workspace(workspace)
         veda_score_tiles(self.handle, q_perm, k_perm, w_q, w_k, scores, workspace, stream)
+
+    def score_noalloc(self, q_perm, k_perm, w_q, w_k, scores, stream=None):
+        """veda_score_tiles with the library's static scratch (no workspace)."""
+        import torch
+        self._expect(q_perm, (self.R, self.D), torch.bfloat16, "q_perm")
+        self._expect(k_perm, (self.R, self.D), torch.bfloat16, "k_perm")
+        self._expect(w_q, (self.H, self.D, 3 * self.D), torch.float32, "w_q")
+        self._expect(w_k, (self.H, self.D, 3 * self.D), torch.float32, "w_k")
+        self._expect(scores, (self.info["total_pairs"],), torch.float32, "scores")
+        veda_score_tiles_noalloc(self.handle, q_perm, k_perm, w_q, w_k, scores, stream)
 
     def select(self, scores, row_ptr, col_idx, dense_mask=None, stream=None):
         import torch

@@ -617,6 +617,28 @@ veda_status veda_score_tiles(const veda_plan* p, const void* q_perm, const void*
                   "score");
 }
 
+veda_status veda_score_tiles_noalloc(const veda_plan* p, const void* q_perm, const void* k_perm,
+                                     const float* w_q, const float* w_k, float* scores, void* stream) {
+  veda_status st = check_plan_ready(p);
+  if (st) return st;
+  if ((st = check_ptr(q_perm, "q_perm")) || (st = check_ptr(k_perm, "k_perm")) ||
+      (st = check_ptr(w_q, "w_q")) || (st = check_ptr(w_k, "w_k")) || (st = check_ptr(scores, "scores")))
+    return st;
+  if (p->info.score_workspace_bytes > kStaticScratchBytes)
+    return fail(VEDA_ERR_WORKSPACE,
+                "the plan's predictor needs %lld bytes of scratch; the static scratch holds %lld "
+                "(T * head_dim * 32 bytes: at most %lld tiles at head dim %d); use veda_score_tiles "
+                "with a workspace",
+                (long long)p->info.score_workspace_bytes, (long long)kStaticScratchBytes,
+                (long long)(kStaticScratchBytes / (32LL * p->info.head_dim)), p->info.head_dim);
+  void* ws = nullptr;
+  const hipError_t e = static_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(VEDA_ERR_LAUNCH, "static scratch address on the current device: %s", hipGetErrorString(e));
+  return launched(launch_score(p->dev, q_perm, k_perm, w_q, w_k, scores, ws, (hipStream_t)stream),
+                  "score (static scratch)");
+}
+
 veda_status veda_permute_qkv(const veda_plan* p, const void* q, const void* k, const void* v, void* q_perm,
                              void* k_perm, void* v_t, void* workspace, size_t workspace_bytes, void* stream) {
   veda_status st = check_plan_ready(p);

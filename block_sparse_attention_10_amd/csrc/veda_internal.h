@@ -98,6 +98,12 @@ hipError_t launch_attn_bwd(const DevPlan& p, const void* q, const void* k, const
                            const int32_t* col_ptr, const int32_t* row_idx, float scale, void* dq, void* dk,
                            void* dv, void* workspace, hipStream_t s);
 
+// The static scratch of veda_score_tiles_noalloc: one array per GPU, fixed
+// size.  static_scratch() returns its device address on the current device
+// (looked up once per device with hipGetSymbolAddress).
+constexpr int64_t kStaticScratchBytes = int64_t(128) << 20;
+hipError_t static_scratch(void** ptr);
+
 // Scratch the score call needs: pooled features of Q and K (fp32 [T, 3D]
 // each) and their projections (fp32 [T, D] each).
 inline int64_t score_workspace_bytes(int64_t total_tiles, int32_t head_dim) {

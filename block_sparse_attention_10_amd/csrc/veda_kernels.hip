@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <map>
+#include <mutex>
 
 #include "veda_internal.h"
 
@@ -2345,6 +2347,41 @@ hipError_t launch_attn_bwd(const DevPlan& p, const void* q, const void* k, const
                        scale_log2, scale, static_cast<uint16_t*>(dq));
   }
   return hipGetLastError();
+}
+
+}  // namespace veda
+
+// ---------------------------------------------------------------------------
+// static scratch for callers that cannot allocate
+// ---------------------------------------------------------------------------
+//
+// One fixed array per GPU, reserved when the library's code object is loaded
+// on that GPU and held until the process ends.  On the host the array's name
+// only stands in for the device symbol: it is never passed to a kernel or a
+// copy.  The first use on a device asks HIP for the array's device address on
+// that device (with it current) and keeps it; every later use takes the kept
+// address.
+static __device__ __align__(256) uint8_t scratch[veda::kStaticScratchBytes];
+
+namespace veda {
+
+hipError_t static_scratch(void** ptr) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;   // device -> device address of `scratch`
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    it = addr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return hipSuccess;
 }
 
 }  // namespace veda

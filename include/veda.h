@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define VEDA_ABI_VERSION 6
+#define VEDA_ABI_VERSION 7
 
 typedef int32_t veda_status;
 enum {
@@ -219,6 +219,23 @@ veda_status veda_score_pooled(const veda_plan* plan, const float* w_q, const flo
 veda_status veda_score_tiles(const veda_plan* plan, const void* q_perm, const void* k_perm,
                              const float* w_q, const float* w_k, float* scores,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* veda_score_tiles without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same kernels and bitwise the same
+ * scores as veda_score_tiles; the pooled features and projections go to a
+ * static scratch array of the library, 128 MiB per GPU, reserved when the
+ * library is loaded on that GPU and held until the process ends.  This call
+ * allocates nothing and calls no allocating routine.
+ *   Limit: the plan's score_workspace_bytes (T * head_dim * 32 bytes) must not
+ *   exceed 128 MiB, i.e. at most 32,768 tiles over all heads at head dim 128
+ *   (65,536 at 64); a larger plan returns VEDA_ERR_WORKSPACE before any launch.
+ *   Every call on one GPU shares that GPU's scratch, and the kernels overwrite
+ *   all of it that they read (nothing needs to start at zero): two calls whose
+ *   work overlaps in time on one GPU (other streams, other threads) race and
+ *   give wrong scores; calls ordered on one stream do not. */
+veda_status veda_score_tiles_noalloc(const veda_plan* plan, const void* q_perm, const void* k_perm,
+                                     const float* w_q, const float* w_k, float* scores, void* stream);
 
 /* Budgeted top-k block mask (Key Features > "Veda sparse attention":
  * equal-kernel-cost budgets, Bresenham rounding, forced diagonal, segmented

@@ -37,7 +37,7 @@ def test_abi_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert vb.veda_abi_version() == 6
+    assert vb.veda_abi_version() == 7
 
 
 def test_available_reports_reason_without_gpu():
@@ -170,6 +170,7 @@ def test_compute_calls_check_on_host_before_any_launch():
                                               fake, 0, None, None, None) == 6
         assert lib.veda_permute_qkv(h, fake, fake, fake, fake, fake, fake, None, 0, None) == 6
         assert lib.veda_score_pooled(h, fake, fake, fake, fake, 1 << 20, None) == 6
+        assert lib.veda_score_tiles_noalloc(h, fake, fake, fake, fake, fake, None) == 6
         assert lib.veda_block_heat(h, fake, fake, fake, ctypes.c_float(0.125), fake, None) == 6
         assert lib.veda_dense_lse_heat(h, fake, fake, fake, fake, ctypes.c_float(0.125), fake, fake, fake,
                                        1 << 30, None) == 6
