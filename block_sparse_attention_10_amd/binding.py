@@ -576,3 +576,14 @@ class Plan:
     def empty_workspace(self):
         import torch
         return torch.empty(self.info["score_workspace_bytes"] // 4, dtype=torch.float32, device="cuda")
+
+    def score_workspace_views(self, workspace):
+        """Named views of a score workspace (fp32 tensor of score_workspace_bytes)
+        in the layout include/veda.h documents for veda_score_tiles: pooled
+        features of Q and K [T, 3D], then the projections q_hat, k_hat [T, D]."""
+        self._check_workspace(workspace)
+        T, D = self.T, self.D
+        w = workspace.view(-1)
+        f = T * 3 * D
+        return {"feat_q": w[0:f].view(T, 3 * D), "feat_k": w[f:2 * f].view(T, 3 * D),
+                "q_hat": w[2 * f:2 * f + T * D].view(T, D), "k_hat": w[2 * f + T * D:2 * f + 2 * T * D].view(T, D)}

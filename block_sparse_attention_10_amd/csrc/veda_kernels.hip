@@ -772,6 +772,33 @@ __device__ __forceinline__ void pv_group(const uint16_t* __restrict__ vhalf, con
   }
 }
 
+// One step of the continuous pipeline: S^T of key group kt (from khalf)
+// and O^T += V^T P^T over key group ktv (from vhalf, P in pg), issued
+// alternately so that neither MFMA chain waits on its own accumulator.
+template <int D>
+__device__ __forceinline__ f32x16 qk_pv_step(const uint16_t* __restrict__ khalf, const bf16x8 (&qf)[D / 16], int kt,
+                                             const uint16_t* __restrict__ vhalf, const bf16x8 (&pg)[2], int ktv,
+                                             f32x16 (&oacc)[D / 32]) {
+  constexpr int CH = D / 8;
+  constexpr int NQ = D / 16, NV = 2 * (D / 32);
+  static_assert(NQ == NV, "as many PV as QK products per step");
+  const int lane = lane_id();
+  const int ln = lane & 31, hl = lane >> 5;
+  const int m = 32 * (kt & 1) + ln;
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(khalf + m * D + 8 * ((2 * s + hl) ^ (m & (CH - 1)))));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc, 0, 0, 0);
+    const int s2 = s / (D / 32), db = s % (D / 32);
+    const int c = 4 * (ktv & 1) + 2 * s2 + hl;
+    const int d = 32 * db + ln;
+    const bf16x8 v = __builtin_bit_cast(bf16x8, ld16(vhalf + d * 64 + 8 * (c ^ ((ln >> 1) & 7))));
+    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pg[s2], oacc[db], 0, 0, 0);
+  }
+  return acc;
+}
+
 // Key slots >= nj of group kt become -inf (the singleton mask rule: slots at
 // or past a tile's valid count are padding).
 __device__ __forceinline__ void mask_group(f32x16& sg, int kt, int nj, int hl) {
@@ -861,10 +888,13 @@ __device__ __forceinline__ int half_pads(int nv, int hh) {
 // worked in four 32-key groups, software-pipelined inside each wave: the QK^T
 // MFMAs of group t are issued together with the PV MFMAs of group t-2 and the
 // softmax VALU work of group t-1, none of which depend on each other, so one
-// wave keeps the matrix core and the vector ALU busy at the same time.  (On
-// gfx950 an MFMA overlaps VALU work of its own wave; a second wave's VALU
-// work largely waits for it.)  VALU work is the scarce resource, so the fast
-// pass spends none on maxima, rescaling or masking:
+// wave keeps the matrix core and the vector ALU busy at the same time.  With
+// PV the pipeline runs over the whole row, across block boundaries, so every
+// step has the same mix (run_fast_pv); the LSE-only pass pipelines each block
+// on its own.  VALU work competes with the matrix core for issue slots and
+// for power (under random bf16 operands the chip runs these kernels at about
+// two thirds of its nominal clock), so the fast pass spends none on maxima,
+// rescaling or masking:
 //
 // Reference point.  p = exp2(s*c - m), c = softmax_scale * log2(e), with one
 // m per query for the whole row: the exact maximum of the row's first key
@@ -885,10 +915,9 @@ __device__ __forceinline__ int half_pads(int nv, int hh) {
 // it grows), block by block with plain synchronous tile copies.
 //
 // K and V^T are single buffers per workgroup, each in two 64-key halves
-// (four LDS arrays) that are refilled separately: K rows of groups 0-1 once
-// every wave has done QK of group 1, K rows of groups 2-3 and V^T keys 0-63
-// once every wave has done QK of group 3 and PV of group 1, V^T keys 64-127
-// after the block.  Two workgroups share a CU (72 KB of LDS each).
+// (four LDS arrays) that are refilled separately as soon as every wave is
+// done with them (run_fast_pv and the block lambda below say when).  Two
+// workgroups share a CU (72 KB of LDS each).
 template <int D, bool PV, bool HB>
 __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* __restrict__ q,
                                               const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
@@ -973,11 +1002,13 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
   // it stays in its pipeline step like the packed p with PV).
   auto pin_sum = [](float& l) { asm volatile("" : "+v"(l)); };
 
-  // One key block of the fast pass.  Steps are separated by scheduling
-  // barriers so that the compiler keeps each step's operand reads and MFMAs
-  // together with that step's softmax work (and register lifetimes short).
-  // It also issues the asynchronous copies of the next block; `compute` =
-  // false runs only those (the pass's first iteration).
+  // One key block of the LSE-only fast pass (without PV: the dense LSE and
+  // the heat; the attention itself runs run_fast_pv below).  Steps are
+  // separated by scheduling barriers so that the compiler keeps each step's
+  // operand reads and MFMAs together with that step's softmax work (and
+  // register lifetimes short).  It also issues the asynchronous copies of
+  // the next block's K; `compute` = false runs only those (the pass's first
+  // iteration).
   // With HB each finished block's sum of p per query (both lane halves) goes
   // to bsum[position][query]; the store waits until the next block's first
   // copy wait, where no copy is in flight, so the copy waits (which count
@@ -990,98 +1021,51 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
       }
     }
   };
+  // the sum of p of one group, into l and (HB) the block's sum
+  auto sum_group = [&](const f32x16& sg, bool first_of_block) {
+    const float g = exp_sum(sg, c, m_run);
+    l_run += g;
+    pin_sum(l_run);
+    if constexpr (HB) {
+      bs = first_of_block ? g : bs + g;
+      pin_sum(bs);
+    }
+  };
   auto block = [&](bool compute, bool first, int ent, bool more, int jn, int bpos) {
     const f32x16 zero16 = {};
     f32x16 s0, s1, s2, s3;
-    bf16x8 p0[2], p1[2], p2[2], p3[2];
     if (compute) {
       s0 = qk_group<D>(kh0, qf, 0, zero16);
       interleave_step<8, 0>();
       if (first) m_run = group_max(s0) * c;   // finite: key 0 always exists
       __builtin_amdgcn_sched_barrier(0);
       s1 = qk_group<D>(kh0, qf, 1, zero16);
-      if constexpr (PV) {
-        l_run += exp_group<true>(s0, c, m_run, p0);
-        pin(p0);
-      } else {
-        const float g = exp_sum(s0, c, m_run);
-        l_run += g;
-        pin_sum(l_run);
-        if constexpr (HB) {
-          bs = g;
-          pin_sum(bs);
-        }
-      }
+      sum_group(s0, true);
       interleave_step<8, 6>();
     }
-    // V^T(b) keys 0-63 have landed (without PV: K rows 64-127 have); K rows
-    // 0-63 are free
-    dma_sync<PV ? H : 0>();
+    // every wave is done with K rows 0-63
+    dma_sync<0>();
     flush_block_sum();
     if (more) dma_k_half<D>(kh0, rk, jn * kTile * D * 2, koff, wave, 0);
     __builtin_amdgcn_sched_barrier(0);
     if (compute) {
       s2 = qk_group<D>(kh1, qf, 2, zero16);
-      if constexpr (PV) pv_group<D>(vh0, p0, 0, oacc);
-      if constexpr (PV) {
-        l_run += exp_group<true>(s1, c, m_run, p1);
-        pin(p1);
-      } else {
-        const float g = exp_sum(s1, c, m_run);
-        l_run += g;
-        pin_sum(l_run);
-        if constexpr (HB) {
-          bs += g;
-          pin_sum(bs);
-        }
-      }
-      interleave_step<PV ? 16 : 8, 3>();
+      sum_group(s1, false);
+      interleave_step<8, 3>();
       __builtin_amdgcn_sched_barrier(0);
       s3 = qk_group<D>(kh1, qf, 3, zero16);
-      if constexpr (PV) pv_group<D>(vh0, p1, 1, oacc);
-      if constexpr (PV) {
-        l_run += exp_group<true>(s2, c, m_run, p2);
-        pin(p2);
-      } else {
-        const float g = exp_sum(s2, c, m_run);
-        l_run += g;
-        pin_sum(l_run);
-        if constexpr (HB) {
-          bs += g;
-          pin_sum(bs);
-        }
-      }
-      interleave_step<PV ? 16 : 8, 3>();
+      sum_group(s2, false);
+      interleave_step<8, 3>();
     }
-    // V^T(b) keys 64-127 have landed; K, V^T keys 0-63 free.  (Without PV
-    // nothing needs to have landed here; with HB the block-sum store issued
-    // before the K copies is allowed to stay in flight too.)
+    // every wave is done with K rows 64-127 (with HB the block-sum store
+    // issued before the K copies is allowed to stay in flight)
     if (more) dma_sync<HB ? H + 1 : H>(); else dma_sync<0>();
-    if (more) {
-      dma_k_half<D>(kh1, rk, jn * kTile * D * 2, koff, wave, 1);
-      if constexpr (PV) dma_vt_half<D>(vh0, rv, jn * kTile * D * 2, voff, wave, 0);
-    }
+    if (more) dma_k_half<D>(kh1, rk, jn * kTile * D * 2, koff, wave, 1);
     __builtin_amdgcn_sched_barrier(0);
     if (compute) {
-      if constexpr (PV) pv_group<D>(vh1, p2, 2, oacc);
-      if constexpr (PV) {
-        l_run += exp_group<true>(s3, c, m_run, p3);
-        pin(p3);
-      } else {
-        const float g = exp_sum(s3, c, m_run);
-        l_run += g;
-        pin_sum(l_run);
-        if constexpr (HB) {
-          bs += g;
-          pin_sum(bs);
-        }
-      }
-      interleave_step<PV ? 8 : 0, 6>();
+      sum_group(s3, false);
+      interleave_step<0, 6>();
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (PV) {
-        pv_group<D>(vh1, p3, 3, oacc);
-        interleave_step<8, 0>();
-      }
       npad += ((ent >> 7) & 127) + (ent & 127);
       if constexpr (HB) {
         pend_b = bs + __shfl_xor(bs, 32, 64);
@@ -1098,11 +1082,11 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
     npad = 0;
   };
 
-  // Fast pass.  Iteration b computes block b and copies block b+1; the first
-  // iteration (b = beg-1) only copies block beg.  Every asynchronous copy of
-  // the kernel is issued from the four call sites of this pass: the
-  // compiler tracks only a few distinct copy sites precisely and makes every
-  // LDS read wait for all copies once there are more.
+  // LSE-only fast pass.  Iteration b computes block b and copies block b+1;
+  // the first iteration (b = beg-1) only copies block beg.  Its K copies come
+  // from two call sites: the compiler tracks only a few distinct copy sites
+  // precisely and makes every LDS read wait for all copies once there are
+  // more.
   auto run_fast = [&]() {
     reset_row();
     fill_list(beg);
@@ -1113,10 +1097,7 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
       const bool more = b + 1 < end;
       const int jn = en >> 14;
       block(b >= beg, b == beg, ent, more, jn, b);
-      if (more) {
-        dma_sync<H>();                // K(b+1) has landed (without PV: its rows 0-63); every wave is done with V^T(b)
-        if constexpr (PV) dma_vt_half<D>(vh1, rv, jn * kTile * D * 2, voff, wave, 1);
-      }
+      if (more) dma_sync<H>();        // K(b+1) rows 0-63 have landed
       ent = en;
       if (b + 2 < end) {
         const int slot = (b + 2 - beg) % kRowList;
@@ -1129,6 +1110,106 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
       }
     }
     flush_block_sum();
+  };
+
+  // Fast pass with PV: one software pipeline over the whole row.  Step t
+  // (t = 4b + g for group g of block b) issues the QK^T MFMAs of group t, the
+  // PV MFMAs of group t-2 and the softmax of group t-1, which do not depend
+  // on each other, so every step has the same mix (16 MFMAs and one group's
+  // softmax), across block boundaries too.  S^T of a group waits for its
+  // softmax in s0/s1 and its packed P for its PV in p0/p1 (by the parity of
+  // t).  K and V^T halves are refilled at two workgroup barriers per block:
+  //   A, after step 4b+1 (every wave is done with K rows 0-63 of b and V^T
+  //      keys 64-127 of b-1): K rows 0-63 of b+1, V^T keys 64-127 of b;
+  //   B, after step 4b+3 (done with K rows 64-127 and V^T keys 0-63 of b):
+  //      K rows 64-127 and V^T keys 0-63 of b+1.
+  // Each barrier first waits for the copies issued at the one before it, two
+  // steps earlier.
+  auto run_fast_pv = [&]() {
+    reset_row();
+    fill_list(beg);
+    dma_sync<0>();
+    const int nb = end - beg;
+    int ent = uni(rowlist[0]);      // current block's list entry
+    int jc = ent >> 14;             // its key tile
+    dma_k_half<D>(kh0, rk, jc * kTile * D * 2, koff, wave, 0);
+    dma_k_half<D>(kh1, rk, jc * kTile * D * 2, koff, wave, 1);
+    dma_vt_half<D>(vh0, rv, jc * kTile * D * 2, voff, wave, 0);
+    dma_sync<0>();
+    const f32x16 zero16 = {};
+    f32x16 s0, s1;
+    bf16x8 p0[2], p1[2];
+    // block 0, step 0: S of group 0
+    s0 = qk_group<D>(kh0, qf, 0, zero16);
+    interleave_step<8, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    // step 1: S of group 1; the row's reference point (group 0's maximum) and group 0's softmax
+    s1 = qk_group<D>(kh0, qf, 1, zero16);
+    m_run = group_max(s0) * c;   // finite: key 0 always exists
+    l_run += exp_group<true>(s0, c, m_run, p0);
+    pin(p0);
+    interleave_step<8, 8>();
+    __builtin_amdgcn_sched_barrier(0);
+    for (int b = 0; b < nb; ++b) {
+      const bool more = b + 1 < nb;
+      // barrier A: K rows 64-127 and V^T keys 0-63 of b have landed
+      dma_sync<0>();
+      int en = 0, jn = 0;
+      if (more) {
+        const int slot = (b + 1) % kRowList;
+        if (slot == 0) {   // only rows longer than kRowList blocks get here
+          fill_list(beg + b + 1);
+          dma_sync<0>();
+        }
+        en = uni(rowlist[slot]);
+        jn = en >> 14;
+        dma_k_half<D>(kh0, rk, jn * kTile * D * 2, koff, wave, 0);
+      }
+      dma_vt_half<D>(vh1, rv, jc * kTile * D * 2, voff, wave, 1);
+      npad += ((ent >> 7) & 127) + (ent & 127);
+      __builtin_amdgcn_sched_barrier(0);
+      // step 4b+2: S of group 2, softmax of group 1, PV of group 0
+      s0 = qk_pv_step<D>(kh1, qf, 2, vh0, p0, 0, oacc);
+      l_run += exp_group<true>(s1, c, m_run, p1);
+      pin(p1);
+      interleave_step<16, 4>();
+      __builtin_amdgcn_sched_barrier(0);
+      // step 4b+3: S of group 3, softmax of group 2, PV of group 1
+      s1 = qk_pv_step<D>(kh1, qf, 3, vh0, p1, 1, oacc);
+      l_run += exp_group<true>(s0, c, m_run, p0);
+      pin(p0);
+      interleave_step<16, 4>();
+      __builtin_amdgcn_sched_barrier(0);
+      // barrier B: K rows 0-63 of b+1 and V^T keys 64-127 of b have landed
+      dma_sync<0>();
+      if (more) {
+        dma_k_half<D>(kh1, rk, jn * kTile * D * 2, koff, wave, 1);
+        dma_vt_half<D>(vh0, rv, jn * kTile * D * 2, voff, wave, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // step 4(b+1): S of group 0 of b+1, softmax of group 3 of b, PV of group 2 of b
+        s0 = qk_pv_step<D>(kh0, qf, 0, vh1, p0, 2, oacc);
+        l_run += exp_group<true>(s1, c, m_run, p1);
+        pin(p1);
+        interleave_step<16, 4>();
+        __builtin_amdgcn_sched_barrier(0);
+        // step 4(b+1)+1: S of group 1 of b+1, softmax of group 0 of b+1, PV of group 3 of b
+        s1 = qk_pv_step<D>(kh0, qf, 1, vh1, p1, 3, oacc);
+        l_run += exp_group<true>(s0, c, m_run, p0);
+        pin(p0);
+        interleave_step<16, 4>();
+        __builtin_amdgcn_sched_barrier(0);
+        ent = en;
+        jc = jn;
+      }
+    }
+    // drain: softmax of the last group 3 and PV of groups 2 and 3
+    l_run += exp_group<true>(s1, c, m_run, p1);
+    pin(p1);
+    pv_group<D>(vh1, p0, 2, oacc);
+    interleave_step<8, 7>();
+    __builtin_amdgcn_sched_barrier(0);
+    pv_group<D>(vh1, p1, 3, oacc);
+    interleave_step<8, 0>();
   };
 
   // Safe pass: per block a plain synchronous tile copy, then the four groups
@@ -1172,7 +1253,7 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
     }
   };
 
-  run_fast();
+  if constexpr (PV) run_fast_pv(); else run_fast();
   float l_all = l_run + __shfl_xor(l_run, 32, 64);
   const float pad_mass = (float)npad * __builtin_amdgcn_exp2f(-m_run);
   l_all -= pad_mass;

@@ -215,7 +215,13 @@ veda_status veda_score_pooled(const veda_plan* plan, const float* w_q, const flo
  *   q_perm, k_perm: device permuted bf16 [R, D]
  *   w_q, w_k:       device fp32 [H, D, 3D]
  *   scores:         device fp32 [sum_h n_h^2]
- *   workspace:      device scratch of score_workspace_bytes (16-byte aligned) */
+ *   workspace:      device scratch of score_workspace_bytes (16-byte aligned).
+ *                   After the call it holds, fp32 and in this order: the
+ *                   pooled features of Q [T, 3D] and of K [T, 3D] (rows in
+ *                   global tile order, columns [mean | max | min]), then the
+ *                   projections q_hat [T, D] and k_hat [T, D]; so does it
+ *                   after veda_permute_qkv (features) and veda_score_pooled
+ *                   (projections). */
 veda_status veda_score_tiles(const veda_plan* plan, const void* q_perm, const void* k_perm,
                              const float* w_q, const float* w_k, float* scores,
                              void* workspace, size_t workspace_bytes, void* stream);

@@ -571,10 +571,9 @@ def test_predictor_sums_follow_the_sequential_order():
     plan.permute_qkv(q, k, v, qp, kp, vt, ws)
     plan.score_pooled(inp["w_q"].to(dev), inp["w_k"].to(dev), sc, ws)
     torch.cuda.synchronize()
-    T, D = op.total_tiles, w.head_dim
-    wsh = ws.cpu().numpy()
-    hq = wsh[6 * T * D:7 * T * D].reshape(T, D)
-    hk = wsh[7 * T * D:8 * T * D].reshape(T, D)
+    views = plan.score_workspace_views(ws)
+    hq = views["q_hat"].cpu().numpy()
+    hk = views["k_hat"].cpu().numpy()
     assert np.array_equal(hq.view(np.uint32), qh.view(np.uint32))
     assert np.array_equal(hk.view(np.uint32), kh.view(np.uint32))
     sg = gp.split_scores(None, op, sc.cpu().numpy())
@@ -613,8 +612,9 @@ def test_permute_qk_only_and_side_stream_v(idx):
     plan.permute_qkv(q, k, None, got[0], got[1], None, got[3])
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    nf = 2 * plan.T * 3 * w.head_dim          # pooled features of Q, then K, at the workspace's start
-    ref[3], got[3] = ref[3][:nf], got[3][:nf]
+    rv, gv = plan.score_workspace_views(ref[3]), plan.score_workspace_views(got[3])
+    ref[3] = torch.cat([rv["feat_q"].reshape(-1), rv["feat_k"].reshape(-1)])
+    got[3] = torch.cat([gv["feat_q"].reshape(-1), gv["feat_k"].reshape(-1)])
     for a, b, name in zip(ref, got, ("q_perm", "k_perm", "v_t", "pooled features")):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
     with pytest.raises(ValueError):
