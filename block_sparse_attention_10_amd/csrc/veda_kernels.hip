@@ -1112,6 +1112,94 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
     flush_block_sum();
   };
 
+  // LSE-only fast pass as one pipeline over the whole row: step t issues the
+  // QK^T MFMAs of group t and the sum of p of group t-1, across block edges
+  // too, so every step has the same mix (8 MFMAs and one group's sum).  K
+  // halves are refilled at two barriers per block as in the pass with PV:
+  // after step 4b+1 K rows 0-63 of b+1, after step 4b+3 K rows 64-127 of
+  // b+1, each barrier first waiting for the copy issued at the previous one.
+  // The LDS stays that of the block pass (K halves and the row list), so
+  // three workgroups still share a CU.  With HB, block b's sum of p per query
+  // is complete at step 4b+4 and stored there; the next barrier's copy wait
+  // also covers the store.
+  auto run_fast_lse = [&]() {
+    reset_row();
+    fill_list(beg);
+    dma_sync<0>();
+    const int nb = end - beg;
+    int ent = uni(rowlist[0]);
+    int jc = ent >> 14;
+    dma_k_half<D>(kh0, rk, jc * kTile * D * 2, koff, wave, 0);
+    dma_k_half<D>(kh1, rk, jc * kTile * D * 2, koff, wave, 1);
+    dma_sync<0>();
+    const f32x16 zero16 = {};
+    f32x16 s0, s1;
+    auto store_block_sum = [&](int bpos) {
+      if constexpr (HB) {
+        const float tot = bs + __shfl_xor(bs, 32, 64);
+        if (hl == 0) bsum[(int64_t)bpos * kTile + 32 * w + ln] = tot;
+      }
+    };
+    // block 0, step 0: S of group 0
+    s0 = qk_group<D>(kh0, qf, 0, zero16);
+    interleave_step<8, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    // step 1: S of group 1; the row's reference point (group 0's maximum) and group 0's sum
+    s1 = qk_group<D>(kh0, qf, 1, zero16);
+    m_run = group_max(s0) * c;   // finite: key 0 always exists
+    sum_group(s0, true);
+    interleave_step<8, 8>();
+    __builtin_amdgcn_sched_barrier(0);
+    for (int b = 0; b < nb; ++b) {
+      const bool more = b + 1 < nb;
+      // barrier A: K rows 64-127 of b have landed; every wave is done with rows 0-63
+      dma_sync<0>();
+      int en = 0, jn = 0;
+      if (more) {
+        const int slot = (b + 1) % kRowList;
+        if (slot == 0) {   // only rows longer than kRowList blocks get here
+          fill_list(beg + b + 1);
+          dma_sync<0>();
+        }
+        en = uni(rowlist[slot]);
+        jn = en >> 14;
+        dma_k_half<D>(kh0, rk, jn * kTile * D * 2, koff, wave, 0);
+      }
+      npad += ((ent >> 7) & 127) + (ent & 127);
+      __builtin_amdgcn_sched_barrier(0);
+      // steps 4b+2, 4b+3: S of groups 2 and 3, sums of groups 1 and 2
+      s0 = qk_group<D>(kh1, qf, 2, zero16);
+      sum_group(s1, false);
+      interleave_step<8, 6>();
+      __builtin_amdgcn_sched_barrier(0);
+      s1 = qk_group<D>(kh1, qf, 3, zero16);
+      sum_group(s0, false);
+      interleave_step<8, 6>();
+      __builtin_amdgcn_sched_barrier(0);
+      // barrier B: K rows 0-63 of b+1 have landed; every wave is done with rows 64-127
+      dma_sync<0>();
+      if (more) {
+        dma_k_half<D>(kh1, rk, jn * kTile * D * 2, koff, wave, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // step 4(b+1): S of group 0 of b+1, the sum of group 3 of b (block b complete)
+        s0 = qk_group<D>(kh0, qf, 0, zero16);
+        sum_group(s1, false);
+        store_block_sum(beg + b);
+        interleave_step<8, 6>();
+        __builtin_amdgcn_sched_barrier(0);
+        // step 4(b+1)+1: S of group 1, the sum of group 0 of b+1
+        s1 = qk_group<D>(kh0, qf, 1, zero16);
+        sum_group(s0, true);
+        interleave_step<8, 6>();
+        __builtin_amdgcn_sched_barrier(0);
+        ent = en;
+      }
+    }
+    // drain: the sum of the last group 3, the last block's sum
+    sum_group(s1, false);
+    store_block_sum(end - 1);
+  };
+
   // Fast pass with PV: one software pipeline over the whole row.  Step t
   // (t = 4b + g for group g of block b) issues the QK^T MFMAs of group t, the
   // PV MFMAs of group t-2 and the softmax of group t-1, which do not depend
@@ -1253,7 +1341,7 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
     }
   };
 
-  if constexpr (PV) run_fast_pv(); else run_fast();
+  if constexpr (PV) run_fast_pv(); else run_fast_lse();
   float l_all = l_run + __shfl_xor(l_run, 32, 64);
   const float pad_mass = (float)npad * __builtin_amdgcn_exp2f(-m_run);
   l_all -= pad_mass;
