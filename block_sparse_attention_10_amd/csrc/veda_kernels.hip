@@ -599,6 +599,149 @@ __global__ void __launch_bounds__(64) select_kernel(DevPlan p, const float* __re
   }
 }
 
+// The same selection for long rows (more than 512 key tiles), with the row
+// staged in LDS: the order keys and key segments are read from memory once,
+// and the four radix passes and the final pass read LDS, where select_kernel
+// reads a 4.5 KB row from the cache five times.  Short rows stay with
+// select_kernel: their keys stay in the L1 cache between passes anyway.  The
+// LDS (keys, 8-bit segments, one 256-bin histogram; about 7 KB for 1,152
+// columns) is kept small so that many rows share a CU.
+template <int CH>
+__global__ void __launch_bounds__(64) select_staged_kernel(DevPlan p, const float* __restrict__ scores,
+                                                          int32_t* __restrict__ row_ptr_out,
+                                                          int32_t* __restrict__ col_idx,
+                                                          uint8_t* __restrict__ dense_mask) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_key[64 * CH];
+  __shared__ int8_t s_seg[64 * CH];   // key segment of the column, -1 past the row
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int h = p.row_head[t];
+  const DevShape& sh = p.shape[p.head_shape[h]];
+  const int n = sh.num_tiles;
+  const int i = (int)(t - p.head_tile_off[h]);
+  const int S = p.num_segments;
+  const int A = sh.tile_seg[i];
+  const float* srow = scores + p.head_pair_off[h] + (int64_t)i * n;
+  const int32_t rp0 = p.row_ptr[t];
+  const int32_t row_len = p.row_ptr[t + 1] - rp0;
+  const int nch = (n + 63) / 64;
+  if (lane == 0) {
+    row_ptr_out[t] = rp0;
+    if (t == p.total_tiles - 1) row_ptr_out[t + 1] = p.row_ptr[t + 1];
+  }
+  for (int r = 0; r < nch; ++r) {
+    const int j = 64 * r + lane;
+    const bool in = j < n;
+    s_key[j] = in ? order_key(srow[j]) : 0u;
+    s_seg[j] = (int8_t)(in ? sh.tile_seg[j] : -1);
+  }
+  // per segment: mode 0 = all, 1 = diagonal only / nothing, 2 = radix threshold
+  uint32_t thr[kMaxSegments];
+  int32_t rem[kMaxSegments], mode[kMaxSegments];
+#pragma unroll
+  for (int B = 0; B < kMaxSegments; ++B) {
+    thr[B] = 0u;
+    rem[B] = 0;
+    mode[B] = 1;
+    if (B >= S) continue;
+    const int first = sh.seg_first[B], count = sh.seg_count[B];
+    const int kb = sh.budget[(int64_t)i * S + B];
+    if (kb >= count) {
+      mode[B] = 0;
+      continue;
+    }
+    const int diag = (A == B) ? i : -1;
+    int need = kb - (diag >= 0 ? 1 : 0);
+    if (need <= 0) continue;
+    mode[B] = 2;
+    uint32_t prefix = 0u, pmask = 0u;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int b = lane; b < 256; b += 64) hist[b] = 0u;
+      __syncthreads();   // also makes the staged row visible on the first pass
+      for (int j = first + lane; j < first + count; j += 64) {
+        if (j == diag) continue;
+        const uint32_t key = s_key[j];
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
+                     c3 = hist[4 * lane + 3];
+      const uint32_t mine = c0 + c1 + c2 + c3;
+      // inclusive suffix sum over lanes: sum of bins of this lane and above
+      uint32_t suf = mine;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_down(suf, off, 64);
+        if (lane + off < 64) suf += y;
+      }
+      uint32_t above = suf - mine;
+      int found = 0, digit = 0, need_left = 0;
+      if (above < (uint32_t)need && (uint32_t)need <= suf) {
+        const uint32_t cs[4] = {c0, c1, c2, c3};
+        for (int b = 3; b >= 0; --b) {
+          if (above + cs[b] >= (uint32_t)need) {
+            digit = 4 * lane + b;
+            need_left = need - (int)above;
+            found = 1;
+            break;
+          }
+          above += cs[b];
+        }
+      }
+      const uint64_t fm = __ballot(found);
+      const int src = fm ? __ffsll((unsigned long long)fm) - 1 : 0;
+      digit = __shfl(digit, src, 64);
+      need = __shfl(need_left, src, 64);
+      prefix |= (uint32_t)digit << shift;
+      pmask |= 255u << shift;
+      __syncthreads();
+    }
+    thr[B] = prefix;
+    rem[B] = need;
+  }
+  __syncthreads();   // the staged row is visible even when no segment needed a radix pass
+  // final pass over the columns in ascending order
+  int32_t eq_seen[kMaxSegments];
+#pragma unroll
+  for (int B = 0; B < kMaxSegments; ++B) eq_seen[B] = 0;
+  int32_t pos = 0;
+  const uint64_t below = lanes_below();
+  uint8_t* mrow = dense_mask ? dense_mask + p.head_pair_off[h] + (int64_t)i * n : nullptr;
+  for (int r = 0; r < nch; ++r) {
+    const int j = 64 * r + lane;
+    const bool in = j < n;
+    const int Bj = s_seg[j];
+    const uint32_t key = s_key[j];
+    bool sel = false;
+#pragma unroll
+    for (int B = 0; B < kMaxSegments; ++B) {
+      if (B >= S) continue;
+      const bool mine = (Bj == B);
+      if (mode[B] == 0) {
+        sel = sel || mine;
+        continue;
+      }
+      const bool isdiag = mine && (A == B) && (j == i);
+      if (mode[B] == 1) {
+        sel = sel || isdiag;
+        continue;
+      }
+      const bool eq = mine && !isdiag && key == thr[B];
+      const uint64_t em = __ballot(eq);
+      const int rank = eq_seen[B] + __popcll(em & below);
+      if (mine) sel = isdiag || (key > thr[B] && !isdiag) || (eq && rank < rem[B]);
+      eq_seen[B] += __popcll(em);
+    }
+    const uint64_t sm = __ballot(sel);
+    const int32_t at = pos + __popcll(sm & below);
+    if (sel && at < row_len) col_idx[rp0 + at] = j;  // a row never exceeds its budget
+    pos += __popcll(sm);
+    if (mrow && in) mrow[j] = sel ? 1 : 0;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // block-sparse attention forward
 // ---------------------------------------------------------------------------
@@ -2382,8 +2525,17 @@ hipError_t launch_score(const DevPlan& p, const void* q, const void* k, const fl
 
 hipError_t launch_select(const DevPlan& p, const float* scores, int32_t* row_ptr, int32_t* col_idx,
                          uint8_t* dense_mask, hipStream_t s) {
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)p.total_tiles), dim3(64), 0, s, p, scores, row_ptr, col_idx,
-                     dense_mask);
+  int maxn = 0;
+  for (int g = 0; g < p.num_shapes; ++g) maxn = maxn > p.shape[g].num_tiles ? maxn : p.shape[g].num_tiles;
+  const dim3 grid((unsigned)p.total_tiles), block(64);
+  // rows of 513 .. 2048 key tiles are staged in LDS (sized to 1,152 or 2,048
+  // columns); shorter and longer rows read the scores in every pass
+  if (maxn > 512 && maxn <= 1152)
+    hipLaunchKernelGGL(select_staged_kernel<18>, grid, block, 0, s, p, scores, row_ptr, col_idx, dense_mask);
+  else if (maxn > 1152 && maxn <= 2048)
+    hipLaunchKernelGGL(select_staged_kernel<32>, grid, block, 0, s, p, scores, row_ptr, col_idx, dense_mask);
+  else
+    hipLaunchKernelGGL(select_kernel, grid, block, 0, s, p, scores, row_ptr, col_idx, dense_mask);
   return hipGetLastError();
 }
 

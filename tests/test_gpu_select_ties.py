@@ -4,6 +4,9 @@ per-row budgets with a forced diagonal; ties go to the lowest key tile index
 and -0 equals +0, as the oracle's sort key (score descending, index ascending)
 fixes them).
 
+Rows of more than 512 key tiles run a second kernel that stages the row in
+LDS; three plans here have such rows.
+
 Random fp32 scores essentially never tie, so the parity tests on generated
 inputs never reach the kernel's tie path (equal keys ranked by ballot order
 across 64-column chunks) or its -0/+0 canonicalisation.  Here the scores are
@@ -41,6 +44,15 @@ def _plans():
         wl.Workload(99, "three_video_segments", (wl.Segment(V, (2, 8, 16), 0), wl.Segment(V, (4, 16, 16), 256),
                                                  wl.Segment(V, (2, 24, 16), 1280)),
                     2, 64, ((1, 8, 16), (2, 8, 8)), wl.KEEP_RATIO, 1, 4),
+        # rows longer than 512 key tiles take the LDS-staged selection (up to
+        # 1,152 and up to 2,048 columns), also with several key segments
+        wl.Workload(96, "long_rows_768", (wl.Segment(V, (32, 48, 64), 0),), 1, 64, ((2, 8, 8),),
+                    wl.KEEP_RATIO, locality_bias=False),
+        wl.Workload(95, "long_rows_1280", (wl.Segment(V, (40, 64, 64), 0),), 1, 64, ((2, 8, 8),),
+                    wl.KEEP_RATIO, locality_bias=False),
+        wl.Workload(94, "long_rows_three_segments", (wl.Segment(V, (8, 32, 32), 0), wl.Segment(V, (16, 48, 64), 8192),
+                                                     wl.Segment(DN, (1, 1, 12800), 57344)),
+                    2, 64, ((2, 8, 8), (4, 4, 8)), wl.KEEP_RATIO, 1, 4, locality_bias=False),
     ]
 
 
