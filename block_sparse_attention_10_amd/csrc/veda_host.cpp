@@ -501,7 +501,7 @@ veda_status veda_plan_create(const veda_plan_desc* d, veda_plan** out) {
   in.max_tiles_per_head = maxtiles;
   in.score_workspace_bytes = score_workspace_bytes(tiles, d->head_dim);
   in.transpose_workspace_bytes = transpose_workspace_bytes(in.total_pairs, in.total_tiles);
-  in.bwd_workspace_bytes = bwd_workspace_bytes(in.total_rows, in.total_tiles);
+  in.bwd_workspace_bytes = bwd_workspace_bytes(in.total_rows, in.total_tiles, in.nnz);
   in.heat_workspace_bytes = heat_workspace_bytes(in.nnz);
   in.reduce_workspace_bytes = reduce_workspace_bytes(H, maxtiles);
   build_attn_order(*p);

@@ -21,10 +21,14 @@ inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 inline int64_t transpose_workspace_bytes(int64_t total_pairs, int64_t total_tiles) {
   return align256(total_pairs) + align256(total_tiles * 4);
 }
-// Per permuted row: (lse * log2(e), rowsum(dO * O)), fp32 pairs [R, 2]; then
-// the dispatch order of the key tiles, int32 [T].
-inline int64_t bwd_workspace_bytes(int64_t total_rows, int64_t total_tiles) {
-  return align256(total_rows * 8) + align256(total_tiles * 4);
+// Per permuted row: (lse * log2(e), rowsum(dO * O)), fp32 pairs [R, 2]; the
+// dispatch order of the key tiles, int32 [T]; per transposed-list entry its
+// position in the CSR, int32 [nnz]; then dS of every kept block as bf16
+// (kBwdBlockBytes each, in the order of the CSR), written by the dK/dV pass
+// and read by the dQ pass.
+constexpr int64_t kBwdBlockBytes = 128 * 128 * 2;
+inline int64_t bwd_workspace_bytes(int64_t total_rows, int64_t total_tiles, int64_t nnz) {
+  return align256(total_rows * 8) + align256(total_tiles * 4) + align256(nnz * 4) + nnz * kBwdBlockBytes;
 }
 // One fp32 per (block, query slot): each block's sum of p per query.
 inline int64_t heat_workspace_bytes(int64_t nnz) { return align256(nnz * 128 * 4); }

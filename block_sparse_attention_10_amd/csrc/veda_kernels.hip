@@ -1965,27 +1965,37 @@ __global__ void __launch_bounds__(1024) csc_scan_kernel(const int32_t* __restric
 // backward: helpers
 // ---------------------------------------------------------------------------
 
-// Dispatch order of the dK/dV workgroups: key tiles by descending list length
-// (a counting sort in one workgroup), so the long lists of popular key tiles
-// start first and the grid ends evenly.  The order inside one length is that
-// of the LDS atomics; it only changes the schedule, never a result.
-constexpr int kOrderBins = 4096;
+// Dispatch order of the dK/dV workgroups.  Workgroup b runs on XCD b mod 8,
+// so the key tiles are cut into 8 contiguous index ranges of equal count
+// (one per XCD: whole heads or runs of neighbouring tiles, whose lists share
+// query tiles in that XCD's L2), and inside each range ordered by descending
+// list length (a counting sort over 8 x 1,024 length bins in one
+// workgroup), so that each XCD starts its long lists first and ends evenly.
+// Range x's k-th tile gets slot 8k + x.  The order inside one length bin is
+// that of the LDS atomics; it only changes the schedule, never a result.
+constexpr int kXcds = 8;
+constexpr int kOrderBins = 1024;   // list lengths 0 .. 1,023; longer lists share the top bin
 __global__ void __launch_bounds__(1024) bwd_order_kernel(const int32_t* __restrict__ col_ptr, int64_t n,
                                                         int32_t* __restrict__ order) {
-  __shared__ int32_t start[kOrderBins];
+  constexpr int NB = kXcds * kOrderBins;
+  __shared__ int32_t start[NB];
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
-  for (int b = tid; b < kOrderBins; b += 1024) start[b] = 0;
+  const int64_t per = n / kXcds, extra = n % kXcds;
+  auto range = [&](int64_t t) -> int {   // ranges 0 .. extra-1 hold per + 1 tiles
+    return t < (per + 1) * extra ? (int)(t / (per + 1)) : (int)(extra + (t - (per + 1) * extra) / per);
+  };
+  for (int b = tid; b < NB; b += 1024) start[b] = 0;
   __syncthreads();
-  auto bin = [&](int64_t t) {   // bin 0 holds the longest lists
-    return kOrderBins - 1 - min(col_ptr[t + 1] - col_ptr[t], kOrderBins - 1);
+  auto bin = [&](int64_t t) {   // inside a range, bin 0 holds the longest lists
+    return range(t) * kOrderBins + kOrderBins - 1 - min(col_ptr[t + 1] - col_ptr[t], kOrderBins - 1);
   };
   for (int64_t t = tid; t < n; t += 1024) atomicAdd(&start[bin(t)], 1);
   __syncthreads();
-  int32_t loc[kOrderBins / 1024], sum = 0;
+  int32_t loc[NB / 1024], sum = 0;
 #pragma unroll
-  for (int u = 0; u < kOrderBins / 1024; ++u) {
-    loc[u] = start[(kOrderBins / 1024) * tid + u];
+  for (int u = 0; u < NB / 1024; ++u) {
+    loc[u] = start[(NB / 1024) * tid + u];
     sum += loc[u];
   }
   part[tid] = sum;
@@ -1998,12 +2008,16 @@ __global__ void __launch_bounds__(1024) bwd_order_kernel(const int32_t* __restri
   }
   int32_t run = part[tid] - sum;
 #pragma unroll
-  for (int u = 0; u < kOrderBins / 1024; ++u) {
-    start[(kOrderBins / 1024) * tid + u] = run;
+  for (int u = 0; u < NB / 1024; ++u) {
+    start[(NB / 1024) * tid + u] = run;
     run += loc[u];
   }
   __syncthreads();
-  for (int64_t t = tid; t < n; t += 1024) order[atomicAdd(&start[bin(t)], 1)] = (int32_t)t;
+  for (int64_t t = tid; t < n; t += 1024) {
+    const int x = range(t);
+    const int64_t k = atomicAdd(&start[bin(t)], 1) - (x * per + min((int64_t)x, extra));   // rank inside the range
+    order[k < per ? kXcds * k + x : kXcds * per + x] = (int32_t)t;
+  }
 }
 
 // aux[r] = (lse[r] * log2(e), sum_d dO[r][d] * O[r][d]) in fp32 for every
@@ -2163,6 +2177,32 @@ __device__ __forceinline__ void tr_group(const uint16_t* __restrict__ tile, cons
   }
 }
 
+// dS of one 32-key x 32-query block as a dK wave holds it (pg: lane (ln, hl)
+// has key ln, queries 16 s2 + 8 hl .. +7), stored in the order the dQ pass
+// takes it as its B operand (lane (ln, hl) of 16-key step s2: query ln, keys
+// 16 s2 + 8 hl .. +7; 1 KB per step).  The transpose goes through 2 KB of LDS
+// that only this wave touches meanwhile (`sb`): 32 rows of 32 queries, one
+// per key, then two transpose reads per step.
+__device__ __forceinline__ void store_ds_block(char* sb, const bf16x8 (&pg)[2], u32x4* __restrict__ dst) {
+  const int lane = lane_id(), ln = lane & 31, hl = lane >> 5;
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+    *reinterpret_cast<u32x4*>(sb + ln * 64 + 32 * s2 + 16 * hl) = __builtin_bit_cast(u32x4, pg[s2]);
+  asm volatile("" ::: "memory");
+  // in each 16-lane group G, lane 4x + a names key 8(G >> 1) + 4r + x (+16 s2)
+  // and queries 16(G & 1) + 4a .. +3
+  const int G = lane >> 4, x = (lane >> 2) & 3, a = lane & 3;
+  const int rd = (8 * (G >> 1) + x) * 64 + (16 * (G & 1) + 4 * a) * 2;
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const s16x4 lo = tr_read(reinterpret_cast<const uint16_t*>(sb + rd + 16 * s2 * 64));
+    const s16x4 hi = tr_read(reinterpret_cast<const uint16_t*>(sb + rd + (16 * s2 + 4) * 64));
+    const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), dst + 64 * s2 + lane);
+  }
+}
+
 // The wave's B operand for 32 rows of a permuted tile: lane (ln, hl) holds
 // row r0 + ln, channels 16s + 8hl .. +7.
 template <int D>
@@ -2219,8 +2259,8 @@ template <int D>
 __global__ void __launch_bounds__(kBwdThreads, 1) attn_bwd_dkdv_kernel(
     DevPlan p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ d_o, const float2* __restrict__ aux, const int32_t* __restrict__ col_ptr,
-    const int32_t* __restrict__ row_idx, const int32_t* __restrict__ order, float scale_log2, float scale,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+    const int32_t* __restrict__ row_idx, const int32_t* __restrict__ order, const int32_t* __restrict__ pos,
+    float scale_log2, float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, u32x4* __restrict__ xds) {
   constexpr int TS = kTile * D;   // bf16 elements of a row tile
   // Q tile + its 128 (lse2, Dsum) pairs, and the dO tile, per buffer set
   __shared__ __attribute__((aligned(16))) uint16_t q0[TS + 512];
@@ -2260,8 +2300,9 @@ __global__ void __launch_bounds__(kBwdThreads, 1) attn_bwd_dkdv_kernel(
     f32x16 acc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-    // the products of one query tile held in (qc, dc)
-    auto tile = [&](const uint16_t* qc, const uint16_t* dc) {
+    // the products of one query tile held in (qc, dc); xb: the block's dS
+    // in the workspace (nullptr: no CSR position, nothing stored)
+    auto tile = [&](const uint16_t* qc, const uint16_t* dc, u32x4* xb) {
       const BwdOffsets<D> o = bwd_offsets_here<D>();
       const float2* xc = reinterpret_cast<const float2*>(qc + TS);
 #pragma unroll 1
@@ -2304,19 +2345,26 @@ __global__ void __launch_bounds__(kBwdThreads, 1) attn_bwd_dkdv_kernel(
             }
             pg[s2] = __builtin_bit_cast(bf16x8, dk4);
           }
+          if (xb) store_ds_block(reinterpret_cast<char*>(&xp[g & 1][w][0][0]), pg, xb + (g * 4 + w) * 128);
           tr_group<D>(qc, o, pg, g, acc);
         }
       }
+    };
+    // where block e's dS goes (only the dK waves store it)
+    auto xdst = [&](int e) -> u32x4* {
+      if constexpr (!DK) return nullptr;
+      const int pe = uni(pos[e]);
+      return pe >= 0 ? xds + (int64_t)pe * (kBwdBlockBytes / 16) : nullptr;
     };
     if (e0 < e1) copy(q0, d0, uni(row_idx[e0]));
     dma_sync<0>();
     for (int e = e0; e < e1; e += 2) {
       if (e + 1 < e1) copy(q1, d1, uni(row_idx[e + 1]));
-      tile(q0, d0);
+      tile(q0, d0, xdst(e));
       dma_sync<0>();                // tile e+1 has landed; every wave is done with set 0
       if (e + 1 >= e1) break;
       if (e + 2 < e1) copy(q0, d0, uni(row_idx[e + 2]));
-      tile(q1, d1);
+      tile(q1, d1, xdst(e + 1));
       dma_sync<0>();
     }
     const bool pad = 32 * w + ln >= nvk;
@@ -2335,89 +2383,98 @@ __global__ void __launch_bounds__(kBwdThreads, 1) attn_bwd_dkdv_kernel(
 // backward: dQ over the row lists
 // ---------------------------------------------------------------------------
 //
+// dQ = scale dS K per query tile, with dS read back from the workspace where
+// the dK/dV pass left it (one 32 KB block per kept block, in CSR order, in
+// this kernel's operand order), so S and dP are not computed a second time.
 // One workgroup of 8 waves per (head, query tile i): wave w & 3 owns queries
-// 32(w & 3) .. +31 as in the forward, and wave w >> 2 of the pair takes key
-// groups 2(w >> 2) and 2(w >> 2) + 1 of every key tile.  S^T = K Q^T and
-// dP^T = V dO^T (A = K and V rows from LDS, B = Q and dO rows in registers),
-// P^T and dS^T per lane (lse and Dsum are per query, i.e. per lane), dQ^T +=
-// K^T dS^T (A = the K tile read transposed).  The two partial dQ of a pair
-// are summed through LDS at the end.  Key tiles are double-buffered like the
-// query tiles of the dK/dV kernel.
+// 32(w & 3) .. +31 and wave w >> 2 of the pair key groups 2(w >> 2) and
+// 2(w >> 2) + 1 of every key tile; dQ^T += K^T dS^T (A = the K tile read
+// transposed, B = the dS operands, one 16-byte LDS read per lane each).  K
+// tiles are double-buffered in LDS and the dS blocks, a stream from HBM,
+// go through a ring of three LDS buffers: while block e computes, K tile
+// e + 1 and dS block e + 2 are in flight.  The two partial dQ of a pair are
+// summed through LDS at the end.
 template <int D>
 __global__ void __launch_bounds__(kBwdThreads, 1) attn_bwd_dq_kernel(
-    DevPlan p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ d_o, const float2* __restrict__ aux, const int32_t* __restrict__ row_ptr,
-    const int32_t* __restrict__ col_idx, float scale_log2, float scale, uint16_t* __restrict__ dq) {
+    DevPlan p, const uint16_t* __restrict__ k, const u32x4* __restrict__ xds, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ col_idx, float scale, uint16_t* __restrict__ dq) {
   constexpr int TS = kTile * D;
+  constexpr int XS = (int)(kBwdBlockBytes / 2);   // bf16 elements of a dS block
   __shared__ __attribute__((aligned(16))) uint16_t k0[TS];
-  __shared__ __attribute__((aligned(16))) uint16_t v0[TS];
   __shared__ __attribute__((aligned(16))) uint16_t k1[TS];
-  __shared__ __attribute__((aligned(16))) uint16_t v1[TS];
+  __shared__ __attribute__((aligned(16))) uint16_t xr0[XS];
+  __shared__ __attribute__((aligned(16))) uint16_t xr1[XS];
+  __shared__ __attribute__((aligned(16))) uint16_t xr2[XS];
   const int t = blockIdx.x;
   const int h = uni(p.row_head[t]);
   const DevShape& sh = p.shape[uni(p.head_shape[h])];
   const int nt = sh.num_tiles;
   const int i = t - uni(p.head_tile_off[h]);
   const int64_t hrow = uni64(p.head_row_off[h]);
-  const int wave = threadIdx.x >> 6, w = wave & 3, kh = wave >> 2, lane = lane_id();
-  const float c = scale_log2;
+  const int wave = uni(threadIdx.x >> 6), w = wave & 3, kh = wave >> 2, lane = lane_id();
   const int64_t qrow0 = hrow + (int64_t)kTile * i + 32 * w;
-  const int ln = lane & 31;
   const int64_t tile_bytes = (int64_t)kTile * D * 2;
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + hrow * D, nt * tile_bytes);
-  const __amdgpu_buffer_rsrc_t rv = head_rsrc(v + hrow * D, nt * tile_bytes);
   const int loff = brow_lane_offset<D>(threadIdx.x);
-  bf16x8 qf[D / 16], dof[D / 16];
-  load_bop<D>(qf, q, qrow0);
-  load_bop<D>(dof, d_o, qrow0);
-  const float2 xq = aux[qrow0 + ln];
-  const float l2 = xq.x, dsq = xq.y;
   f32x16 dqacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dqacc[db] = f32x16{};
-  auto copy = [&](uint16_t* kd, uint16_t* vd, int jj) {
-    jj = min(max(jj, 0), nt - 1);   // stay inside the head
+  auto copy_k = [&](uint16_t* kd, int e) {
+    const int jj = min(max(uni(col_idx[e]), 0), nt - 1);   // stay inside the head
     dma_row_tile<D>(kd, rk, jj * (int)tile_bytes, loff, wave);
-    dma_row_tile<D>(vd, rv, jj * (int)tile_bytes, loff, wave);
   };
-  auto tile = [&](const uint16_t* kc, const uint16_t* vc) {
-    const BwdOffsets<D> o = bwd_offsets_here<D>();
+  // dS block e, a plain 32 KB copy (four 16-byte pieces per thread), with
+  // the non-temporal cache policy: each block is read once, the K tiles
+  // should keep the L2
+  constexpr int kStreamLoad = 2;
+  auto copy_x = [&](uint16_t* xd, int e) {
+    const __amdgpu_buffer_rsrc_t rx = head_rsrc(xds + (int64_t)e * (kBwdBlockBytes / 16), kBwdBlockBytes);
+#pragma unroll
+    for (int it = 0; it < (int)(kBwdBlockBytes / (16 * kBwdThreads)); ++it)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, xd + it * 8 * kBwdThreads + 512 * wave, 16, 16 * (int)threadIdx.x,
+                                               it * 16 * kBwdThreads, 0, kStreamLoad);
+  };
+  constexpr int XCOPY = (int)(kBwdBlockBytes / (16 * kBwdThreads));   // copy instructions per dS block
+  const BwdOffsets<D> o = bwd_offsets<D>(lane);
+  auto tile = [&](const uint16_t* kc, const uint16_t* xc) {
+    // the wave's operands: key groups 2kh, 2kh+1, two 16-key steps each
+    const u32x4* xw = reinterpret_cast<const u32x4*>(xc) + (w * 4 + 2 * kh) * 128 + lane;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int kt = 2 * kh + u;
-      const f32x16 sg = brows_group<D>(kc, o, qf, kt);
-      const f32x16 dpg = brows_group<D>(vc, o, dof, kt);
-      bf16x8 dsp[2];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        u32x4 dk4;
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int r0 = 8 * s2 + 2 * e2, r1 = r0 + 1;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sg[r0], c, -l2));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sg[r1], c, -l2));
-          dk4[e2] = pack_bf16x2(p0 * (dpg[r0] - dsq), p1 * (dpg[r1] - dsq));
-        }
-        dsp[s2] = __builtin_bit_cast(bf16x8, dk4);
-      }
-      tr_group<D>(kc, o, dsp, kt, dqacc);
+      const bf16x8 xv[2] = {__builtin_bit_cast(bf16x8, xw[u * 128]), __builtin_bit_cast(bf16x8, xw[u * 128 + 64])};
+      tr_group<D>(kc, o, xv, 2 * kh + u, dqacc);
     }
   };
   const int e0 = uni(row_ptr[t]), e1 = uni(row_ptr[t + 1]);
-  if (e0 < e1) copy(k0, v0, uni(col_idx[e0]));
+  // step e: K tile e+1 and dS block e+2 are issued, block e computes; the
+  // wait at its end leaves the copy of e+2 (issued last) in flight
+  auto step = [&](int e, const uint16_t* kc, uint16_t* kn, const uint16_t* xc, uint16_t* xn) {
+    if (e + 1 < e1) copy_k(kn, e + 1);
+    const bool x2 = e + 2 < e1;
+    if (x2) copy_x(xn, e + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    tile(kc, xc);
+    __builtin_amdgcn_sched_barrier(0);   // this block's products stay before the wait
+    if (x2) dma_sync<XCOPY>(); else dma_sync<0>();
+  };
+  if (e0 < e1) {
+    copy_k(k0, e0);
+    copy_x(xr0, e0);
+    if (e0 + 1 < e1) copy_x(xr1, e0 + 1);
+  }
   dma_sync<0>();
-  for (int e = e0; e < e1; e += 2) {
-    if (e + 1 < e1) copy(k1, v1, uni(col_idx[e + 1]));
-    tile(k0, v0);
-    dma_sync<0>();
-    if (e + 1 >= e1) break;
-    if (e + 2 < e1) copy(k0, v0, uni(col_idx[e + 2]));
-    tile(k1, v1);
-    dma_sync<0>();
+  int xi = 0;   // ring slot of block e
+#pragma unroll 1
+  for (int e = e0; e < e1; ++e) {
+    const bool odd = ((e - e0) & 1) != 0;
+    uint16_t* xc = xi == 0 ? xr0 : (xi == 1 ? xr1 : xr2);
+    uint16_t* xn = xi == 0 ? xr2 : (xi == 1 ? xr0 : xr1);   // the slot of block e + 2
+    step(e, odd ? k1 : k0, odd ? k0 : k1, xc, xn);
+    xi = xi == 2 ? 0 : xi + 1;
   }
   // pair reduction: the second wave of each pair parks its partial dQ in the
   // (now free) tile buffers, lane-major, the first adds it and stores
-  float* park = reinterpret_cast<float*>(w < 2 ? k0 : v0) + (w & 1) * (D / 2) * 64;
+  float* park = reinterpret_cast<float*>(w < 2 ? k0 : k1) + (w & 1) * (D / 2) * 64;
   if (kh == 1) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -2431,6 +2488,35 @@ __global__ void __launch_bounds__(kBwdThreads, 1) attn_bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) dqacc[db][r] += park[(16 * db + r) * 64 + lane];
     store_t_rows<D>(dq, qrow0, dqacc, scale, false);
+  }
+}
+
+// Position in the CSR of every transposed-list entry: for key tile t and
+// entry e (query tile i = row_idx[e] of the same head), the index of t's
+// head-local key tile in row i's ascending col_idx (binary search), or -1 if
+// the row does not hold it.  One wave per key tile.
+__global__ void __launch_bounds__(64) bwd_pos_kernel(DevPlan p, const int32_t* __restrict__ row_ptr,
+                                                    const int32_t* __restrict__ col_idx,
+                                                    const int32_t* __restrict__ col_ptr,
+                                                    const int32_t* __restrict__ row_idx, int32_t* __restrict__ pos) {
+  const int64_t t = blockIdx.x;
+  const int h = p.row_head[t];
+  const int64_t toff = p.head_tile_off[h];
+  const int n = p.shape[p.head_shape[h]].num_tiles;
+  const int j = (int)(t - toff);
+  const int e1 = col_ptr[t + 1];
+  for (int e = col_ptr[t] + threadIdx.x; e < e1; e += 64) {
+    const int64_t ti = toff + min(max(row_idx[e], 0), n - 1);
+    const int end = row_ptr[ti + 1];
+    int lo = row_ptr[ti], hi = end;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (col_idx[mid] < j)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    pos[e] = (lo < end && col_idx[lo] == j) ? lo : -1;
   }
 }
 
@@ -2643,29 +2729,33 @@ hipError_t launch_attn_bwd(const DevPlan& p, const void* q, const void* k, const
                            void* dv, void* workspace, hipStream_t s) {
   const int D = p.head_dim;
   const int64_t R = p.total_rows, T = p.total_tiles;
-  float2* aux = static_cast<float2*>(workspace);
-  int32_t* order = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + align256(R * 8));
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float2* aux = reinterpret_cast<float2*>(ws);
+  int32_t* order = reinterpret_cast<int32_t*>(ws + align256(R * 8));
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + align256(R * 8) + align256(T * 4));
+  u32x4* xds = reinterpret_cast<u32x4*>(ws + align256(R * 8) + align256(T * 4) + align256(p.nnz * 4));
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   const uint16_t* oo = static_cast<const uint16_t*>(o);
   const uint16_t* dd = static_cast<const uint16_t*>(d_o);
+  uint16_t* dqq = static_cast<uint16_t*>(dq);
+  uint16_t* dkk = static_cast<uint16_t*>(dk);
+  uint16_t* dvv = static_cast<uint16_t*>(dv);
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 gt((unsigned)T), gprep((unsigned)((R * (D / 8) + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL(bwd_order_kernel, dim3(1), dim3(1024), 0, s, col_ptr, T, order);
+  hipLaunchKernelGGL(bwd_pos_kernel, gt, dim3(64), 0, s, p, row_ptr, col_idx, col_ptr, row_idx, pos);
   if (D == 128) {
     hipLaunchKernelGGL(bwd_prep_kernel<128>, gprep, dim3(kThreads), 0, s, R, oo, dd, lse, aux);
-    hipLaunchKernelGGL(bwd_order_kernel, dim3(1), dim3(1024), 0, s, col_ptr, T, order);
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, gt, dim3(kBwdThreads), 0, s, p, qq, kk, vv, dd, aux, col_ptr, row_idx,
-                       order, scale_log2, scale, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, gt, dim3(kBwdThreads), 0, s, p, qq, kk, vv, dd, aux, row_ptr, col_idx,
-                       scale_log2, scale, static_cast<uint16_t*>(dq));
+                       order, pos, scale_log2, scale, dkk, dvv, xds);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, gt, dim3(kBwdThreads), 0, s, p, kk, xds, row_ptr, col_idx, scale, dqq);
   } else {
     hipLaunchKernelGGL(bwd_prep_kernel<64>, gprep, dim3(kThreads), 0, s, R, oo, dd, lse, aux);
-    hipLaunchKernelGGL(bwd_order_kernel, dim3(1), dim3(1024), 0, s, col_ptr, T, order);
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, gt, dim3(kBwdThreads), 0, s, p, qq, kk, vv, dd, aux, col_ptr, row_idx,
-                       order, scale_log2, scale, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, gt, dim3(kBwdThreads), 0, s, p, qq, kk, vv, dd, aux, row_ptr, col_idx,
-                       scale_log2, scale, static_cast<uint16_t*>(dq));
+                       order, pos, scale_log2, scale, dkk, dvv, xds);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, gt, dim3(kBwdThreads), 0, s, p, kk, xds, row_ptr, col_idx, scale, dqq);
   }
   return hipGetLastError();
 }

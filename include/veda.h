@@ -384,8 +384,13 @@ veda_status veda_mask_transpose(const veda_plan* plan, const int32_t* row_ptr, c
  * (same source).  With P = softmax over the valid keys of the kept blocks:
  *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
  *   dQ = scale dS K,  dK = scale dS^T Q.
- * dQ is gathered per query tile over the row lists, dK and dV per key tile
- * over the transposed lists, so no output is accumulated by atomics.
+ * dK and dV are gathered per key tile over the transposed lists, dQ per query
+ * tile over the row lists, so no output is accumulated by atomics.  The dK/dV
+ * pass leaves dS of every kept block (bf16, 32 KB per block) in the workspace
+ * for the dQ pass, which therefore computes neither S nor dP again; the
+ * transposed lists must be veda_mask_transpose's output for exactly this
+ * CSR, whose rows are ascending and free of repeats (veda_select_blocks'
+ * output): a kept block missing from them leaves its share of dQ undefined.
  *   q, k, v, o, d_o: device permuted bf16 [R, D] (o and lse as the forward
  *             wrote them with VEDA_LAYOUT_PERMUTED; d_o's padding rows zero,
  *             as veda_permute_tiles writes them; k's and v's padding rows
@@ -394,7 +399,9 @@ veda_status veda_mask_transpose(const veda_plan* plan, const int32_t* row_ptr, c
  *   row_ptr, col_idx: the forward's CSR; col_ptr, row_idx: its transpose
  *             (veda_mask_transpose)
  *   dq, dk, dv: device permuted bf16 [R, D]; rows of padding slots are zero
- *   workspace: device, bwd_workspace_bytes (contents overwritten)
+ *   workspace: device, bwd_workspace_bytes (contents overwritten): per row
+ *             two fp32, per key tile and per kept block one int32, and
+ *             nnz x 32 KB of dS
  * Errors: VEDA_ERR_INVALID_ARG if dq, dk, dv are not three different buffers
  * or one of them is an input or the workspace; VEDA_ERR_WORKSPACE if
  * workspace_bytes is too small. */

@@ -372,13 +372,18 @@ def _backward_case(w, seed, oracle=True):
     row_idx = torch.empty(plan.info["nnz"], dtype=torch.int32, device=dev)
     plan.transpose(g["row_ptr"], g["col_idx"], col_ptr, row_idx, plan.empty_bytes("transpose_workspace_bytes"))
     dq, dk, dv = plan.empty_perm(), plan.empty_perm(), plan.empty_perm()
+    # every byte of the workspace starts as 0xff (NaN as bf16 or fp32): a dS
+    # block the dQ pass read before the dK/dV pass wrote it would show up
+    ws = plan.empty_bytes("bwd_workspace_bytes").fill_(255)
     plan.backward(g["q_perm"], g["k_perm"], vp, o, dop, lse, g["row_ptr"], g["col_idx"], col_ptr, row_idx,
-                  w.softmax_scale, dq, dk, dv, plan.empty_bytes("bwd_workspace_bytes"))
+                  w.softmax_scale, dq, dk, dv, ws)
     torch.cuda.synchronize()
     op = vo.Plan.from_workload(w)
     sel = _csr_to_selection(op, g["row_ptr"].cpu().numpy(), g["col_idx"].cpu().numpy())
     if not oracle:
-        return op, sel, col_ptr, row_idx, {"inputs": (g["q_perm"], g["k_perm"], vp, dop), "grads": (dq, dk, dv)}, None
+        return op, sel, col_ptr, row_idx, {"inputs": (g["q_perm"], g["k_perm"], vp, dop), "grads": (dq, dk, dv),
+                                           "plan": plan, "o": o, "lse": lse, "row_ptr": g["row_ptr"],
+                                           "col_idx": g["col_idx"]}, None
     ref = vo.block_sparse_attention_backward(op, gp.f64(g["q_perm"]), gp.f64(g["k_perm"]), gp.f64(vp), gp.f64(dop),
                                              sel, w.softmax_scale)
     return op, sel, col_ptr, row_idx, (dq, dk, dv), ref
@@ -453,6 +458,26 @@ def test_oracle_mask_mass_and_recall():
     heat_ref = vo.block_heat(op, qp, kp, L, w.softmax_scale)
     for h in range(w.num_heads):
         assert np.max(np.abs(heat_gpu[h] - heat_ref[h])) <= gp.HEAT_ABS
+
+
+def test_backward_deterministic_and_workspace_independent():
+    """The backward twice on the same inputs, the second time over a
+    workspace cleared to zero instead of 0xff: dQ, dK, dV bitwise equal (dS
+    goes through the workspace, but every block is written before it is
+    read, and all sums run in a fixed order)."""
+    w = small_workloads()[1]
+    op, sel, col_ptr, row_idx, got, _ = _backward_case(w, w.index, oracle=False)
+    g = got["grads"]
+    q, k, vp, dop = got["inputs"]
+    plan = got["plan"]
+    dq2, dk2, dv2 = plan.empty_perm(), plan.empty_perm(), plan.empty_perm()
+    ws = plan.empty_bytes("bwd_workspace_bytes").zero_()
+    plan.backward(q, k, vp, got["o"], dop, got["lse"], got["row_ptr"], got["col_idx"], col_ptr, row_idx,
+                  w.softmax_scale, dq2, dk2, dv2, ws)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), g, (dq2, dk2, dv2)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+        assert torch.isfinite(a.float()).all(), name
 
 
 def test_backward_config3_one_head():

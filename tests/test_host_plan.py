@@ -86,6 +86,8 @@ def _compare_plan(w):
         assert np.array_equal(vb.veda_plan_copy_row_ptr(h), rp)
         assert info["nnz"] == rp[-1]
         assert info["heat_workspace_bytes"] >= info["nnz"] * 128 * 4
+        # the backward keeps dS of every kept block (128 x 128 bf16) besides its per-row pairs
+        assert info["bwd_workspace_bytes"] >= info["nnz"] * 128 * 128 * 2 + info["total_rows"] * 8
         assert info["reduce_workspace_bytes"] >= w.num_heads * max(32, -(-info["max_tiles_per_head"] // 16)) * 16
     finally:
         vb.veda_plan_destroy(h)
