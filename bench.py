@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (known bytes) to scale HBM counters")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="rough budget of the oracle sample")
+    ap.add_argument("--q-copy", action="store_true",
+                    help="write the permuted copy of Q in the layer and have the attention read it, instead of "
+                         "gathering Q's rows from the natural layout in the attention kernel")
     ap.add_argument("--backward", action="store_true",
                     help="also time the block-sparse backward (transposed lists, dK/dV and dQ) of the same layer")
     ap.add_argument("--search", action="store_true",
@@ -54,8 +57,12 @@ def parse():
 class Layer:
     """Device buffers and the calls of one attention layer."""
 
-    def __init__(self, w, inputs, vb):
+    def __init__(self, w, inputs, vb, q_copy=False):
         self.w, self.vb = w, vb
+        # q_copy: the permutation also writes the permuted copy of Q and the
+        # attention reads it; by default the attention gathers Q's rows from
+        # the natural [N, H, D] layout and no copy of Q is written
+        self.q_copy = q_copy
         self.plan = vb.Plan.from_workload(w)
         p = self.plan
         dev = "cuda"
@@ -84,13 +91,19 @@ class Layer:
         self.attn_events = []
         self.perm_events = []
 
+    def q_of(self, x):
+        """The Q operand of the attention calls and its layout."""
+        if self.q_copy:
+            return self.qp, self.vb.VEDA_LAYOUT_PERMUTED
+        return x["q"], self.vb.VEDA_LAYOUT_NATURAL
+
     def step(self, s, time_attn=False):
         vb, p, w = self.vb, self.plan, self.w
         x = self.sets[s % len(self.sets)]
         if time_attn:
             g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             g0.record()
-        p.permute_qkv(x["q"], x["k"], x["v"], self.qp, self.kp, self.vt, self.ws)
+        p.permute_qkv(x["q"], x["k"], x["v"], self.qp if self.q_copy else None, self.kp, self.vt, self.ws)
         if time_attn:
             g1.record()
             self.perm_events.append((g0, g1))
@@ -99,8 +112,9 @@ class Layer:
         if time_attn:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-        p.attention(self.qp, self.kp, self.vt, self.row_ptr, self.col, w.softmax_scale, self.o_nat, self.lse,
-                    o_layout=vb.VEDA_LAYOUT_NATURAL)
+        q, ql = self.q_of(x)
+        p.attention(q, self.kp, self.vt, self.row_ptr, self.col, w.softmax_scale, self.o_nat, self.lse,
+                    o_layout=vb.VEDA_LAYOUT_NATURAL, q_layout=ql)
         if time_attn:
             e1.record()
             self.attn_events.append((e0, e1))
@@ -108,8 +122,8 @@ class Layer:
             d = self.dense
             d.select(self.scores, self.d_row_ptr, self.d_col)
             # the dense LSE and the block heat in one pass over all blocks
-            d.lse_heat(self.qp, self.kp, self.d_row_ptr, self.d_col, w.softmax_scale, self.d_lse, self.heat,
-                       self.heat_ws)
+            d.lse_heat(q, self.kp, self.d_row_ptr, self.d_col, w.softmax_scale, self.d_lse, self.heat,
+                       self.heat_ws, q_layout=ql)
             p.select(self.heat, self.o_row_ptr, self.o_col)
             p.mask_mass(self.heat, self.row_ptr, self.col, self.m_pred)
             p.mask_mass(self.heat, self.o_row_ptr, self.o_col, self.m_orc)
@@ -232,7 +246,7 @@ def main():
     w = wl.workload(args.config)
     print("bench: generating inputs for %s" % w.describe(), file=sys.stderr, flush=True)
     inputs = [wl.make_inputs(w, seed=s) for s in wl.rotation_seeds(w)]
-    layer = Layer(w, inputs, vb)
+    layer = Layer(w, inputs, vb, q_copy=args.q_copy)
     p = layer.plan
     nnz = p.info["nnz"]
     flops_attn = 4.0 * 128 * 128 * w.head_dim * nnz
@@ -289,6 +303,8 @@ def main():
         "attn_valid_only_tflops": round(valid_flops / (attn_avg * 1e-3) / 1e12, 2),
         "attn_cold_cache": cold,
         "permute_qkv": perm,
+        "q_operand": "permuted copy written by the permutation" if args.q_copy else
+                     "natural [N, H, D] rows gathered by the attention kernel (no permuted copy of Q)",
         "bf16_gemm_reference": dict(gemm, attn_kernel_over_gemm=round(attn_tflops / gemm["tflops"], 4)),
         "library": vb.loaded_library(),
     }
@@ -336,7 +352,8 @@ def permute_rate(layer, w):
     p = layer.plan
     ms = float(np.mean([a.elapsed_time(b) for a, b in layer.perm_events]))
     d = w.head_dim
-    nbytes = (3 * w.num_tokens * w.num_heads * d * 2 + 3 * p.R * d * 2 + 2 * p.T * 3 * d * 4)
+    copies = 3 if layer.q_copy else 2      # permuted K and V^T (and Q with --q-copy)
+    nbytes = (3 * w.num_tokens * w.num_heads * d * 2 + copies * p.R * d * 2 + 2 * p.T * 3 * d * 4)
     a = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
     b = torch.empty_like(a)
     for _ in range(3):
@@ -387,10 +404,11 @@ def attention_cold(layer, n):
     for s in range(n):
         layer.step(s)                      # this set's permutation and mask
         scrub.fill_(float(s))
+        q, ql = layer.q_of(layer.sets[s % len(layer.sets)])
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        p.attention(layer.qp, layer.kp, layer.vt, layer.row_ptr, layer.col, w.softmax_scale, layer.o_nat,
-                    layer.lse, o_layout=vb.VEDA_LAYOUT_NATURAL)
+        p.attention(q, layer.kp, layer.vt, layer.row_ptr, layer.col, w.softmax_scale, layer.o_nat,
+                    layer.lse, o_layout=vb.VEDA_LAYOUT_NATURAL, q_layout=ql)
         e1.record()
         torch.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
@@ -406,6 +424,8 @@ def time_backward(layer, w, steps):
     p, vb = layer.plan, layer.vb
     dev = "cuda"
     x = layer.sets[0]
+    layer.step(0)                                          # K, V^T and the mask of input set 0
+    p.permute(x["q"], layer.qp, vb.VEDA_PERMUTE_FORWARD)   # the backward takes permuted Q
     vp, dop, o = p.empty_perm(), p.empty_perm(), p.empty_perm()
     p.permute(x["v"], vp, vb.VEDA_PERMUTE_FORWARD)
     gen = torch.Generator().manual_seed(5)

@@ -89,9 +89,9 @@ _SIGS = {
     "veda_permute_qkv": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "veda_score_pooled": (_I32, [_P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "veda_select_blocks": (_I32, [_P, _P, _P, _P, _P, _P]),
-    "veda_block_sparse_attn_fwd": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _P, _P, _P]),
+    "veda_block_sparse_attn_fwd": (_I32, [_P, _P, _I32, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _P, _P, _P]),
     "veda_block_heat": (_I32, [_P, _P, _P, _P, ctypes.c_float, _P, _P]),
-    "veda_dense_lse_heat": (_I32, [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
+    "veda_dense_lse_heat": (_I32, [_P, _P, _I32, _P, _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
     "veda_mask_mass": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "veda_output_error": (_I32, [_P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "veda_mask_transpose": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -101,6 +101,7 @@ _SIGS = {
     "veda_score_tiles_noalloc": (_I32, [_P, _P, _P, _P, _P, _P, _P]),
 }
 EXPORTED = tuple(_SIGS)
+ABI_VERSION = 8   # the signatures above; a library built from other sources is refused
 
 _lib = None
 
@@ -117,6 +118,10 @@ def lib() -> ctypes.CDLL:
             fn = getattr(l, name)
             fn.restype = res
             fn.argtypes = args
+        if l.veda_abi_version() != ABI_VERSION:
+            raise ImportError("%s has ABI version %d, this binding needs %d; rebuild it with "
+                              "python -m block_sparse_attention_10_amd.build" % (LIB_PATH, l.veda_abi_version(),
+                                                                                 ABI_VERSION))
         _lib = l
     return _lib
 
@@ -263,9 +268,9 @@ def veda_select_blocks(plan: int, scores, row_ptr, col_idx, dense_mask=None, str
 
 def veda_block_sparse_attn_fwd(plan: int, q, k, v_t, row_ptr, col_idx, softmax_scale: float, o,
                                o_layout: int = VEDA_LAYOUT_PERMUTED, lse=None, blocks_visited=None,
-                               stream=None) -> None:
-    _check(lib().veda_block_sparse_attn_fwd(plan, _ptr(q), _ptr(k), _ptr(v_t), _ptr(row_ptr), _ptr(col_idx),
-                                            float(softmax_scale), _ptr(o), int(o_layout), _ptr(lse),
+                               stream=None, q_layout: int = VEDA_LAYOUT_PERMUTED) -> None:
+    _check(lib().veda_block_sparse_attn_fwd(plan, _ptr(q), int(q_layout), _ptr(k), _ptr(v_t), _ptr(row_ptr),
+                                            _ptr(col_idx), float(softmax_scale), _ptr(o), int(o_layout), _ptr(lse),
                                             _ptr(blocks_visited), _stream(stream)))
 
 
@@ -275,9 +280,10 @@ def veda_block_heat(plan: int, q, k, lse, softmax_scale: float, heat, stream=Non
 
 
 def veda_dense_lse_heat(plan: int, q, k, row_ptr, col_idx, softmax_scale: float, lse, heat, workspace,
-                        stream=None) -> None:
-    _check(lib().veda_dense_lse_heat(plan, _ptr(q), _ptr(k), _ptr(row_ptr), _ptr(col_idx), float(softmax_scale),
-                                     _ptr(lse), _ptr(heat), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+                        stream=None, q_layout: int = VEDA_LAYOUT_PERMUTED) -> None:
+    _check(lib().veda_dense_lse_heat(plan, _ptr(q), int(q_layout), _ptr(k), _ptr(row_ptr), _ptr(col_idx),
+                                     float(softmax_scale), _ptr(lse), _ptr(heat), _ptr(workspace),
+                                     _nbytes(workspace), _stream(stream)))
 
 
 def veda_mask_mass(plan: int, heat, row_ptr, col_idx, mass, workspace, stream=None) -> None:
@@ -408,7 +414,11 @@ class Plan:
         nat = (self.N, self.H, self.D)
         for t, n in ((q, "q"), (k, "k")):
             self._expect(t, nat, bf, n)
-        self._expect(q_perm, (self.R, self.D), bf, "q_perm")
+        if q_perm is None:      # Q pooled, not written (attention then reads natural Q)
+            if workspace is None:
+                raise ValueError("permute_qkv: q_perm=None needs the pooling workspace")
+        else:
+            self._expect(q_perm, (self.R, self.D), bf, "q_perm")
         self._expect(k_perm, (self.R, self.D), bf, "k_perm")
         if (v is None) != (v_t is None):
             raise ValueError("permute_qkv: give both v and v_t, or neither")
@@ -461,11 +471,18 @@ class Plan:
             self._expect(dense_mask, (self.info["total_pairs"],), torch.uint8, "dense_mask")
         veda_select_blocks(self.handle, scores, row_ptr, col_idx, dense_mask, stream)
 
+    def _expect_q(self, q, q_layout):
+        import torch
+        if q_layout == VEDA_LAYOUT_NATURAL:
+            self._expect(q, (self.N, self.H, self.D), torch.bfloat16, "q")
+        else:
+            self._expect(q, (self.R, self.D), torch.bfloat16, "q")
+
     def attention(self, q, k, v_t, row_ptr, col_idx, scale, o, lse=None, visited=None, stream=None,
-                  o_layout=VEDA_LAYOUT_PERMUTED):
+                  o_layout=VEDA_LAYOUT_PERMUTED, q_layout=VEDA_LAYOUT_PERMUTED):
         import torch
         bf = torch.bfloat16
-        self._expect(q, (self.R, self.D), bf, "q")
+        self._expect_q(q, q_layout)
         self._expect(k, (self.R, self.D), bf, "k")
         self._expect(v_t, (self.T, self.D, 128), bf, "v_t")
         self._expect(row_ptr, (self.T + 1,), torch.int32, "row_ptr")
@@ -483,7 +500,7 @@ class Plan:
         if visited is not None:
             self._expect(visited, (1,), torch.int32, "blocks_visited")
         veda_block_sparse_attn_fwd(self.handle, q, k, v_t, row_ptr, col_idx, scale, o, o_layout, lse, visited,
-                                   stream)
+                                   stream, q_layout)
 
     def heat(self, q, k, lse, scale, heat, stream=None):
         import torch
@@ -493,9 +510,10 @@ class Plan:
         self._expect(heat, (self.info["total_pairs"],), torch.float32, "heat")
         veda_block_heat(self.handle, q, k, lse, scale, heat, stream)
 
-    def lse_heat(self, q, k, row_ptr, col_idx, scale, lse, heat, workspace, stream=None):
+    def lse_heat(self, q, k, row_ptr, col_idx, scale, lse, heat, workspace, stream=None,
+                 q_layout=VEDA_LAYOUT_PERMUTED):
         import torch
-        self._expect(q, (self.R, self.D), torch.bfloat16, "q")
+        self._expect_q(q, q_layout)
         self._expect(k, (self.R, self.D), torch.bfloat16, "k")
         self._expect(row_ptr, (self.T + 1,), torch.int32, "row_ptr")
         self._expect(col_idx, (self.info["nnz"],), torch.int32, "col_idx")
@@ -503,7 +521,7 @@ class Plan:
             self._expect(lse, (self.R,), torch.float32, "lse")
         self._expect(heat, (self.info["total_pairs"],), torch.float32, "heat")
         self._check_ws(workspace, "heat_workspace_bytes")
-        veda_dense_lse_heat(self.handle, q, k, row_ptr, col_idx, scale, lse, heat, workspace, stream)
+        veda_dense_lse_heat(self.handle, q, k, row_ptr, col_idx, scale, lse, heat, workspace, stream, q_layout)
 
     def transpose(self, row_ptr, col_idx, col_ptr, row_idx, workspace, stream=None):
         import torch

@@ -643,9 +643,11 @@ veda_status veda_permute_qkv(const veda_plan* p, const void* q, const void* k, c
                              void* k_perm, void* v_t, void* workspace, size_t workspace_bytes, void* stream) {
   veda_status st = check_plan_ready(p);
   if (st) return st;
-  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(q_perm, "q_perm")) ||
-      (st = check_ptr(k_perm, "k_perm")))
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(k_perm, "k_perm")))
     return st;
+  if (q_perm && (st = check_ptr(q_perm, "q_perm"))) return st;
+  if (!q_perm && !workspace)
+    return fail(VEDA_ERR_INVALID_ARG, "q_perm may be NULL only with a workspace (Q pooled, not written)");
   if ((v == nullptr) != (v_t == nullptr)) return fail(VEDA_ERR_INVALID_ARG, "v and v_t must both be given or both NULL");
   if (v && ((st = check_ptr(v, "v")) || (st = check_ptr(v_t, "v_t")))) return st;
   const int nt = v ? 3 : 2;   // without V: Q and K only
@@ -653,7 +655,7 @@ veda_status veda_permute_qkv(const veda_plan* p, const void* q, const void* k, c
   void* outs[3] = {q_perm, k_perm, v_t};
   for (int a = 0; a < nt; ++a)
     for (int b = 0; b < nt; ++b)
-      if (ins[a] == outs[b]) return fail(VEDA_ERR_INVALID_ARG, "an input aliases an output");
+      if (outs[b] && ins[a] == outs[b]) return fail(VEDA_ERR_INVALID_ARG, "an input aliases an output");
   if (workspace) {
     if ((st = check_ptr(workspace, "workspace"))) return st;
     if ((int64_t)workspace_bytes < p->info.score_workspace_bytes)
@@ -689,7 +691,8 @@ veda_status veda_select_blocks(const veda_plan* p, const float* scores, int32_t*
   return launched(launch_select(p->dev, scores, row_ptr, col_idx, dense_mask, (hipStream_t)stream), "select");
 }
 
-veda_status veda_block_sparse_attn_fwd(const veda_plan* p, const void* q, const void* k, const void* v_t,
+veda_status veda_block_sparse_attn_fwd(const veda_plan* p, const void* q, int32_t q_layout, const void* k,
+                                       const void* v_t,
                                        const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
                                        void* o, int32_t o_layout, float* lse, uint32_t* blocks_visited,
                                        void* stream) {
@@ -707,9 +710,12 @@ veda_status veda_block_sparse_attn_fwd(const veda_plan* p, const void* q, const 
     return fail(VEDA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if (o_layout != VEDA_LAYOUT_PERMUTED && o_layout != VEDA_LAYOUT_NATURAL)
     return fail(VEDA_ERR_INVALID_ARG, "unknown o_layout %d", o_layout);
+  if (q_layout != VEDA_LAYOUT_PERMUTED && q_layout != VEDA_LAYOUT_NATURAL)
+    return fail(VEDA_ERR_INVALID_ARG, "unknown q_layout %d", q_layout);
   if (o && (o == q || o == k || o == v_t)) return fail(VEDA_ERR_INVALID_ARG, "o aliases an input");
-  return launched(launch_attn_fwd(p->dev, q, k, v_t, row_ptr, col_idx, softmax_scale, o,
-                                  o_layout == VEDA_LAYOUT_NATURAL, lse, blocks_visited, (hipStream_t)stream),
+  return launched(launch_attn_fwd(p->dev, q, q_layout == VEDA_LAYOUT_NATURAL, k, v_t, row_ptr, col_idx,
+                                  softmax_scale, o, o_layout == VEDA_LAYOUT_NATURAL, lse, blocks_visited,
+                                  (hipStream_t)stream),
                   "block-sparse attention");
 }
 
@@ -727,9 +733,9 @@ veda_status veda_block_heat(const veda_plan* p, const void* q, const void* k, co
   return launched(launch_heat(p->dev, q, k, lse, softmax_scale, heat, (hipStream_t)stream), "block heat");
 }
 
-veda_status veda_dense_lse_heat(const veda_plan* p, const void* q, const void* k, const int32_t* row_ptr,
-                                const int32_t* col_idx, float softmax_scale, float* lse, float* heat,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+veda_status veda_dense_lse_heat(const veda_plan* p, const void* q, int32_t q_layout, const void* k,
+                                const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale, float* lse,
+                                float* heat, void* workspace, size_t workspace_bytes, void* stream) {
   veda_status st = check_plan_ready(p);
   if (st) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(row_ptr, "row_ptr")) ||
@@ -744,11 +750,13 @@ veda_status veda_dense_lse_heat(const veda_plan* p, const void* q, const void* k
     return fail(VEDA_ERR_INVALID_ARG, "lse, heat and workspace must be distinct from each other and the inputs");
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
     return fail(VEDA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (q_layout != VEDA_LAYOUT_PERMUTED && q_layout != VEDA_LAYOUT_NATURAL)
+    return fail(VEDA_ERR_INVALID_ARG, "unknown q_layout %d", q_layout);
   if ((int64_t)workspace_bytes < p->info.heat_workspace_bytes)
     return fail(VEDA_ERR_WORKSPACE, "workspace of %zu bytes, %lld needed", workspace_bytes,
                 (long long)p->info.heat_workspace_bytes);
-  return launched(launch_lse_heat(p->dev, q, k, row_ptr, col_idx, softmax_scale, lse, static_cast<float*>(workspace),
-                                  heat, (hipStream_t)stream),
+  return launched(launch_lse_heat(p->dev, q, q_layout == VEDA_LAYOUT_NATURAL, k, row_ptr, col_idx, softmax_scale, lse,
+                                  static_cast<float*>(workspace), heat, (hipStream_t)stream),
                   "dense LSE and heat");
 }
 

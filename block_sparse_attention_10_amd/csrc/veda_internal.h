@@ -83,10 +83,10 @@ hipError_t launch_score_pooled(const DevPlan& p, const float* wq, const float* w
                                void* ws, hipStream_t s);
 hipError_t launch_select(const DevPlan& p, const float* scores, int32_t* row_ptr,
                          int32_t* col_idx, uint8_t* dense_mask, hipStream_t s);
-hipError_t launch_attn_fwd(const DevPlan& p, const void* q, const void* k, const void* vt,
+hipError_t launch_attn_fwd(const DevPlan& p, const void* q, int q_natural, const void* k, const void* vt,
                            const int32_t* row_ptr, const int32_t* col_idx, float scale,
                            void* o, int o_natural, float* lse, uint32_t* visited, hipStream_t s);
-hipError_t launch_lse_heat(const DevPlan& p, const void* q, const void* k, const int32_t* row_ptr,
+hipError_t launch_lse_heat(const DevPlan& p, const void* q, int q_natural, const void* k, const int32_t* row_ptr,
                            const int32_t* col_idx, float scale, float* lse, float* bsum, float* heat,
                            hipStream_t s);
 hipError_t launch_heat(const DevPlan& p, const void* q, const void* k, const float* lse,

@@ -151,9 +151,11 @@ __global__ void __launch_bounds__(D * 2) permute_qkv_kernel(DevPlan p, const uin
     }
     return;
   }
-  uint16_t* dst = y == 0 ? qp : kp;
+  uint16_t* dst = y == 0 ? qp : kp;   // qp NULL: Q pooled only
+  if (dst) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) st16(dst + (t * kTile + 8 * sb + e) * D + 8 * cb, blk[e]);
+    for (int e = 0; e < 8; ++e) st16(dst + (t * kTile + 8 * sb + e) * D + 8 * cb, blk[e]);
+  }
   float* feat = y == 0 ? feat_q : feat_k;
   if (!feat) return;
   double sum[8];
@@ -1062,7 +1064,7 @@ __device__ __forceinline__ int half_pads(int nv, int hh) {
 // done with them (run_fast_pv and the block lambda below say when).  Two
 // workgroups share a CU (72 KB of LDS each).
 template <int D, bool PV, bool HB>
-__device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* __restrict__ q,
+__device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* __restrict__ q, int q_natural,
                                               const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
                                               const int32_t* __restrict__ row_ptr,
                                               const int32_t* __restrict__ col_idx, float scale_log2,
@@ -1102,11 +1104,22 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
   const bool qvalid = 32 * w + ln < sh.valid[i];
   if (threadIdx.x == 0) redo = 0;
 
-  // Q^T operand: query row 32w + ln, channels 16s + 8hl .. +7
+  // Q^T operand: query row 32w + ln, channels 16s + 8hl .. +7; from the
+  // permuted rows, or gathered from the natural [N, H, D] rows through the
+  // slot -> token table (a padding slot reads zeros, as its permuted row holds)
   bf16x8 qf[D / 16];
-  const uint16_t* qrow = q + (row0 + 32 * w + ln) * D + 8 * hl;
+  {
+    const uint16_t* qrow = q + (row0 + 32 * w + ln) * D + 8 * hl;
+    bool qzero = false;
+    if (q_natural) {
+      const int tok = sh.perm[(int64_t)kTile * i + 32 * w + ln];
+      qzero = tok < 0;
+      qrow = q + ((int64_t)(qzero ? 0 : tok) * p.num_heads + h) * D + 8 * hl;
+    }
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld16(qrow + 16 * s));
+    for (int s = 0; s < D / 16; ++s)
+      qf[s] = __builtin_bit_cast(bf16x8, qzero ? u32x4{0u, 0u, 0u, 0u} : ld16(qrow + 16 * s));
+  }
 
   f32x16 oacc[D / 32];
   float m_run, l_run;   // reference point (log2 units) and the lane's sum of p
@@ -1585,14 +1598,14 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
 
 template <int D, bool PV>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const uint16_t* __restrict__ q,
-                                                              const uint16_t* __restrict__ k,
+                                                              int q_natural, const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ vt,
                                                               const int32_t* __restrict__ row_ptr,
                                                               const int32_t* __restrict__ col_idx, float scale_log2,
                                                               uint16_t* __restrict__ o, int o_natural,
                                                               float* __restrict__ lse, uint32_t* __restrict__ visited) {
-  attn_fwd_body<D, PV, false>(p, q, k, vt, row_ptr, col_idx, scale_log2, o, o_natural, lse, visited, nullptr,
-                              nullptr);
+  attn_fwd_body<D, PV, false>(p, q, q_natural, k, vt, row_ptr, col_idx, scale_log2, o, o_natural, lse, visited,
+                              nullptr, nullptr);
 }
 
 // The dense LSE and the block heat in one pass over an all-blocks mask: the
@@ -1600,12 +1613,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
 // per query in bsum and reduces them into the heat at the end of each row.
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) lse_heat_kernel(DevPlan p, const uint16_t* __restrict__ q,
-                                                              const uint16_t* __restrict__ k,
+                                                              int q_natural, const uint16_t* __restrict__ k,
                                                               const int32_t* __restrict__ row_ptr,
                                                               const int32_t* __restrict__ col_idx, float scale_log2,
                                                               float* __restrict__ lse, float* __restrict__ bsum,
                                                               float* __restrict__ heat) {
-  attn_fwd_body<D, false, true>(p, q, k, k, row_ptr, col_idx, scale_log2, nullptr, 0, lse, nullptr, bsum, heat);
+  attn_fwd_body<D, false, true>(p, q, q_natural, k, k, row_ptr, col_idx, scale_log2, nullptr, 0, lse, nullptr, bsum,
+                                heat);
 }
 
 // ---------------------------------------------------------------------------
@@ -2625,7 +2639,8 @@ hipError_t launch_select(const DevPlan& p, const float* scores, int32_t* row_ptr
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd(const DevPlan& p, const void* q, const void* k, const void* vt, const int32_t* row_ptr,
+hipError_t launch_attn_fwd(const DevPlan& p, const void* q, int q_natural, const void* k, const void* vt,
+                           const int32_t* row_ptr,
                            const int32_t* col_idx, float scale, void* o, int o_natural, float* lse,
                            uint32_t* visited, hipStream_t s) {
   const float scale_log2 = scale * 1.4426950408889634f;
@@ -2637,33 +2652,33 @@ hipError_t launch_attn_fwd(const DevPlan& p, const void* q, const void* k, const
   // o == nullptr: only the LSE (no PV products, no V^T copies)
   if (p.head_dim == 128) {
     if (oo)
-      hipLaunchKernelGGL((attn_fwd_kernel<128, true>), grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
+      hipLaunchKernelGGL((attn_fwd_kernel<128, true>), grid, dim3(kThreads), 0, s, p, qq, q_natural, kk, vv, row_ptr, col_idx,
                          scale_log2, oo, o_natural, lse, visited);
     else
-      hipLaunchKernelGGL((attn_fwd_kernel<128, false>), grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
+      hipLaunchKernelGGL((attn_fwd_kernel<128, false>), grid, dim3(kThreads), 0, s, p, qq, q_natural, kk, vv, row_ptr, col_idx,
                          scale_log2, oo, o_natural, lse, visited);
   } else {
     if (oo)
-      hipLaunchKernelGGL((attn_fwd_kernel<64, true>), grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
+      hipLaunchKernelGGL((attn_fwd_kernel<64, true>), grid, dim3(kThreads), 0, s, p, qq, q_natural, kk, vv, row_ptr, col_idx,
                          scale_log2, oo, o_natural, lse, visited);
     else
-      hipLaunchKernelGGL((attn_fwd_kernel<64, false>), grid, dim3(kThreads), 0, s, p, qq, kk, vv, row_ptr, col_idx,
+      hipLaunchKernelGGL((attn_fwd_kernel<64, false>), grid, dim3(kThreads), 0, s, p, qq, q_natural, kk, vv, row_ptr, col_idx,
                          scale_log2, oo, o_natural, lse, visited);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_lse_heat(const DevPlan& p, const void* q, const void* k, const int32_t* row_ptr,
+hipError_t launch_lse_heat(const DevPlan& p, const void* q, int q_natural, const void* k, const int32_t* row_ptr,
                            const int32_t* col_idx, float scale, float* lse, float* bsum, float* heat, hipStream_t s) {
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid((unsigned)p.attn_grid);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   if (p.head_dim == 128)
-    hipLaunchKernelGGL(lse_heat_kernel<128>, grid, dim3(kThreads), 0, s, p, qq, kk, row_ptr, col_idx, scale_log2, lse,
+    hipLaunchKernelGGL(lse_heat_kernel<128>, grid, dim3(kThreads), 0, s, p, qq, q_natural, kk, row_ptr, col_idx, scale_log2, lse,
                        bsum, heat);
   else
-    hipLaunchKernelGGL(lse_heat_kernel<64>, grid, dim3(kThreads), 0, s, p, qq, kk, row_ptr, col_idx, scale_log2, lse,
+    hipLaunchKernelGGL(lse_heat_kernel<64>, grid, dim3(kThreads), 0, s, p, qq, q_natural, kk, row_ptr, col_idx, scale_log2, lse,
                        bsum, heat);
   return hipGetLastError();
 }

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define VEDA_ABI_VERSION 7
+#define VEDA_ABI_VERSION 8
 
 typedef int32_t veda_status;
 enum {
@@ -195,7 +195,10 @@ veda_status veda_permute_tiles(const veda_plan* plan, const void* src, void* dst
  * must hold score_workspace_bytes.  v and v_t may both be NULL: then only Q
  * and K are permuted (and pooled), e.g. so that V's permutation
  * (veda_permute_tiles, FORWARD_TRANSPOSED) can run on another stream while
- * the predictor scores; one NULL without the other is VEDA_ERR_INVALID_ARG. */
+ * the predictor scores; one NULL without the other is VEDA_ERR_INVALID_ARG.
+ * q_perm may be NULL when workspace is given: Q is then read and pooled but
+ * not written, for a layer whose attention reads Q in its natural layout
+ * (q_layout VEDA_LAYOUT_NATURAL below). */
 veda_status veda_permute_qkv(const veda_plan* plan, const void* q, const void* k, const void* v,
                              void* q_perm, void* k_perm, void* v_t, void* workspace,
                              size_t workspace_bytes, void* stream);
@@ -263,7 +266,12 @@ veda_status veda_select_blocks(const veda_plan* plan, const float* scores, int32
  *   O[r] = softmax_c(scale * q_r . k_c) v_c,  LSE[r] = log sum_c exp(scale q_r.k_c)
  * over the valid slots c of the listed key tiles (slots >= valid(j) are
  * masked: the only mask rule).  bf16 MFMA products, fp32 softmax.
- *   q, k:   device permuted bf16 [R, D]
+ *   q:      device bf16, q_layout VEDA_LAYOUT_PERMUTED: [R, D];
+ *           VEDA_LAYOUT_NATURAL: [N, H, D], each query tile's rows gathered
+ *           through the plan's slot -> token table when the tile is loaded
+ *           (padding slots read as zeros), so no permuted copy of Q is
+ *           needed; both layouts give bitwise the same O and LSE
+ *   k:      device permuted bf16 [R, D]
  *   v_t:    device tile-transposed bf16 [T, D, 128]
  * The padding slots of k (rows) and v_t (columns) must hold zeros, as
  * veda_permute_qkv and veda_permute_tiles write them: the kernel removes the
@@ -283,7 +291,7 @@ veda_status veda_select_blocks(const veda_plan* plan, const float* scores, int32
  *   blocks_visited: device uint32 counter the kernel adds the number of
  *           blocks it computed to (caller zeroes it), or NULL.
  * softmax_scale must be finite and > 0 (1/sqrt(D) for the usual scale). */
-veda_status veda_block_sparse_attn_fwd(const veda_plan* plan, const void* q, const void* k,
+veda_status veda_block_sparse_attn_fwd(const veda_plan* plan, const void* q, int32_t q_layout, const void* k,
                                        const void* v_t, const int32_t* row_ptr,
                                        const int32_t* col_idx, float softmax_scale, void* o,
                                        int32_t o_layout, float* lse, uint32_t* blocks_visited,
@@ -314,7 +322,9 @@ veda_status veda_block_heat(const veda_plan* plan, const void* q, const void* k,
  * the end of the row, so the key tiles are walked once instead of twice
  * (rows that need the exact fallback pass are walked again with the final
  * LSE).  The padding rows of k must hold zeros.
- *   q, k:      device permuted bf16 [R, D]
+ *   q:         device bf16 in q_layout, as for veda_block_sparse_attn_fwd
+ *              (VEDA_LAYOUT_PERMUTED [R, D] or VEDA_LAYOUT_NATURAL [N, H, D])
+ *   k:         device permuted bf16 [R, D]
  *   lse:       device fp32 [R] natural log, or NULL (not stored)
  *   heat:      device fp32 [sum_h n_h^2], layout of the scores; every pair
  *              is written
@@ -324,7 +334,7 @@ veda_status veda_block_heat(const veda_plan* plan, const void* q, const void* k,
  * Errors: VEDA_ERR_WORKSPACE if workspace_bytes is too small;
  * VEDA_ERR_INVALID_ARG if lse, heat and workspace are not three different
  * buffers or one of them is q or k. */
-veda_status veda_dense_lse_heat(const veda_plan* plan, const void* q, const void* k,
+veda_status veda_dense_lse_heat(const veda_plan* plan, const void* q, int32_t q_layout, const void* k,
                                 const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
                                 float* lse, float* heat, void* workspace, size_t workspace_bytes,
                                 void* stream);

@@ -649,6 +649,64 @@ def test_permute_qk_only_and_side_stream_v(idx):
     assert e.value.status == 1                   # VEDA_ERR_INVALID_ARG: v without v_t
 
 
+@pytest.mark.parametrize("which", ["small", "config3"])
+def test_natural_q_layout(which):
+    """Q in its natural [N, H, D] layout (q_layout NATURAL, gathered through
+    the slot -> token table) against the permuted copy: the attention's O and
+    LSE, and the dense LSE and heat, bitwise equal; veda_permute_qkv with
+    q_perm = NULL writes K, V^T and the pooled features of Q and K bitwise
+    as the full call does (ragged tiles, two tile shapes, D = 64 and 128,
+    packed segments, the 16:9 clip)."""
+    ws = small_workloads() if which == "small" else [wl.workload(3)]
+    for w in ws:
+        inp = wl.make_inputs(w, seed=w.index)
+        g = gp.gpu_path(w, inp)
+        plan, dev = g["plan"], "cuda"
+        q, k, v = inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev)
+        # the layer's permutation without the Q copy
+        got = [torch.full_like(g["k_perm"], -1), torch.full_like(g["v_t"], -1),
+               torch.full_like(plan.empty_workspace(), float("nan"))]
+        ref_ws = plan.empty_workspace()
+        plan.permute_qkv(q, k, v, plan.empty_perm(), plan.empty_perm(), plan.empty_vt(), ref_ws)
+        plan.permute_qkv(q, k, v, None, got[0], got[1], got[2])
+        torch.cuda.synchronize()
+        assert torch.equal(got[0].view(torch.int16), g["k_perm"].view(torch.int16)), w.name
+        assert torch.equal(got[1].view(torch.int16), g["v_t"].view(torch.int16)), w.name
+        rv, gv = plan.score_workspace_views(ref_ws), plan.score_workspace_views(got[2])
+        for key in ("feat_q", "feat_k"):
+            assert torch.equal(rv[key].view(torch.int32), gv[key].view(torch.int32)), (w.name, key)
+        # attention: permuted Q against natural Q, O in both layouts
+        for o_layout in (vb.VEDA_LAYOUT_NATURAL, vb.VEDA_LAYOUT_PERMUTED):
+            shape = (w.num_tokens, w.num_heads, w.head_dim) if o_layout == vb.VEDA_LAYOUT_NATURAL else (plan.R, w.head_dim)
+            outs = []
+            for q_in, q_layout in ((g["q_perm"], vb.VEDA_LAYOUT_PERMUTED), (q, vb.VEDA_LAYOUT_NATURAL)):
+                o = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+                lse = torch.full((plan.R,), float("nan"), dtype=torch.float32, device=dev)
+                plan.attention(q_in, g["k_perm"], g["v_t"], g["row_ptr"], g["col_idx"], w.softmax_scale, o, lse,
+                               o_layout=o_layout, q_layout=q_layout)
+                outs.append((o, lse))
+            torch.cuda.synchronize()
+            (o0, l0), (o1, l1) = outs
+            assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)), (w.name, o_layout)
+            assert torch.equal(l0.view(torch.int32), l1.view(torch.int32)), (w.name, o_layout)
+        # the dense LSE and heat
+        if which == "small":
+            gd = gp.gpu_path(w, inp, budget_mode=wl.ALL_BLOCKS, dense_mask=False)
+            pd = gd["plan"]
+            res = []
+            for q_in, q_layout in ((gd["q_perm"], vb.VEDA_LAYOUT_PERMUTED), (q, vb.VEDA_LAYOUT_NATURAL)):
+                lse = torch.full((pd.R,), float("nan"), dtype=torch.float32, device=dev)
+                heat = torch.full((pd.info["total_pairs"],), float("nan"), dtype=torch.float32, device=dev)
+                wsh = torch.full((pd.info["heat_workspace_bytes"] // 4,), float("nan"), dtype=torch.float32,
+                                 device=dev)
+                pd.lse_heat(q_in, gd["k_perm"], gd["row_ptr"], gd["col_idx"], w.softmax_scale, lse, heat, wsh,
+                            q_layout=q_layout)
+                res.append((lse, heat))
+            torch.cuda.synchronize()
+            assert torch.equal(res[0][0].view(torch.int32), res[1][0].view(torch.int32)), w.name
+            assert torch.equal(res[0][1].view(torch.int32), res[1][1].view(torch.int32)), w.name
+
+
 def test_all_mask_equals_dense_attention():
     """The ALL budget through the same kernels is dense attention (library fp64 SDPA)."""
     w = wl.Workload(95, "dense_small", (wl.Segment(wl.VIDEO3D, (4, 10, 12), 0),), 2, 128, ((2, 8, 8),) * 2,
@@ -771,12 +829,20 @@ def test_error_paths_on_device():
     buf = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
     # misaligned pointer -> INVALID_ARG before any launch
     assert lib.veda_permute_tiles(plan.handle, buf.data_ptr() + 2, buf.data_ptr() + 4096, 0, None) == 1
-    assert lib.veda_block_sparse_attn_fwd(plan.handle, buf.data_ptr(), buf.data_ptr(), buf.data_ptr(),
+    assert lib.veda_block_sparse_attn_fwd(plan.handle, buf.data_ptr(), 0, buf.data_ptr(), buf.data_ptr(),
                                           buf.data_ptr(), buf.data_ptr(), ctypes.c_float(float("nan")),
                                           buf.data_ptr(), 0, None, None, None) == 1
-    assert lib.veda_block_sparse_attn_fwd(plan.handle, buf.data_ptr(), buf.data_ptr(), buf.data_ptr(),
+    assert lib.veda_block_sparse_attn_fwd(plan.handle, buf.data_ptr(), 0, buf.data_ptr(), buf.data_ptr(),
                                           buf.data_ptr(), buf.data_ptr(), ctypes.c_float(0.125),
                                           buf.data_ptr() + 8192, 7, None, None, None) == 1
+    # unknown q_layout: INVALID_ARG before any launch
+    assert lib.veda_block_sparse_attn_fwd(plan.handle, buf.data_ptr(), 3, buf.data_ptr(), buf.data_ptr(),
+                                          buf.data_ptr(), buf.data_ptr(), ctypes.c_float(0.125),
+                                          buf.data_ptr() + 8192, 0, None, None, None) == 1
+    assert "q_layout" in vb.veda_last_error()
+    # q_perm NULL without the pooling workspace: INVALID_ARG
+    assert lib.veda_permute_qkv(plan.handle, buf.data_ptr(), buf.data_ptr() + 4096, None, None,
+                                buf.data_ptr() + 8192, None, None, 0, None) == 1
     assert lib.veda_score_tiles(plan.handle, buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(),
                                 buf.data_ptr(), buf.data_ptr(), 16, None) == 4
     # the two-launch reductions refuse a short workspace (WORKSPACE) on the host
