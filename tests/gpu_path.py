@@ -9,11 +9,15 @@ from block_sparse_attention_10_amd import binding as vb
 from oracle import veda_oracle as vo
 
 
-def gpu_path(w, inp, budget_mode=None, dense_mask=True, fused=True):
+def gpu_path(w, inp, budget_mode=None, dense_mask=True, fused=True, layer=False):
     """All calls of the hot path on cuda:0; returns a dict of device tensors.
 
     fused=True: veda_permute_qkv (permutes + pooling) -> veda_score_pooled ->
-    select -> attention writing O in natural order (the layout bench.py runs).
+    select -> attention writing O in natural order.
+    layer=True (with fused): the calls bench.py times: veda_permute_qkv
+    without the Q copy (Q pooled only) and the attention reading Q in its
+    natural layout; the permuted Q is then made by a separate
+    veda_permute_tiles call, for the checks only.
     fused=False: one veda_permute_tiles per tensor -> veda_score_tiles ->
     select -> attention into permuted rows -> veda_permute_tiles(INVERSE).
     """
@@ -25,7 +29,7 @@ def gpu_path(w, inp, budget_mode=None, dense_mask=True, fused=True):
     scores = torch.empty(plan.info["total_pairs"], dtype=torch.float32, device=dev)
     ws = plan.empty_workspace()
     if fused:
-        plan.permute_qkv(q, k, v, qp, kp, vt, ws)
+        plan.permute_qkv(q, k, v, None if layer else qp, kp, vt, ws)
         plan.score_pooled(wq, wk, scores, ws)
     else:
         plan.permute(q, qp, vb.VEDA_PERMUTE_FORWARD)
@@ -40,8 +44,13 @@ def gpu_path(w, inp, budget_mode=None, dense_mask=True, fused=True):
     visited = torch.zeros(1, dtype=torch.int32, device=dev)
     o_nat = torch.zeros((w.num_tokens, w.num_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
     if fused:
-        plan.attention(qp, kp, vt, row_ptr, col, w.softmax_scale, o_nat, lse, visited,
-                       o_layout=vb.VEDA_LAYOUT_NATURAL)
+        if layer:
+            plan.attention(q, kp, vt, row_ptr, col, w.softmax_scale, o_nat, lse, visited,
+                           o_layout=vb.VEDA_LAYOUT_NATURAL, q_layout=vb.VEDA_LAYOUT_NATURAL)
+            plan.permute(q, qp, vb.VEDA_PERMUTE_FORWARD)
+        else:
+            plan.attention(qp, kp, vt, row_ptr, col, w.softmax_scale, o_nat, lse, visited,
+                           o_layout=vb.VEDA_LAYOUT_NATURAL)
         o = None
     else:
         o = plan.empty_perm()

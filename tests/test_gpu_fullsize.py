@@ -13,6 +13,11 @@ on every query tile of two heads; the dense LSE and the block heat (the fused
 one-pass call and the heat from a given LSE) on every head against the
 oracle's dense LSE and heat; the whole path twice, bitwise equal.
 
+Both run the calls the benchmark times: the permutation writes K and V^T
+only (Q is pooled), and the attention and the dense LSE and heat read Q in
+its natural layout; the permuted Q checked here comes from a separate
+permutation call.
+
 The oracle runs per head in a pool of host worker processes (tests/oracle_pool).
 """
 
@@ -112,7 +117,7 @@ def _check_attention_heads(w, inp, g, plan, op, fronts, heads):
 
 
 def _check_repeat_bitwise(g, w, inp):
-    again = _host(gp.gpu_path(w, inp))
+    again = _host(gp.gpu_path(w, inp, layer=True))
     for key in ("q_perm", "k_perm", "v_t", "scores", "row_ptr", "col_idx", "dense_mask", "lse", "o_nat"):
         a, b = g[key], again[key]
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), key
@@ -121,8 +126,8 @@ def _check_repeat_bitwise(g, w, inp):
 def test_config4_long_clip_full():
     w = wl.workload(4)
     inp = wl.make_inputs(w)
-    print("config 4: GPU path", flush=True)
-    dev = gp.gpu_path(w, inp)
+    print("config 4: GPU path (the benchmark's layer calls)", flush=True)
+    dev = gp.gpu_path(w, inp, layer=True)
     plan = dev["plan"]
     g = _host(dev)
     del dev
@@ -142,8 +147,8 @@ def test_config4_long_clip_full():
 def test_config5_packed_full():
     w = wl.workload(5)
     inp = wl.make_inputs(w)
-    print("config 5: GPU path", flush=True)
-    dev = gp.gpu_path(w, inp)
+    print("config 5: GPU path (the benchmark's layer calls)", flush=True)
+    dev = gp.gpu_path(w, inp, layer=True)
     plan = dev["plan"]
     g = _host(dev)
     assert g["visited"] == plan.info["nnz"]
@@ -157,7 +162,9 @@ def test_config5_packed_full():
     lse1 = torch.full_like(d["lse"], float("nan"))
     heat1 = torch.full((dplan.info["total_pairs"],), float("nan"), dtype=torch.float32, device="cuda")
     ws = torch.empty(dplan.info["heat_workspace_bytes"] // 4, dtype=torch.float32, device="cuda")
-    dplan.lse_heat(d["q_perm"], d["k_perm"], d["row_ptr"], d["col_idx"], w.softmax_scale, lse1, heat1, ws)
+    # Q in its natural layout, as the benchmark's layer passes it
+    dplan.lse_heat(inp["q"].to("cuda"), d["k_perm"], d["row_ptr"], d["col_idx"], w.softmax_scale, lse1, heat1, ws,
+                   q_layout=vb.VEDA_LAYOUT_NATURAL)
     heat2 = torch.full_like(heat1, float("nan"))
     dplan.heat(d["q_perm"], d["k_perm"], d["lse"], w.softmax_scale, heat2)
     torch.cuda.synchronize()
