@@ -779,6 +779,10 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+// s_waitcnt immediate for vmcnt(n), n = 0 .. 63 (bits 3:0 and 15:14), with
+// lgkmcnt(0); expcnt not waited for.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
 template <int PENDING>
 __device__ __forceinline__ void dma_sync() {
   static_assert(PENDING >= 0 && PENDING < 16, "vmcnt field");
@@ -2251,62 +2255,115 @@ __device__ __forceinline__ void store_t_rows(uint16_t* __restrict__ out, int64_t
 // backward: dK, dV over the transposed lists
 // ---------------------------------------------------------------------------
 //
-// One workgroup of 8 waves per (head, key tile j), longest lists first.
-// Waves 0-3 are dV waves, waves 4-7 dK waves; wave w & 3 of either kind owns
-// keys 32(w & 3) .. +31, whose K (dV wave) or V (dK wave) rows it holds as B
-// operands.  For every query tile i that selected j, group g of 32 queries
-// at a time:
+// Two workgroups of 4 waves per (head, key tile j), one per 64-key half, so
+// that two of them share a CU and one computes while the other waits at its
+// barrier.  Waves 0-1 are dV waves, waves 2-3 dK waves; wave w & 1 of either
+// kind owns keys 64 half + 32(w & 1) .. +31, whose K (dV wave) or V (dK
+// wave) rows it holds as B operands.  The query tiles i that selected j
+// are walked as a stream of 32-query chunks c = 4 e + g (entry e of the
+// column, group g of tile i); for every chunk:
 //   dV wave:  S' = Q K_w^T, P' = exp2(S' c - lse2) (packed bf16, also handed
 //             to the dK wave of the same keys through LDS), dV_w^T += dO^T P'
-//   dK wave:  dP' = dO V_w^T, dS' = P' (dP' - Dsum), dK_w^T += Q^T dS'
+//   dK wave:  dP' = dO V_w^T, dS' = P' (dP' - Dsum), dK_w^T += Q^T dS', and
+//             dS' stored for the dQ pass
 // (A = Q and dO rows from LDS, read as rows or transposed; B = P' / dS'
 // straight from registers: with the pi row order a lane's eight values of a
-// 16-query step are eight consecutive queries).  Splitting the products over
-// two waves keeps every wave within 256 registers, so two waves share each
-// SIMD, and each does 16 MFMAs per group; a workgroup barrier per group
-// publishes P'.  Query tiles are double-buffered in LDS (two fixed buffer
-// sets, the loop unrolled by two), the next one copied asynchronously during
-// the current one's products.  Padding
-// keys' rows are written as zeros; padding queries have zero Q and dO rows
-// and contribute nothing.
+// 16-query step are eight consecutive queries); one workgroup barrier per
+// chunk publishes P'.  The chunks (Q and dO rows, 8 KB each at D = 128, and
+// their 32 (lse2, Dsum) pairs) go through a ring of 4 LDS slots, copied by
+// the dV waves only: at chunk c's barrier the copy of chunk c + 1 has landed
+// and chunk c + 3 is issued into the slot chunk c - 1 has left (every wave
+// is past it).  Workgroup b runs on XCD b mod 8; the two halves of a key
+// tile take slots 16k + x and 16k + 8 + x, so they run on one XCD one after
+// the other and share the column's query tiles in its L2.  Padding keys'
+// rows are written as zeros; padding queries have zero Q and dO rows and
+// contribute nothing.
+constexpr int kBwdHalfThreads = 256;   // dK/dV workgroups: 4 waves, 64 keys
+
 template <int D>
-__global__ void __launch_bounds__(kBwdThreads, 1) attn_bwd_dkdv_kernel(
+__global__ void __launch_bounds__(kBwdHalfThreads, 2) attn_bwd_dkdv_kernel(
     DevPlan p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ d_o, const float2* __restrict__ aux, const int32_t* __restrict__ col_ptr,
     const int32_t* __restrict__ row_idx, const int32_t* __restrict__ order, const int32_t* __restrict__ pos,
     float scale_log2, float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, u32x4* __restrict__ xds) {
-  constexpr int TS = kTile * D;   // bf16 elements of a row tile
-  // Q tile + its 128 (lse2, Dsum) pairs, and the dO tile, per buffer set
-  __shared__ __attribute__((aligned(16))) uint16_t q0[TS + 512];
-  __shared__ __attribute__((aligned(16))) uint16_t d0[TS];
-  __shared__ __attribute__((aligned(16))) uint16_t q1[TS + 512];
-  __shared__ __attribute__((aligned(16))) uint16_t d1[TS];
-  // P' of group g handed from the dV wave to the dK wave of the same keys:
-  // [group parity][key slice][16-query step][lane], packed bf16
-  __shared__ __attribute__((aligned(16))) u32x4 xp[2][4][2][64];
-  const int t = uni(order[blockIdx.x]);
+  constexpr int CS = 32 * D;                // bf16 elements of a 32-row chunk
+  constexpr int SLOT = 2 * CS + 128;        // Q chunk, dO chunk, 32 (lse2, Dsum) pairs
+  constexpr int AHEAD = 3;                  // chunks issued ahead of the one computing
+  constexpr int CH = D / 8;                 // 16-byte pieces of a row
+  constexpr int NIT = 32 * CH / 128;        // copy instructions per chunk, tensor and dV wave
+  constexpr int NCOPY = 2 * NIT;            // per chunk and dV wave (wave 0: one more, the pairs)
+  static_assert(NIT * 128 == 32 * CH, "a chunk is a whole number of copy instructions");
+  // four separate slot arrays: a read of one slot never waits for the copies
+  // still in flight into the others
+  __shared__ __attribute__((aligned(16))) uint16_t r0[SLOT], r1[SLOT], r2[SLOT], r3[SLOT];
+  // P' of chunk c handed from the dV wave to the dK wave of the same keys:
+  // [chunk parity][key slice][16-query step][lane], packed bf16
+  __shared__ __attribute__((aligned(16))) u32x4 xp[2][2][2][64];
+  const int64_t T = p.total_tiles;
+  const int bx = blockIdx.x, x8 = bx & 7, k2 = bx >> 3, half = k2 & 1;
+  const int64_t slot_idx = (int64_t)8 * (k2 >> 1) + x8;
+  if (slot_idx >= T) return;                // past the last key tile (uniform)
+  const int t = uni(order[slot_idx]);
   const int h = uni(p.row_head[t]);
   const DevShape& sh = p.shape[uni(p.head_shape[h])];
   const int nt = sh.num_tiles;
   const int j = t - uni(p.head_tile_off[h]);
   const int nvk = uni(sh.valid[j]);
   const int64_t hrow = uni64(p.head_row_off[h]);
-  const int wave = threadIdx.x >> 6, w = wave & 3, lane = lane_id(), ln = lane & 31, hl = lane >> 5;
-  const bool dk_wave = wave >= 4;
+  const int wave = uni(threadIdx.x >> 6), w = wave & 1, lane = lane_id(), ln = lane & 31, hl = lane >> 5;
+  const bool dk_wave = wave >= 2;
+  const int kslice = 2 * half + w;          // the wave's 32-key group inside the tile
   const float c = scale_log2;
-  const int64_t krow0 = hrow + (int64_t)kTile * j + 32 * w;
+  const int64_t krow0 = hrow + (int64_t)kTile * j + 32 * kslice;
   const int64_t tile_bytes = (int64_t)kTile * D * 2;
   const __amdgpu_buffer_rsrc_t rq = head_rsrc(q + hrow * D, nt * tile_bytes);
   const __amdgpu_buffer_rsrc_t rd = head_rsrc(d_o + hrow * D, nt * tile_bytes);
   const __amdgpu_buffer_rsrc_t rx = head_rsrc(aux + hrow, (int64_t)nt * kTile * 8);
-  const int loff = brow_lane_offset<D>(threadIdx.x);
-  // copies query tile i into one buffer set
-  auto copy = [&](uint16_t* qd, uint16_t* dd, int i) {
-    dma_row_tile<D>(qd, rq, i * (int)tile_bytes, loff, wave);
-    dma_row_tile<D>(dd, rd, i * (int)tile_bytes, loff, wave);
-    if (wave == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, qd + TS, 16, 16 * lane, i * kTile * 8, 0, 0);
-  };
   const int e0 = uni(col_ptr[t]), e1 = uni(col_ptr[t + 1]);
+  const int nchunk = 4 * (e1 - e0);
+  auto slot_of = [&](int cc) -> uint16_t* {
+    const int sl = cc & 3;
+    return sl < 2 ? (sl == 0 ? r0 : r1) : (sl == 2 ? r2 : r3);
+  };
+  // chunk cc into its ring slot (dV waves, 128 threads: instruction it moves
+  // LDS positions 128 it + tid of the chunk, whose source rows follow the
+  // row-tile layout)
+  auto copy = [&](int cc) {
+    const int i = min(max(uni(row_idx[e0 + (cc >> 2)]), 0), nt - 1);   // stay inside the head
+    const int g = cc & 3;
+    uint16_t* sl = slot_of(cc);
+    const int cb = (i * kTile + 32 * g) * D * 2;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int loff = brow_lane_offset<D>((int)threadIdx.x + 128 * it);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, sl + it * 8 * 128 + 512 * wave, 16, loff, cb, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, sl + CS + it * 8 * 128 + 512 * wave, 16, loff, cb, 0, 0);
+    }
+    if (wave == 0 && lane < 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, sl + 2 * CS, 16, 16 * lane, (i * kTile + 32 * g) * 8, 0, 0);
+  };
+  // The dV waves wait until a chunk's copy has landed, `younger` later
+  // chunks (0 .. AHEAD - 1) being allowed in flight (per dV wave NCOPY copy
+  // instructions a chunk, wave 0 one more for the pairs; the dV waves issue
+  // no other vector memory instruction), then every wave meets at the barrier.
+  auto chunk_sync = [&](int younger) {
+    asm volatile("" ::: "memory");
+    if (!dk_wave) {
+      if (wave == 0) {
+        if (younger >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (NCOPY + 1)));
+        else if (younger == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NCOPY + 1));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      } else {
+        if (younger >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NCOPY));
+        else if (younger == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NCOPY));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  static_assert(2 * (NCOPY + 1) < 64, "vmcnt counts fit the 6-bit field");
   auto run = [&](auto dkc) {
     constexpr bool DK = decltype(dkc)::value;
     bf16x8 bop[D / 16];   // K rows (dV wave) or V rows (dK wave) of the wave's 32 keys
@@ -2314,74 +2371,71 @@ __global__ void __launch_bounds__(kBwdThreads, 1) attn_bwd_dkdv_kernel(
     f32x16 acc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-    // the products of one query tile held in (qc, dc); xb: the block's dS
-    // in the workspace (nullptr: no CSR position, nothing stored)
-    auto tile = [&](const uint16_t* qc, const uint16_t* dc, u32x4* xb) {
-      const BwdOffsets<D> o = bwd_offsets_here<D>();
-      const float2* xc = reinterpret_cast<const float2*>(qc + TS);
+    // prologue: chunks 0 .. AHEAD-1 issued, chunk 0 waited for
+    if constexpr (!DK) {
+      for (int cc = 0; cc < min(nchunk, AHEAD); ++cc) copy(cc);
+    }
+    if (nchunk > 0) chunk_sync(min(nchunk, AHEAD) - 1);
+    u32x4* xb = nullptr;   // the current block's dS in the workspace (nullptr: not stored)
 #pragma unroll 1
-      for (int g = 0; g < 4; ++g) {
-        // register r holds query 32g + 16(r >> 3) + 8hl + (r & 7)
-        u32x4* slot = &xp[g & 1][w][0][lane];
-        bf16x8 pg[2];
-        if constexpr (!DK) {
-          const f32x16 sg = brows_group<D>(qc, o, bop, g);
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const float4* src = reinterpret_cast<const float4*>(&xc[32 * g + 16 * s2 + 8 * hl]);
-            u32x4 pk;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-              const float4 f = src[e2];   // (lse2, Dsum) of two consecutive queries
-              const int r0 = 8 * s2 + 2 * e2, r1 = r0 + 1;
-              pk[e2] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sg[r0], c, -f.x)),
-                                   __builtin_amdgcn_exp2f(fmaf(sg[r1], c, -f.z)));
-            }
-            slot[64 * s2] = pk;      // P' for the dK wave of the same keys
-            pg[s2] = __builtin_bit_cast(bf16x8, pk);
-          }
-          lds_sync();                // P'(g) published
-          tr_group<D>(dc, o, pg, g, acc);
-        } else {
-          const f32x16 dpg = brows_group<D>(dc, o, bop, g);
-          lds_sync();                // P'(g) published
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const float4* src = reinterpret_cast<const float4*>(&xc[32 * g + 16 * s2 + 8 * hl]);
-            const u32x4 pk = slot[64 * s2];
-            u32x4 dk4;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-              const float4 f = src[e2];
-              const int r0 = 8 * s2 + 2 * e2, r1 = r0 + 1;
-              const float p0 = __uint_as_float(pk[e2] << 16), p1 = __uint_as_float(pk[e2] & 0xffff0000u);
-              dk4[e2] = pack_bf16x2(p0 * (dpg[r0] - f.y), p1 * (dpg[r1] - f.w));
-            }
-            pg[s2] = __builtin_bit_cast(bf16x8, dk4);
-          }
-          if (xb) store_ds_block(reinterpret_cast<char*>(&xp[g & 1][w][0][0]), pg, xb + (g * 4 + w) * 128);
-          tr_group<D>(qc, o, pg, g, acc);
+    for (int cc = 0; cc < nchunk; ++cc) {
+      const int g = cc & 3;
+      if constexpr (DK) {
+        if (g == 0) {
+          const int pe = uni(pos[e0 + (cc >> 2)]);
+          xb = pe >= 0 ? xds + (int64_t)pe * (kBwdBlockBytes / 16) : nullptr;
         }
       }
-    };
-    // where block e's dS goes (only the dK waves store it)
-    auto xdst = [&](int e) -> u32x4* {
-      if constexpr (!DK) return nullptr;
-      const int pe = uni(pos[e]);
-      return pe >= 0 ? xds + (int64_t)pe * (kBwdBlockBytes / 16) : nullptr;
-    };
-    if (e0 < e1) copy(q0, d0, uni(row_idx[e0]));
-    dma_sync<0>();
-    for (int e = e0; e < e1; e += 2) {
-      if (e + 1 < e1) copy(q1, d1, uni(row_idx[e + 1]));
-      tile(q0, d0, xdst(e));
-      dma_sync<0>();                // tile e+1 has landed; every wave is done with set 0
-      if (e + 1 >= e1) break;
-      if (e + 2 < e1) copy(q0, d0, uni(row_idx[e + 2]));
-      tile(q1, d1, xdst(e + 1));
-      dma_sync<0>();
+      const uint16_t* qc = slot_of(cc);
+      const uint16_t* dc = qc + CS;
+      const float2* xc = reinterpret_cast<const float2*>(qc + 2 * CS);
+      const BwdOffsets<D> o = bwd_offsets_here<D>();
+      // register r holds query 16(r >> 3) + 8hl + (r & 7) of the chunk
+      u32x4* slot = &xp[cc & 1][w][0][lane];
+      bf16x8 pg[2];
+      if constexpr (!DK) {
+        const f32x16 sg = brows_group<D>(qc, o, bop, 0);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const float2* src = &xc[16 * s2 + 8 * hl];
+          u32x4 pk;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float4 f = __builtin_bit_cast(float4, ld16(src + 2 * e2));   // (lse2, Dsum) of two queries
+            const int r0i = 8 * s2 + 2 * e2, r1i = r0i + 1;
+            pk[e2] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sg[r0i], c, -f.x)),
+                                 __builtin_amdgcn_exp2f(fmaf(sg[r1i], c, -f.z)));
+          }
+          slot[64 * s2] = pk;      // P' for the dK wave of the same keys
+          pg[s2] = __builtin_bit_cast(bf16x8, pk);
+        }
+        // P'(cc) published and chunk cc+1 landed; chunks up to cc+AHEAD-1 were
+        // issued, so min(AHEAD-2, nchunk-2-cc) of them are younger than cc+1
+        chunk_sync(min(AHEAD - 2, nchunk - 2 - cc));
+        if (cc + AHEAD < nchunk) copy(cc + AHEAD);    // into the slot chunk cc-1 has left
+        tr_group<D>(dc, o, pg, 0, acc);
+      } else {
+        const f32x16 dpg = brows_group<D>(dc, o, bop, 0);
+        chunk_sync(0);   // the dK waves issue no copies: their count is not used
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const float2* src = &xc[16 * s2 + 8 * hl];
+          const u32x4 pk = slot[64 * s2];
+          u32x4 dk4;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float4 f = __builtin_bit_cast(float4, ld16(src + 2 * e2));
+            const int r0i = 8 * s2 + 2 * e2, r1i = r0i + 1;
+            const float p0 = __uint_as_float(pk[e2] << 16), p1 = __uint_as_float(pk[e2] & 0xffff0000u);
+            dk4[e2] = pack_bf16x2(p0 * (dpg[r0i] - f.y), p1 * (dpg[r1i] - f.w));
+          }
+          pg[s2] = __builtin_bit_cast(bf16x8, dk4);
+        }
+        if (xb) store_ds_block(reinterpret_cast<char*>(&xp[cc & 1][w][0][0]), pg, xb + (g * 4 + kslice) * 128);
+        tr_group<D>(qc, o, pg, 0, acc);
+      }
     }
-    const bool pad = 32 * w + ln >= nvk;
+    const bool pad = 32 * kslice + ln >= nvk;
     if constexpr (DK)
       store_t_rows<D>(dk, krow0, acc, scale, pad);
     else
@@ -2759,16 +2813,19 @@ hipError_t launch_attn_bwd(const DevPlan& p, const void* q, const void* k, const
   uint16_t* dvv = static_cast<uint16_t*>(dv);
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 gt((unsigned)T), gprep((unsigned)((R * (D / 8) + kThreads - 1) / kThreads));
+  const dim3 gkv((unsigned)(16 * ((T + 7) / 8)));   // two halves per key tile, slots as bwd_order_kernel deals them
   hipLaunchKernelGGL(bwd_order_kernel, dim3(1), dim3(1024), 0, s, col_ptr, T, order);
   hipLaunchKernelGGL(bwd_pos_kernel, gt, dim3(64), 0, s, p, row_ptr, col_idx, col_ptr, row_idx, pos);
   if (D == 128) {
     hipLaunchKernelGGL(bwd_prep_kernel<128>, gprep, dim3(kThreads), 0, s, R, oo, dd, lse, aux);
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, gt, dim3(kBwdThreads), 0, s, p, qq, kk, vv, dd, aux, col_ptr, row_idx,
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, gkv, dim3(kBwdHalfThreads), 0, s, p, qq, kk, vv, dd, aux, col_ptr,
+                       row_idx,
                        order, pos, scale_log2, scale, dkk, dvv, xds);
     hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, gt, dim3(kBwdThreads), 0, s, p, kk, xds, row_ptr, col_idx, scale, dqq);
   } else {
     hipLaunchKernelGGL(bwd_prep_kernel<64>, gprep, dim3(kThreads), 0, s, R, oo, dd, lse, aux);
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, gt, dim3(kBwdThreads), 0, s, p, qq, kk, vv, dd, aux, col_ptr, row_idx,
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, gkv, dim3(kBwdHalfThreads), 0, s, p, qq, kk, vv, dd, aux, col_ptr,
+                       row_idx,
                        order, pos, scale_log2, scale, dkk, dvv, xds);
     hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, gt, dim3(kBwdThreads), 0, s, p, kk, xds, row_ptr, col_idx, scale, dqq);
   }
