@@ -2087,7 +2087,7 @@ __device__ __forceinline__ int brow_off(int m, int c) {
 // workgroup instruction of 512 threads fills STEP = 512 / (D / 8) rows (32 or
 // 64); the swizzle and the pi order only use the low five bits of the row, so
 // every instruction of a thread uses one byte offset plus a uniform step.
-constexpr int kBwdThreads = 512;   // backward workgroups: 8 waves, 2 per SIMD
+constexpr int kBwdThreads = 512;   // dQ workgroups: 8 waves, 2 per SIMD
 
 template <int D>
 __device__ __forceinline__ int brow_lane_offset(int tid) {   // bytes
