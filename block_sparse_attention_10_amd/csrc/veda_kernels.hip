@@ -779,10 +779,6 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-// s_waitcnt immediate for vmcnt(n), n = 0 .. 63 (bits 3:0 and 15:14), with
-// lgkmcnt(0); expcnt not waited for.
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
-
 template <int PENDING>
 __device__ __forceinline__ void dma_sync() {
   static_assert(PENDING >= 0 && PENDING < 16, "vmcnt field");
@@ -2278,6 +2274,10 @@ __device__ __forceinline__ void store_t_rows(uint16_t* __restrict__ out, int64_t
 // the other and share the column's query tiles in its L2.  Padding keys'
 // rows are written as zeros; padding queries have zero Q and dO rows and
 // contribute nothing.
+// s_waitcnt immediate for vmcnt(n), n = 0 .. 63 (bits 3:0 and 15:14), with
+// lgkmcnt(0); expcnt not waited for.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
 constexpr int kBwdHalfThreads = 256;   // dK/dV workgroups: 4 waves, 64 keys
 
 template <int D>
