@@ -2377,6 +2377,7 @@ __global__ void __launch_bounds__(kBwdHalfThreads, 2) attn_bwd_dkdv_kernel(
     }
     if (nchunk > 0) chunk_sync(min(nchunk, AHEAD) - 1);
     u32x4* xb = nullptr;   // the current block's dS in the workspace (nullptr: not stored)
+    const BwdOffsets<D> o = bwd_offsets<D>(lane);   // the operand offsets, kept for the whole column
 #pragma unroll 1
     for (int cc = 0; cc < nchunk; ++cc) {
       const int g = cc & 3;
@@ -2389,7 +2390,6 @@ __global__ void __launch_bounds__(kBwdHalfThreads, 2) attn_bwd_dkdv_kernel(
       const uint16_t* qc = slot_of(cc);
       const uint16_t* dc = qc + CS;
       const float2* xc = reinterpret_cast<const float2*>(qc + 2 * CS);
-      const BwdOffsets<D> o = bwd_offsets_here<D>();
       // register r holds query 16(r >> 3) + 8hl + (r & 7) of the chunk
       u32x4* slot = &xp[cc & 1][w][0][lane];
       bf16x8 pg[2];
