@@ -2196,14 +2196,20 @@ __device__ __forceinline__ void tr_group(const uint16_t* __restrict__ tile, cons
 // takes it as its B operand (lane (ln, hl) of 16-key step s2: query ln, keys
 // 16 s2 + 8 hl .. +7; 1 KB per step).  The transpose goes through 2 KB of LDS
 // that only this wave touches meanwhile (`sb`): 32 rows of 32 queries, one
-// per key, then two transpose reads per step.
-__device__ __forceinline__ void store_ds_block(char* sb, const bf16x8 (&pg)[2], u32x4* __restrict__ dst) {
+// per key, then two transpose reads per step.  Two halves, so that the wave
+// can issue its products between writing the block into the slot
+// (stage_ds_block) and reading it back transposed for the global stores
+// (flush_ds_block).
+__device__ __forceinline__ void stage_ds_block(char* sb, const bf16x8 (&pg)[2]) {
   const int lane = lane_id(), ln = lane & 31, hl = lane >> 5;
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2)
     *reinterpret_cast<u32x4*>(sb + ln * 64 + 32 * s2 + 16 * hl) = __builtin_bit_cast(u32x4, pg[s2]);
   asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void flush_ds_block(const char* sb, u32x4* __restrict__ dst) {
+  const int lane = lane_id();
   // in each 16-lane group G, lane 4x + a names key 8(G >> 1) + 4r + x (+16 s2)
   // and queries 16(G & 1) + 4a .. +3
   const int G = lane >> 4, x = (lane >> 2) & 3, a = lane & 3;
@@ -2216,7 +2222,6 @@ __device__ __forceinline__ void store_ds_block(char* sb, const bf16x8 (&pg)[2], 
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), dst + 64 * s2 + lane);
   }
 }
-
 // The wave's B operand for 32 rows of a permuted tile: lane (ln, hl) holds
 // row r0 + ln, channels 16s + 8hl .. +7.
 template <int D>
@@ -2431,8 +2436,10 @@ __global__ void __launch_bounds__(kBwdHalfThreads, 2) attn_bwd_dkdv_kernel(
           }
           pg[s2] = __builtin_bit_cast(bf16x8, dk4);
         }
-        if (xb) store_ds_block(reinterpret_cast<char*>(&xp[cc & 1][w][0][0]), pg, xb + (g * 4 + kslice) * 128);
+        char* sb = reinterpret_cast<char*>(&xp[cc & 1][w][0][0]);
+        if (xb) stage_ds_block(sb, pg);
         tr_group<D>(qc, o, pg, 0, acc);
+        if (xb) flush_ds_block(sb, xb + (g * 4 + kslice) * 128);   // the transpose reads under the products
       }
     }
     const bool pad = 32 * kslice + ln >= nvk;
