@@ -41,6 +41,14 @@ def small_workloads():
                     wl.KEEP_RATIO, 1, 10),
         wl.Workload(94, "dense_only_audio", (wl.Segment(DN, (1, 1, 300), 0),), 1, 128, ((2, 8, 8),),
                     wl.KEEP_RATIO, 1, 10),
+        # degenerate budgets: only the diagonal (FIXED_K 0, two tile shapes); keep ratio 0 with a
+        # dense audio segment (video rows keep the diagonal and the audio tiles); keep ratio 1
+        wl.Workload(87, "diag_only_fixed_k0", (wl.Segment(V, (2, 16, 24), 0),), 2, 128, ((2, 8, 8), (1, 8, 16)),
+                    wl.FIXED_K, fixed_k=0),
+        wl.Workload(86, "keep_zero_with_audio", (wl.Segment(V, (2, 8, 24), 0), wl.Segment(DN, (1, 1, 150), 384)),
+                    2, 64, ((2, 8, 8),) * 2, wl.KEEP_RATIO, 0, 10),
+        wl.Workload(88, "keep_all_ratio", (wl.Segment(V, (2, 8, 24), 0), wl.Segment(DN, (1, 1, 150), 384)),
+                    2, 64, ((2, 8, 8),) * 2, wl.KEEP_RATIO, 1, 1),
     ]
 
 
@@ -94,11 +102,14 @@ def op_nnz(op, sel):
     return sum(len(r) for rows in sel for r in rows)
 
 
-@pytest.mark.parametrize("fused", [True, False], ids=["fused", "separate"])
+@pytest.mark.parametrize("mode", ["fused", "separate", "layer"])
 @pytest.mark.parametrize("w", small_workloads(), ids=lambda w: w.name)
-def test_small_workloads(w, fused):
+def test_small_workloads(w, mode):
+    """The whole path against the oracle: fused permutation and pooling,
+    separate calls, and the benchmark's layer calls (no permuted Q copy, the
+    attention reading Q in its natural layout)."""
     inp = wl.make_inputs(w, seed=w.index)
-    g = gp.gpu_path(w, inp, fused=fused)
+    g = gp.gpu_path(w, inp, fused=mode != "separate", layer=mode == "layer")
     op, qp, kp, sel = check_front(w, inp, g)
     check_attention(w, inp, g, op, qp, kp, sel)
 
