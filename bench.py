@@ -4,9 +4,10 @@ One step = one attention layer through the whole hot path on one batch of
 resident synthetic input: permute Q, K (rows) and V (tile-transposed) with the
 tile pooling fused in, project and score tile pairs, select blocks, and run
 block-sparse attention whose epilogue writes O back in natural token order
-(plus, for the packed workload, the dense LSE and the block heat in one pass
-over all blocks, the oracle mask selected on the heat and the attention mass
-of the predicted and the oracle mask).  Four seeded input
+(plus, for the packed workload, the dense LSE and the block heat over all
+blocks, by default in the same pass as the attention, the oracle mask
+selected on the heat and the attention mass of the predicted and the oracle
+mask).  Four seeded input
 sets rotate across steps, so each call sees a new block pattern.
 
 Prints one JSON line.  value = attention FLOP over computed blocks / layer
@@ -41,6 +42,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (known bytes) to scale HBM counters")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="rough budget of the oracle sample")
+    ap.add_argument("--separate-heat", action="store_true",
+                    help="packed workload: the attention and the dense LSE + heat as two calls instead of "
+                         "veda_attn_fwd_lse_heat")
     ap.add_argument("--q-copy", action="store_true",
                     help="write the permuted copy of Q in the layer and have the attention read it, instead of "
                          "gathering Q's rows from the natural layout in the attention kernel")
@@ -57,8 +61,11 @@ def parse():
 class Layer:
     """Device buffers and the calls of one attention layer."""
 
-    def __init__(self, w, inputs, vb, q_copy=False):
+    def __init__(self, w, inputs, vb, q_copy=False, separate_heat=False):
         self.w, self.vb = w, vb
+        # with the heat: the attention runs inside the dense LSE + heat pass
+        # (veda_attn_fwd_lse_heat) unless separate_heat
+        self.fused_heat = bool(w.with_heat) and not separate_heat
         # q_copy: the permutation also writes the permuted copy of Q and the
         # attention reads it; by default the attention gathers Q's rows from
         # the natural [N, H, D] layout and no copy of Q is written
@@ -109,21 +116,31 @@ class Layer:
             self.perm_events.append((g0, g1))
         p.score_pooled(x["w_q"], x["w_k"], self.scores, self.ws)
         p.select(self.scores, self.row_ptr, self.col)
+        q, ql = self.q_of(x)
+        if self.fused_heat:
+            d = self.dense
+            d.select(self.scores, self.d_row_ptr, self.d_col)
         if time_attn:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-        q, ql = self.q_of(x)
-        p.attention(q, self.kp, self.vt, self.row_ptr, self.col, w.softmax_scale, self.o_nat, self.lse,
-                    o_layout=vb.VEDA_LAYOUT_NATURAL, q_layout=ql)
+        if self.fused_heat:
+            # the attention of the predicted mask, the dense LSE and the block heat in one pass
+            p.attention_lse_heat(d, q, self.kp, self.vt, self.row_ptr, self.col, self.d_row_ptr, self.d_col,
+                                 w.softmax_scale, self.o_nat, self.lse, self.d_lse, self.heat, self.heat_ws,
+                                 o_layout=vb.VEDA_LAYOUT_NATURAL, q_layout=ql)
+        else:
+            p.attention(q, self.kp, self.vt, self.row_ptr, self.col, w.softmax_scale, self.o_nat, self.lse,
+                        o_layout=vb.VEDA_LAYOUT_NATURAL, q_layout=ql)
         if time_attn:
             e1.record()
             self.attn_events.append((e0, e1))
         if self.dense is not None:
             d = self.dense
-            d.select(self.scores, self.d_row_ptr, self.d_col)
-            # the dense LSE and the block heat in one pass over all blocks
-            d.lse_heat(q, self.kp, self.d_row_ptr, self.d_col, w.softmax_scale, self.d_lse, self.heat,
-                       self.heat_ws, q_layout=ql)
+            if not self.fused_heat:
+                d.select(self.scores, self.d_row_ptr, self.d_col)
+                # the dense LSE and the block heat in one pass over all blocks
+                d.lse_heat(q, self.kp, self.d_row_ptr, self.d_col, w.softmax_scale, self.d_lse, self.heat,
+                           self.heat_ws, q_layout=ql)
             p.select(self.heat, self.o_row_ptr, self.o_col)
             p.mask_mass(self.heat, self.row_ptr, self.col, self.m_pred)
             p.mask_mass(self.heat, self.o_row_ptr, self.o_col, self.m_orc)
@@ -246,10 +263,15 @@ def main():
     w = wl.workload(args.config)
     print("bench: generating inputs for %s" % w.describe(), file=sys.stderr, flush=True)
     inputs = [wl.make_inputs(w, seed=s) for s in wl.rotation_seeds(w)]
-    layer = Layer(w, inputs, vb, q_copy=args.q_copy)
+    layer = Layer(w, inputs, vb, q_copy=args.q_copy, separate_heat=args.separate_heat)
     p = layer.plan
     nnz = p.info["nnz"]
     flops_attn = 4.0 * 128 * 128 * w.head_dim * nnz
+    # the timed kernel's work: the attention, plus with the fused heat pass the
+    # dense QK^T products (2 * 128^2 * D per block of the all-blocks mask)
+    flops_kernel = flops_attn
+    if layer.fused_heat:
+        flops_kernel += 2.0 * 128 * 128 * w.head_dim * layer.dense.info["nnz"]
     print("bench: warmup %d, steps %d, nnz %d" % (args.warmup, args.steps, nnz), file=sys.stderr, flush=True)
     for s in range(args.warmup):
         layer.step(s)
@@ -276,13 +298,13 @@ def main():
     cold = attention_cold(layer, 5)
     perm = permute_rate(layer, w)
     gemm = gemm_reference()
-    attn_tflops = flops_attn / (attn_avg * 1e-3) / 1e12
+    attn_tflops = flops_kernel / (attn_avg * 1e-3) / 1e12
     value = flops_attn / (ms_step * 1e-3) / 1e12
     traffic = None
     try:
         with open(args.traffic_json) as f:
             tj = json.load(f)
-        key = "attn_fwd_config%d" % args.config
+        key = ("attn_lse_heat_config%d" if layer.fused_heat else "attn_fwd_config%d") % args.config
         if key in tj and tj[key].get("kernel_source_sha") == _kernel_sha():
             traffic = tj[key]["bytes_per_launch"]
     except (OSError, ValueError):
@@ -294,13 +316,15 @@ def main():
         "config": {"workload": "config %d %s" % (args.config, w.describe()), "tokens": w.num_tokens,
                    "heads": w.num_heads, "head_dim": w.head_dim, "nnz_blocks": nnz,
                    "block_density": round(nnz / p.info["total_pairs"], 4), "parallelism": "single GPU"},
+        "attn_kernel": ("attn_lse_heat_kernel (the attention inside the dense LSE + heat pass; its work counts "
+                        "the dense QK^T products too)" if layer.fused_heat else "attn_fwd_kernel"),
         "attn_kernel_ms": round(attn_avg, 4), "attn_kernel_tflops": round(attn_tflops, 2),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "attn_kernel_calls": {"n": len(attn_ms), "median_ms": round(float(np.median(attn_ms)), 4),
                               "min_ms": round(float(np.min(attn_ms)), 4),
                               "p90_ms": round(float(np.percentile(attn_ms, 90)), 4)},
-        "attn_valid_only_tflops": round(valid_flops / (attn_avg * 1e-3) / 1e12, 2),
+        "attn_valid_only_tflops": None if layer.fused_heat else round(valid_flops / (attn_avg * 1e-3) / 1e12, 2),
         "attn_cold_cache": cold,
         "permute_qkv": perm,
         "q_operand": "permuted copy written by the permutation" if args.q_copy else
@@ -413,7 +437,10 @@ def attention_cold(layer, n):
         torch.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
     del scrub
-    return {"n": n, "mean_ms": round(float(np.mean(ms)), 4), "note": "after a 1 GiB device write per call"}
+    note = "after a 1 GiB device write per call"
+    if layer.fused_heat:
+        note += "; the separate attention call (veda_block_sparse_attn_fwd), not the fused heat pass"
+    return {"n": n, "mean_ms": round(float(np.mean(ms)), 4), "note": note}
 
 
 def time_backward(layer, w, steps):

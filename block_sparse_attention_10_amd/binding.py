@@ -92,6 +92,8 @@ _SIGS = {
     "veda_block_sparse_attn_fwd": (_I32, [_P, _P, _I32, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _P, _P, _P]),
     "veda_block_heat": (_I32, [_P, _P, _P, _P, ctypes.c_float, _P, _P]),
     "veda_dense_lse_heat": (_I32, [_P, _P, _I32, _P, _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
+    "veda_attn_fwd_lse_heat": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _P, _P,
+                                      _P, _P, ctypes.c_size_t, _P]),
     "veda_mask_mass": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "veda_output_error": (_I32, [_P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "veda_mask_transpose": (_I32, [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -101,7 +103,7 @@ _SIGS = {
     "veda_score_tiles_noalloc": (_I32, [_P, _P, _P, _P, _P, _P, _P]),
 }
 EXPORTED = tuple(_SIGS)
-ABI_VERSION = 8   # the signatures above; a library built from other sources is refused
+ABI_VERSION = 9   # the signatures above; a library built from other sources is refused
 
 _lib = None
 
@@ -284,6 +286,15 @@ def veda_dense_lse_heat(plan: int, q, k, row_ptr, col_idx, softmax_scale: float,
     _check(lib().veda_dense_lse_heat(plan, _ptr(q), int(q_layout), _ptr(k), _ptr(row_ptr), _ptr(col_idx),
                                      float(softmax_scale), _ptr(lse), _ptr(heat), _ptr(workspace),
                                      _nbytes(workspace), _stream(stream)))
+
+
+def veda_attn_fwd_lse_heat(plan: int, dense_plan: int, q, k, v_t, row_ptr, col_idx, dense_row_ptr, dense_col_idx,
+                           softmax_scale: float, o, lse, dense_lse, heat, workspace, stream=None,
+                           o_layout: int = VEDA_LAYOUT_PERMUTED, q_layout: int = VEDA_LAYOUT_PERMUTED) -> None:
+    _check(lib().veda_attn_fwd_lse_heat(plan, dense_plan, _ptr(q), int(q_layout), _ptr(k), _ptr(v_t), _ptr(row_ptr),
+                                        _ptr(col_idx), _ptr(dense_row_ptr), _ptr(dense_col_idx),
+                                        float(softmax_scale), _ptr(o), int(o_layout), _ptr(lse), _ptr(dense_lse),
+                                        _ptr(heat), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def veda_mask_mass(plan: int, heat, row_ptr, col_idx, mass, workspace, stream=None) -> None:
@@ -522,6 +533,32 @@ class Plan:
         self._expect(heat, (self.info["total_pairs"],), torch.float32, "heat")
         self._check_ws(workspace, "heat_workspace_bytes")
         veda_dense_lse_heat(self.handle, q, k, row_ptr, col_idx, scale, lse, heat, workspace, stream, q_layout)
+
+    def attention_lse_heat(self, dense, q, k, v_t, row_ptr, col_idx, dense_row_ptr, dense_col_idx, scale, o, lse,
+                           dense_lse, heat, workspace, stream=None, o_layout=VEDA_LAYOUT_PERMUTED,
+                           q_layout=VEDA_LAYOUT_PERMUTED):
+        """attention() over this plan's selected CSR and dense.lse_heat() over
+        the dense plan's all-blocks CSR, in one pass (veda_attn_fwd_lse_heat)."""
+        import torch
+        bf = torch.bfloat16
+        self._expect_q(q, q_layout)
+        self._expect(k, (self.R, self.D), bf, "k")
+        self._expect(v_t, (self.T, self.D, 128), bf, "v_t")
+        self._expect(row_ptr, (self.T + 1,), torch.int32, "row_ptr")
+        self._expect(col_idx, (self.info["nnz"],), torch.int32, "col_idx")
+        self._expect(dense_row_ptr, (dense.T + 1,), torch.int32, "dense_row_ptr")
+        self._expect(dense_col_idx, (dense.info["nnz"],), torch.int32, "dense_col_idx")
+        if o_layout == VEDA_LAYOUT_NATURAL:
+            self._expect(o, (self.N, self.H, self.D), bf, "o")
+        else:
+            self._expect(o, (self.R, self.D), bf, "o")
+        for name, x in (("lse", lse), ("dense_lse", dense_lse)):
+            if x is not None:
+                self._expect(x, (self.R,), torch.float32, name)
+        self._expect(heat, (self.info["total_pairs"],), torch.float32, "heat")
+        dense._check_ws(workspace, "heat_workspace_bytes")
+        veda_attn_fwd_lse_heat(self.handle, dense.handle, q, k, v_t, row_ptr, col_idx, dense_row_ptr, dense_col_idx,
+                               scale, o, lse, dense_lse, heat, workspace, stream, o_layout, q_layout)
 
     def transpose(self, row_ptr, col_idx, col_ptr, row_idx, workspace, stream=None):
         import torch

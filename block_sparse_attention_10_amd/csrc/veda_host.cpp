@@ -502,7 +502,7 @@ veda_status veda_plan_create(const veda_plan_desc* d, veda_plan** out) {
   in.score_workspace_bytes = score_workspace_bytes(tiles, d->head_dim);
   in.transpose_workspace_bytes = transpose_workspace_bytes(in.total_pairs, in.total_tiles);
   in.bwd_workspace_bytes = bwd_workspace_bytes(in.total_rows, in.total_tiles, in.nnz);
-  in.heat_workspace_bytes = heat_workspace_bytes(in.nnz);
+  in.heat_workspace_bytes = heat_workspace_bytes(in.nnz, in.total_tiles, in.total_rows);
   in.reduce_workspace_bytes = reduce_workspace_bytes(H, maxtiles);
   build_attn_order(*p);
   build_staging(*p);
@@ -758,6 +758,94 @@ veda_status veda_dense_lse_heat(const veda_plan* p, const void* q, int32_t q_lay
   return launched(launch_lse_heat(p->dev, q, q_layout == VEDA_LAYOUT_NATURAL, k, row_ptr, col_idx, softmax_scale, lse,
                                   static_cast<float*>(workspace), heat, (hipStream_t)stream),
                   "dense LSE and heat");
+}
+
+namespace {
+// Two plans tile the same sequence the same way: same segments, heads, head
+// dimension and per-head tile shape (the tiling is a function of these).
+bool same_geometry(const veda_plan* a, const veda_plan* b) {
+  if (a->info.num_heads != b->info.num_heads || a->info.head_dim != b->info.head_dim ||
+      a->info.num_tokens != b->info.num_tokens || a->segs.size() != b->segs.size())
+    return false;
+  for (size_t i = 0; i < a->segs.size(); ++i) {
+    const veda_segment &x = a->segs[i], &y = b->segs[i];
+    if (x.kind != y.kind || x.t != y.t || x.h != y.h || x.w != y.w || x.token_offset != y.token_offset) return false;
+  }
+  for (int32_t h = 0; h < a->info.num_heads; ++h) {
+    const HostShape &x = a->shapes[a->head_shape[h]], &y = b->shapes[b->head_shape[h]];
+    if (x.a != y.a || x.b != y.b || x.c != y.c) return false;
+  }
+  return true;
+}
+}  // namespace
+
+veda_status veda_attn_fwd_lse_heat(const veda_plan* plan, const veda_plan* dense_plan, const void* q,
+                                   int32_t q_layout, const void* k, const void* v_t, const int32_t* row_ptr,
+                                   const int32_t* col_idx, const int32_t* dense_row_ptr,
+                                   const int32_t* dense_col_idx, float softmax_scale, void* o, int32_t o_layout,
+                                   float* lse, float* dense_lse, float* heat, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  veda_status st = check_plan_ready(plan);
+  if (st) return st;
+  if ((st = check_plan_ready(dense_plan))) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v_t, "v_t")) ||
+      (st = check_ptr(row_ptr, "row_ptr")) || (st = check_ptr(col_idx, "col_idx")) ||
+      (st = check_ptr(dense_row_ptr, "dense_row_ptr")) || (st = check_ptr(dense_col_idx, "dense_col_idx")) ||
+      (st = check_ptr(o, "o")) || (st = check_ptr(heat, "heat")) || (st = check_ptr(workspace, "workspace")))
+    return st;
+  if (lse && (st = check_ptr(lse, "lse"))) return st;
+  if (dense_lse && (st = check_ptr(dense_lse, "dense_lse"))) return st;
+  if (dense_plan->budget_mode != VEDA_BUDGET_ALL)
+    return fail(VEDA_ERR_UNSUPPORTED, "dense_plan must have budget mode ALL");
+  if (!same_geometry(plan, dense_plan))
+    return fail(VEDA_ERR_SHAPE, "plan and dense_plan do not tile the same sequence the same way");
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return fail(VEDA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (o_layout != VEDA_LAYOUT_PERMUTED && o_layout != VEDA_LAYOUT_NATURAL)
+    return fail(VEDA_ERR_INVALID_ARG, "unknown o_layout %d", o_layout);
+  if (q_layout != VEDA_LAYOUT_PERMUTED && q_layout != VEDA_LAYOUT_NATURAL)
+    return fail(VEDA_ERR_INVALID_ARG, "unknown q_layout %d", q_layout);
+  const void* outs[5] = {o, heat, workspace, lse, dense_lse};
+  const void* ins[3] = {q, k, v_t};
+  for (int i = 0; i < 5; ++i) {
+    if (!outs[i]) continue;
+    for (int j = 0; j < 3; ++j)
+      if (outs[i] == ins[j]) return fail(VEDA_ERR_INVALID_ARG, "an output aliases an input");
+    for (int j = i + 1; j < 5; ++j)
+      if (outs[i] == outs[j]) return fail(VEDA_ERR_INVALID_ARG, "o, heat, workspace, lse and dense_lse must be distinct");
+  }
+  if ((int64_t)workspace_bytes < dense_plan->info.heat_workspace_bytes)
+    return fail(VEDA_ERR_WORKSPACE, "workspace of %zu bytes, %lld needed", workspace_bytes,
+                (long long)dense_plan->info.heat_workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 15) return fail(VEDA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  const int64_t sel_nnz = plan->info.nnz, dense_nnz = dense_plan->info.nnz;
+  if (sel_nnz > dense_nnz)
+    return fail(VEDA_ERR_SHAPE, "plan keeps %lld blocks, more than the dense plan's %lld", (long long)sel_nnz,
+                (long long)dense_nnz);
+  // layout: shares of the selected blocks | block sums of the rest | rest
+  // columns | per-tile flags | the selected rows' LSE (if lse is NULL)
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  SplitWorkspace ws{};
+  ws.rest_nnz = dense_nnz - sel_nnz;
+  int64_t off = 0;
+  ws.mass = reinterpret_cast<float*>(base + off);
+  off += align256(sel_nnz * 128 * 4);
+  ws.rest_bsum = reinterpret_cast<float*>(base + off);
+  off += align256(ws.rest_nnz * 128 * 4);
+  ws.rest_col = reinterpret_cast<int32_t*>(base + off);
+  off += align256(dense_nnz * 4);
+  ws.cflag = reinterpret_cast<int32_t*>(base + off);
+  off += align256(dense_plan->info.total_tiles * 4);
+  float* lse_sel = lse ? lse : reinterpret_cast<float*>(base + off);
+  off += align256(dense_plan->info.total_rows * 4);
+  if (off > dense_plan->info.heat_workspace_bytes)
+    return fail(VEDA_ERR_WORKSPACE, "internal: workspace layout of %lld bytes exceeds %lld", (long long)off,
+                (long long)dense_plan->info.heat_workspace_bytes);
+  return launched(launch_attn_lse_heat(plan->dev, dense_plan->dev, q, q_layout == VEDA_LAYOUT_NATURAL, k, v_t,
+                                       row_ptr, col_idx, dense_row_ptr, dense_col_idx, softmax_scale, o,
+                                       o_layout == VEDA_LAYOUT_NATURAL, lse_sel, dense_lse, heat, ws,
+                                       (hipStream_t)stream),
+                  "attention with the dense LSE and heat");
 }
 
 namespace {

@@ -31,7 +31,13 @@ inline int64_t bwd_workspace_bytes(int64_t total_rows, int64_t total_tiles, int6
   return align256(total_rows * 8) + align256(total_tiles * 4) + align256(nnz * 4) + nnz * kBwdBlockBytes;
 }
 // One fp32 per (block, query slot): each block's sum of p per query.
-inline int64_t heat_workspace_bytes(int64_t nnz) { return align256(nnz * 128 * 4); }
+// veda_dense_lse_heat: nnz x 128 block sums.  veda_attn_fwd_lse_heat (with
+// this plan as the dense plan): the same floats split between the selected
+// and the rest blocks (one more alignment gap), the rest's columns, one flag
+// per tile and an LSE of the selected rows when the caller passes none.
+inline int64_t heat_workspace_bytes(int64_t nnz, int64_t tiles, int64_t rows) {
+  return align256(nnz * 128 * 4) + 256 + align256(nnz * 4) + align256(tiles * 4) + align256(rows * 4);
+}
 // Per-head partial sums of the two-launch reductions (mask mass: one per 16
 // rows; output error: 32 token chunks), two fp64 each.
 inline int mass_chunks(int32_t max_tiles) { return (max_tiles + 15) / 16; }
@@ -89,6 +95,21 @@ hipError_t launch_attn_fwd(const DevPlan& p, const void* q, int q_natural, const
 hipError_t launch_lse_heat(const DevPlan& p, const void* q, int q_natural, const void* k, const int32_t* row_ptr,
                            const int32_t* col_idx, float scale, float* lse, float* bsum, float* heat,
                            hipStream_t s);
+// veda_attn_fwd_lse_heat's scratch: the selected blocks' shares (mass,
+// sel nnz x 128 floats), the rest's block sums (rest_nnz x 128 floats), the
+// rest CSR's columns and the per-tile mismatch flags
+struct SplitWorkspace {
+  float* mass;
+  float* rest_bsum;
+  int32_t* rest_col;
+  int32_t* cflag;
+  int64_t rest_nnz;
+};
+hipError_t launch_attn_lse_heat(const DevPlan& sel, const DevPlan& dense, const void* q, int q_natural,
+                                const void* k, const void* vt, const int32_t* row_ptr, const int32_t* col_idx,
+                                const int32_t* dense_row_ptr, const int32_t* dense_col_idx, float scale, void* o,
+                                int o_natural, float* lse_sel, float* dense_lse, float* heat,
+                                const SplitWorkspace& ws, hipStream_t s);
 hipError_t launch_heat(const DevPlan& p, const void* q, const void* k, const float* lse,
                        float scale, float* heat, hipStream_t s);
 hipError_t launch_mask_mass(const DevPlan& p, int32_t max_tiles, const float* heat, const int32_t* row_ptr,

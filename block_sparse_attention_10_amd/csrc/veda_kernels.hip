@@ -1063,15 +1063,36 @@ __device__ __forceinline__ int half_pads(int nv, int hh) {
 // (four LDS arrays) that are refilled separately as soon as every wave is
 // done with them (run_fast_pv and the block lambda below say when).  Two
 // workgroups share a CU (72 KB of LDS each).
-template <int D, bool PV, bool HB>
+//
+// The attention and the dense heat of one layer split the dense row of a
+// query tile in two (veda_attn_fwd_lse_heat): its selected blocks and the
+// rest.
+//  PV and HB (attn_mass_kernel): the attention over the selected row that
+//    also keeps, per selected block and query, the block's share of the
+//    query's attention probability (bsum, normalised at the end of the row).
+//  HB and REST (rest_heat_kernel): the LSE-only pass over the rest of the
+//    dense row (the complement list); at the end of the row it joins its sum
+//    with the selected row's LSE into the dense LSE and writes the heat of
+//    every block of the dense row, the selected ones from their shares.
+// So no block's QK^T product is computed twice.
+struct HeatSplit {
+  const int32_t* srow;    // the selected CSR (REST)
+  const int32_t* scol;
+  const int32_t* cflag;   // per query tile: the two lists do not match (REST)
+  const float* lse_sel;   // the selected row's LSE, natural log (REST)
+  const float* mass;      // per selected block and query, the share of the probability (REST)
+};
+
+template <int D, bool PV, bool HB, bool REST = false>
 __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* __restrict__ q, int q_natural,
                                               const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
                                               const int32_t* __restrict__ row_ptr,
                                               const int32_t* __restrict__ col_idx, float scale_log2,
                                               uint16_t* __restrict__ o, int o_natural, float* __restrict__ lse,
                                               uint32_t* __restrict__ visited, float* __restrict__ bsum,
-                                              float* __restrict__ heat) {
-  static_assert(!(PV && HB), "the block heat is fused into the LSE-only pass");
+                                              float* __restrict__ heat, const HeatSplit hs) {
+  static_assert(!REST || (HB && !PV), "the rest of the dense row is an LSE-only heat pass");
+  constexpr bool MASS = PV && HB;
   constexpr int H = D / 32;   // copy instructions per thread and half tile (K or V^T)
   constexpr int kRowList = 2048;
   // K and V^T halves as four separate arrays: the compiler then knows that
@@ -1085,6 +1106,7 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
   __shared__ int32_t redo;
   __shared__ float s_inv[HB ? kTile : 1];   // heat: per query, the factor of its block sums
   __shared__ float s_pe[HB ? kTile : 1];    // heat: per query, one padding key's share of its row
+  __shared__ float s_sel[REST ? kTile : 1]; // rest: per query, the factor of its selected blocks' shares
   const int t = uni(p.attn_order[blockIdx.x]);
   if (t < 0) return;
   const int h = uni(p.row_head[t]);
@@ -1097,7 +1119,10 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + hrow * D, (int64_t)nt * kTile * D * 2);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(vt + htile * D * kTile, (int64_t)nt * kTile * D * 2);
   const int wave = uni(threadIdx.x >> 6);
-  const int beg = uni(row_ptr[t]), end = uni(row_ptr[t + 1]);
+  // REST: the row of the complement list sits at the dense row's start minus
+  // the selected entries before it
+  const int beg = uni(REST ? row_ptr[t] - hs.srow[t] : row_ptr[t]);
+  const int end = uni(REST ? row_ptr[t + 1] - hs.srow[t + 1] : row_ptr[t + 1]);
   const int w = threadIdx.x >> 6, lane = lane_id(), ln = lane & 31, hl = lane >> 5;
   const int koff = k_lane_offset<D>(threadIdx.x), voff = vt_lane_offset(threadIdx.x);
   const float c = scale_log2;
@@ -1132,13 +1157,14 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
   // (padsX = half_pads of the tile's valid count) so the loop issues no
   // vector loads besides the tile copies; rows longer than kRowList refill it
   // at that boundary.
-  auto fill_list = [&](int base) {
-    for (int e = threadIdx.x; e < kRowList && base + e < end; e += kThreads) {
-      const int jj = min(max(col_idx[base + e], 0), nt - 1);   // stay inside the head
+  auto fill_entries = [&](const int32_t* __restrict__ cols, int base, int lim) {
+    for (int e = threadIdx.x; e < kRowList && base + e < lim; e += kThreads) {
+      const int jj = min(max(cols[base + e], 0), nt - 1);   // stay inside the head
       const int nv = sh.valid[jj];
       rowlist[e] = (jj << 14) | (half_pads(nv, 1) << 7) | half_pads(nv, 0);
     }
   };
+  auto fill_list = [&](int base) { fill_entries(col_idx, base, end); };
 
   // exact maximum of a group over both lane halves
   auto group_max = [&](const f32x16& sg) {
@@ -1369,6 +1395,23 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
   //      K rows 64-127 and V^T keys 0-63 of b+1.
   // Each barrier first waits for the copies issued at the one before it, two
   // steps earlier.
+  // The softmax of one group with PV: p packed into pg, its sum into l and
+  // (MASS) into the block's sum, which store_bsum writes to bsum[position]
+  // once the block is complete (both lane halves).
+  auto soft_pv = [&](const f32x16& sg, bf16x8 (&pg)[2], bool first_of_block) {
+    const float g = exp_group<true>(sg, c, m_run, pg);
+    pin(pg);
+    l_run += g;
+    if constexpr (MASS) {
+      bs = first_of_block ? g : bs + g;
+      pin_sum(bs);
+    }
+  };
+  auto store_bsum = [&](int bpos) {
+    const float tot = bs + __shfl_xor(bs, 32, 64);
+    if (hl == 0) bsum[(int64_t)bpos * kTile + 32 * w + ln] = tot;
+  };
+
   auto run_fast_pv = [&]() {
     reset_row();
     fill_list(beg);
@@ -1390,8 +1433,7 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
     // step 1: S of group 1; the row's reference point (group 0's maximum) and group 0's softmax
     s1 = qk_group<D>(kh0, qf, 1, zero16);
     m_run = group_max(s0) * c;   // finite: key 0 always exists
-    l_run += exp_group<true>(s0, c, m_run, p0);
-    pin(p0);
+    soft_pv(s0, p0, true);
     interleave_step<8, 8>();
     __builtin_amdgcn_sched_barrier(0);
     for (int b = 0; b < nb; ++b) {
@@ -1414,14 +1456,12 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
       __builtin_amdgcn_sched_barrier(0);
       // step 4b+2: S of group 2, softmax of group 1, PV of group 0
       s0 = qk_pv_step<D>(kh1, qf, 2, vh0, p0, 0, oacc);
-      l_run += exp_group<true>(s1, c, m_run, p1);
-      pin(p1);
+      soft_pv(s1, p1, false);
       interleave_step<16, 4>();
       __builtin_amdgcn_sched_barrier(0);
       // step 4b+3: S of group 3, softmax of group 2, PV of group 1
       s1 = qk_pv_step<D>(kh1, qf, 3, vh0, p1, 1, oacc);
-      l_run += exp_group<true>(s0, c, m_run, p0);
-      pin(p0);
+      soft_pv(s0, p0, false);
       interleave_step<16, 4>();
       __builtin_amdgcn_sched_barrier(0);
       // barrier B: K rows 0-63 of b+1 and V^T keys 64-127 of b have landed
@@ -1432,14 +1472,13 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
         __builtin_amdgcn_sched_barrier(0);
         // step 4(b+1): S of group 0 of b+1, softmax of group 3 of b, PV of group 2 of b
         s0 = qk_pv_step<D>(kh0, qf, 0, vh1, p0, 2, oacc);
-        l_run += exp_group<true>(s1, c, m_run, p1);
-        pin(p1);
+        soft_pv(s1, p1, false);
+        if constexpr (MASS) store_bsum(beg + b);   // block b is complete
         interleave_step<16, 4>();
         __builtin_amdgcn_sched_barrier(0);
         // step 4(b+1)+1: S of group 1 of b+1, softmax of group 0 of b+1, PV of group 3 of b
         s1 = qk_pv_step<D>(kh0, qf, 1, vh1, p1, 3, oacc);
-        l_run += exp_group<true>(s0, c, m_run, p0);
-        pin(p0);
+        soft_pv(s0, p0, true);
         interleave_step<16, 4>();
         __builtin_amdgcn_sched_barrier(0);
         ent = en;
@@ -1447,8 +1486,8 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
       }
     }
     // drain: softmax of the last group 3 and PV of groups 2 and 3
-    l_run += exp_group<true>(s1, c, m_run, p1);
-    pin(p1);
+    soft_pv(s1, p1, false);
+    if constexpr (MASS) store_bsum(end - 1);
     pv_group<D>(vh1, p0, 2, oacc);
     interleave_step<8, 7>();
     __builtin_amdgcn_sched_barrier(0);
@@ -1456,23 +1495,25 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
     interleave_step<8, 0>();
   };
 
-  // Safe pass: per block a plain synchronous tile copy, then the four groups
-  // one after another with explicit masking and exact re-basing.
-  auto run_safe = [&]() {
+  // Safe pass over the blocks b0 .. b1-1 of the list cols: per block a plain
+  // synchronous tile copy, then the four groups one after another with
+  // explicit masking and exact re-basing; with SPV also the PV products.
+  auto run_safe = [&](auto pvc, const int32_t* __restrict__ cols, int b0, int b1) {
+    constexpr bool SPV = decltype(pvc)::value;
     reset_row();
-    for (int b = beg; b < end; ++b) {
-      const int slot = (b - beg) % kRowList;
+    for (int b = b0; b < b1; ++b) {
+      const int slot = (b - b0) % kRowList;
       if (slot == 0) {
         lds_sync();
-        fill_list(b);
+        fill_entries(cols, b, b1);
         dma_sync<0>();
       }
       const int ent = uni(rowlist[slot]);
       const int j = ent >> 14;
       const int nj = kTile - ((ent >> 7) & 127) - (ent & 127);
       lds_sync();                     // every wave is done with the previous tiles
-      copy_kv_halves<D, PV>(kh0, kh1, vh0, vh1, k + (hrow + (int64_t)kTile * j) * D,
-                            vt + (htile + j) * D * kTile);
+      copy_kv_halves<D, SPV>(kh0, kh1, vh0, vh1, k + (hrow + (int64_t)kTile * j) * D,
+                             vt + (htile + j) * D * kTile);
       lds_sync();
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
@@ -1491,35 +1532,56 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
         }
         bf16x8 pg[2];
         l_run += exp_group<true>(sg, c, m_run, pg);
-        if constexpr (PV) pv_group<D>(kt < 2 ? vh0 : vh1, pg, kt, oacc);
+        if constexpr (SPV) pv_group<D>(kt < 2 ? vh0 : vh1, pg, kt, oacc);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
 
-  if constexpr (PV) run_fast_pv(); else run_fast_lse();
+  // REST: a query tile whose two lists do not match gets NaN; an empty rest
+  // (every block selected) contributes nothing
+  bool rbad = false;
+  if constexpr (REST) rbad = uni(hs.cflag[t]) != 0;
+  const bool empty = REST && (rbad || end <= beg);
+  if (empty) reset_row();
+  else if constexpr (PV) run_fast_pv();
+  else run_fast_lse();
   float l_all = l_run + __shfl_xor(l_run, 32, 64);
-  const float pad_mass = (float)npad * __builtin_amdgcn_exp2f(-m_run);
+  const float pad_mass = empty ? 0.0f : (float)npad * __builtin_amdgcn_exp2f(-m_run);
   l_all -= pad_mass;
-  const bool bad = qvalid && !(l_all <= kMaxRowSum && pad_mass <= kMaxPadRatio * l_all);
+  const bool bad = !empty && qvalid && !(l_all <= kMaxRowSum && pad_mass <= kMaxPadRatio * l_all);
   if (__any(bad) && lane == 0) redo = 1;
   lds_sync();
   if (uni(redo)) {
-    run_safe();
+    run_safe(BoolC<PV>{}, col_idx, beg, end);
     l_all = l_run + __shfl_xor(l_run, 32, 64);
+  }
+  const float m_all = m_run;
+
+  // REST: the dense row's LSE (log2 units) from the rest's sum and the
+  // selected row's LSE: L2 = log2(2^ls2 + l * 2^m)
+  float L2 = 0.0f, ls2 = 0.0f;
+  if constexpr (REST) {
+    ls2 = hs.lse_sel[row0 + 32 * w + ln] * 1.4426950408889634f;
+    const float lr2 = m_all + __log2f(l_all);         // -inf for an empty rest
+    const float mx = fmaxf(ls2, lr2);
+    L2 = rbad ? __builtin_nanf("") : mx + __log2f(__builtin_amdgcn_exp2f(ls2 - mx) + __builtin_amdgcn_exp2f(lr2 - mx));
   }
 
   // Block heat of this query tile (HB): heat(i, j) is the mean over the
   // tile's valid queries of the probability mass on key tile j's valid keys.
   // After the fast pass, bsum holds per (block, query) the sum of
   // exp2(s*c - m) over the block's 128 key slots, so the mass is
-  // (bsum - pads(j) * exp2(-m)) / l with the row's final l.  After the safe
+  // (bsum - pads(j) * exp2(-m)) / l with the row's final l (REST: times
+  // 2^(m + log2 l - L2), the rest's share of the dense row).  After the safe
   // pass those sums are not on one reference point, so every block is walked
   // again with the final LSE and its exact masked mass stored instead.
+  // MASS keeps the masses per query (normalised in place) instead of
+  // reducing them; REST adds the selected blocks from those.
   if constexpr (HB) {
     const bool exact = uni(redo) != 0;
     if (exact) {
-      const float lse2 = m_run + __log2f(l_all);
+      const float lse2 = REST ? L2 : m_all + __log2f(l_all);
       for (int b = beg; b < end; ++b) {
         const int j = min(max(col_idx[b], 0), nt - 1);
         const int nj = sh.valid[j];
@@ -1542,26 +1604,64 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
       }
     }
     if (hl == 0) {
-      s_inv[32 * w + ln] = qvalid ? (exact ? 1.0f : 1.0f / l_all) : 0.0f;
-      s_pe[32 * w + ln] = (qvalid && !exact) ? __builtin_amdgcn_exp2f(-m_run) / l_all : 0.0f;
+      if constexpr (REST) {
+        s_inv[32 * w + ln] = qvalid ? (exact ? 1.0f : __builtin_amdgcn_exp2f(m_all - L2)) : 0.0f;
+        s_pe[32 * w + ln] = (qvalid && !exact && !empty) ? __builtin_amdgcn_exp2f(-L2) : 0.0f;
+        s_sel[32 * w + ln] = qvalid ? __builtin_amdgcn_exp2f(ls2 - L2) : 0.0f;
+      } else {
+        s_inv[32 * w + ln] = qvalid ? (exact ? 1.0f : 1.0f / l_all) : 0.0f;
+        s_pe[32 * w + ln] = (qvalid && !exact) ? __builtin_amdgcn_exp2f(-m_all) / l_all : 0.0f;
+      }
     }
     __syncthreads();                    // every wave's block sums and factors are visible
-    float pe = 0.0f;                    // one padding key's mass, summed over the queries
-#pragma unroll 4
-    for (int qq = 0; qq < kTile; ++qq) pe += s_pe[qq];
-    const float inv_nq = 1.0f / (float)sh.valid[i];
-    float* hrow_out = heat + p.head_pair_off[h] + (int64_t)i * nt;
-    for (int e = threadIdx.x; e < end - beg; e += kThreads) {
-      const int j = min(max(col_idx[beg + e], 0), nt - 1);
-      const float* bp = bsum + (int64_t)(beg + e) * kTile;
-      float acc = 0.0f;
-#pragma unroll 2
-      for (int q4 = 0; q4 < kTile; q4 += 4) {
-        const u32x4 bv = ld16(bp + q4);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc = fmaf(__uint_as_float(bv[u]), s_inv[q4 + u], acc);
+    const int nv_i = sh.valid[i];
+    if constexpr (MASS) {
+      // share of query qq's probability on block e: (bsum - pads * pe) / l,
+      // 0 for padding queries
+      for (int idx = threadIdx.x; idx < (end - beg) * kTile; idx += kThreads) {
+        const int e = idx >> 7, qq = idx & (kTile - 1);
+        const int j = min(max(col_idx[beg + e], 0), nt - 1);
+        float* bp = bsum + (int64_t)(beg + e) * kTile + qq;
+        *bp = qq < nv_i ? fmaf(-(float)(kTile - sh.valid[j]), s_pe[qq], *bp * s_inv[qq]) : 0.0f;
       }
-      hrow_out[j] = fmaf(-(float)(kTile - sh.valid[j]), pe, acc) * inv_nq;
+    } else {
+      float pe = 0.0f;                  // one padding key's mass, summed over the queries
+#pragma unroll 4
+      for (int qq = 0; qq < kTile; ++qq) pe += s_pe[qq];
+      const float inv_nq = 1.0f / (float)nv_i;
+      float* hrow_out = heat + p.head_pair_off[h] + (int64_t)i * nt;
+      if (rbad) {
+        for (int j = threadIdx.x; j < nt; j += kThreads) hrow_out[j] = __builtin_nanf("");
+      } else {
+        for (int e = threadIdx.x; e < end - beg; e += kThreads) {
+          const int j = min(max(col_idx[beg + e], 0), nt - 1);
+          const float* bp = bsum + (int64_t)(beg + e) * kTile;
+          float acc = 0.0f;
+#pragma unroll 2
+          for (int q4 = 0; q4 < kTile; q4 += 4) {
+            const u32x4 bv = ld16(bp + q4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc = fmaf(__uint_as_float(bv[u]), s_inv[q4 + u], acc);
+          }
+          hrow_out[j] = fmaf(-(float)(kTile - sh.valid[j]), pe, acc) * inv_nq;
+        }
+        if constexpr (REST) {
+          // the selected blocks: their shares of the selected row times 2^(ls2 - L2)
+          const int sb = uni(hs.srow[t]), se = uni(hs.srow[t + 1]);
+          for (int e = threadIdx.x; e < se - sb; e += kThreads) {
+            const int j = min(max(hs.scol[sb + e], 0), nt - 1);
+            const float* mp = hs.mass + (int64_t)(sb + e) * kTile;
+            float acc = 0.0f;
+#pragma unroll 2
+            for (int q4 = 0; q4 < kTile; q4 += 4) {
+              const u32x4 mv = ld16(mp + q4);
+#pragma unroll
+              for (int u = 0; u < 4; ++u) acc = fmaf(__uint_as_float(mv[u]), s_sel[q4 + u], acc);
+            }
+            hrow_out[j] = acc * inv_nq;
+          }
+        }
+      }
     }
   }
 
@@ -1592,7 +1692,8 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
         if (store) *reinterpret_cast<uint2*>(orow + 32 * db + 8 * jj + 4 * hl) = v;
       }
   }
-  if (lse && hl == 0) lse[row0 + 32 * w + ln] = m_run * 0.69314718055994531f + logf(l_all);
+  if (lse && hl == 0)
+    lse[row0 + 32 * w + ln] = REST ? L2 * 0.69314718055994531f : m_run * 0.69314718055994531f + logf(l_all);
   if (visited && threadIdx.x == 0) atomicAdd(visited, (uint32_t)(end - beg));
 }
 
@@ -1605,7 +1706,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(DevPlan p, const 
                                                               uint16_t* __restrict__ o, int o_natural,
                                                               float* __restrict__ lse, uint32_t* __restrict__ visited) {
   attn_fwd_body<D, PV, false>(p, q, q_natural, k, vt, row_ptr, col_idx, scale_log2, o, o_natural, lse, visited,
-                              nullptr, nullptr);
+                              nullptr, nullptr, HeatSplit{});
 }
 
 // The dense LSE and the block heat in one pass over an all-blocks mask: the
@@ -1619,7 +1720,79 @@ __global__ void __launch_bounds__(kThreads, 2) lse_heat_kernel(DevPlan p, const 
                                                               float* __restrict__ lse, float* __restrict__ bsum,
                                                               float* __restrict__ heat) {
   attn_fwd_body<D, false, true>(p, q, q_natural, k, k, row_ptr, col_idx, scale_log2, nullptr, 0, lse, nullptr, bsum,
-                                heat);
+                                heat, HeatSplit{});
+}
+
+// The attention and the dense heat of one layer without computing any
+// block's QK^T twice (veda_attn_fwd_lse_heat), in three launches:
+//  attn_mass_kernel: the attention over the selected CSR; it also leaves in
+//    mass[position][query] each selected block's share of the query's
+//    attention probability (over the selected blocks);
+//  complement_kernel: the rest of every dense row (its blocks that are not
+//    selected) as a CSR of its own;
+//  rest_heat_kernel: the LSE-only heat pass over that rest, which joins the
+//    two rows into the dense LSE and writes the heat of every block.
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2) attn_mass_kernel(
+    DevPlan p, const uint16_t* __restrict__ q, int q_natural, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    float scale_log2, uint16_t* __restrict__ o, int o_natural, float* __restrict__ lse, float* __restrict__ mass) {
+  attn_fwd_body<D, true, true>(p, q, q_natural, k, vt, row_ptr, col_idx, scale_log2, o, o_natural, lse, nullptr, mass,
+                               nullptr, HeatSplit{});
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2) rest_heat_kernel(
+    DevPlan p, const uint16_t* __restrict__ q, int q_natural, const uint16_t* __restrict__ k,
+    const int32_t* __restrict__ dense_row_ptr, const int32_t* __restrict__ rest_col, float scale_log2,
+    float* __restrict__ lse, float* __restrict__ bsum, float* __restrict__ heat, HeatSplit hs) {
+  attn_fwd_body<D, false, true, true>(p, q, q_natural, k, k, dense_row_ptr, rest_col, scale_log2, nullptr, 0, lse,
+                                      nullptr, bsum, heat, hs);
+}
+
+// One workgroup per query tile t: the entries of the dense row that are not
+// in the selected row, in order, at rest_col[dbeg - sbeg ..] (the selected
+// row is a subset of the dense row, so the rest of row t starts after the
+// rest of the rows before it).  Each dense entry finds its rank in the
+// selected row by binary search (both rows ascending).  cflag[t] = 1 when the
+// two rows do not fit that description (a selected column missing from the
+// dense row, repeats, a longer selected row); nothing is then written
+// outside the row's own range.
+__global__ void __launch_bounds__(kThreads) complement_kernel(const int32_t* __restrict__ drow,
+                                                              const int32_t* __restrict__ dcol,
+                                                              const int32_t* __restrict__ srow,
+                                                              const int32_t* __restrict__ scol, int64_t rest_nnz,
+                                                              int32_t* __restrict__ rest_col,
+                                                              int32_t* __restrict__ cflag) {
+  __shared__ int32_t found, outside;
+  const int64_t t = blockIdx.x;
+  const int dbeg = drow[t], dend = drow[t + 1], sbeg = srow[t], send = srow[t + 1];
+  const int cbeg = dbeg - sbeg, cend = dend - send;
+  const bool bad = sbeg < 0 || send < sbeg || cbeg < 0 || cend < cbeg || cend > rest_nnz;
+  if (threadIdx.x == 0) {
+    found = 0;
+    outside = 0;
+  }
+  __syncthreads();
+  if (!bad) {
+    for (int e = dbeg + (int)threadIdx.x; e < dend; e += kThreads) {
+      const int col = dcol[e];
+      int lo = sbeg, hi = send;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (scol[mid] < col) lo = mid + 1; else hi = mid;
+      }
+      if (lo < send && scol[lo] == col) {
+        atomicAdd(&found, 1);
+      } else {
+        const int pos = cbeg + (e - dbeg) - (lo - sbeg);
+        if (pos >= cbeg && pos < cend) rest_col[pos] = col;
+        else outside = 1;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) cflag[t] = (bad || outside || found != send - sbeg) ? 1 : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -2741,6 +2914,38 @@ hipError_t launch_lse_heat(const DevPlan& p, const void* q, int q_natural, const
   else
     hipLaunchKernelGGL(lse_heat_kernel<64>, grid, dim3(kThreads), 0, s, p, qq, q_natural, kk, row_ptr, col_idx, scale_log2, lse,
                        bsum, heat);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_lse_heat(const DevPlan& sel, const DevPlan& dense, const void* q, int q_natural,
+                                const void* k, const void* vt, const int32_t* row_ptr, const int32_t* col_idx,
+                                const int32_t* dense_row_ptr, const int32_t* dense_col_idx, float scale, void* o,
+                                int o_natural, float* lse_sel, float* dense_lse, float* heat,
+                                const SplitWorkspace& ws, hipStream_t s) {
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(vt);
+  uint16_t* oo = static_cast<uint16_t*>(o);
+  if (sel.head_dim == 128)
+    hipLaunchKernelGGL(attn_mass_kernel<128>, dim3((unsigned)sel.attn_grid), dim3(kThreads), 0, s, sel, qq, q_natural,
+                       kk, vv, row_ptr, col_idx, scale_log2, oo, o_natural, lse_sel, ws.mass);
+  else
+    hipLaunchKernelGGL(attn_mass_kernel<64>, dim3((unsigned)sel.attn_grid), dim3(kThreads), 0, s, sel, qq, q_natural,
+                       kk, vv, row_ptr, col_idx, scale_log2, oo, o_natural, lse_sel, ws.mass);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(complement_kernel, dim3((unsigned)dense.total_tiles), dim3(kThreads), 0, s, dense_row_ptr,
+                     dense_col_idx, row_ptr, col_idx, ws.rest_nnz, ws.rest_col, ws.cflag);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const HeatSplit hs{row_ptr, col_idx, ws.cflag, lse_sel, ws.mass};
+  if (dense.head_dim == 128)
+    hipLaunchKernelGGL(rest_heat_kernel<128>, dim3((unsigned)dense.attn_grid), dim3(kThreads), 0, s, dense, qq,
+                       q_natural, kk, dense_row_ptr, ws.rest_col, scale_log2, dense_lse, ws.rest_bsum, heat, hs);
+  else
+    hipLaunchKernelGGL(rest_heat_kernel<64>, dim3((unsigned)dense.attn_grid), dim3(kThreads), 0, s, dense, qq,
+                       q_natural, kk, dense_row_ptr, ws.rest_col, scale_log2, dense_lse, ws.rest_bsum, heat, hs);
   return hipGetLastError();
 }
 

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define VEDA_ABI_VERSION 8
+#define VEDA_ABI_VERSION 9
 
 typedef int32_t veda_status;
 enum {
@@ -124,7 +124,9 @@ typedef struct veda_plan_info {
   int64_t bwd_workspace_bytes; /* bytes veda_block_sparse_attn_bwd needs       */
   int32_t max_tiles_per_head;
   int32_t uploaded;           /* 1 after a successful veda_plan_upload        */
-  int64_t heat_workspace_bytes; /* bytes veda_dense_lse_heat needs (nnz*512)   */
+  int64_t heat_workspace_bytes; /* bytes veda_dense_lse_heat and (as the dense
+                                   plan) veda_attn_fwd_lse_heat need: about
+                                   nnz*516 + 4*(T + R)                        */
   int64_t reduce_workspace_bytes; /* bytes veda_mask_mass / veda_output_error
                                      need (per-head partial sums)             */
 } veda_plan_info;
@@ -328,8 +330,8 @@ veda_status veda_block_heat(const veda_plan* plan, const void* q, const void* k,
  *   lse:       device fp32 [R] natural log, or NULL (not stored)
  *   heat:      device fp32 [sum_h n_h^2], layout of the scores; every pair
  *              is written
- *   workspace: device scratch of at least heat_workspace_bytes (the plan's
- *              nnz x 128 x 4 bytes: one fp32 per block and query slot),
+ *   workspace: device scratch of at least heat_workspace_bytes (its first
+ *              nnz x 128 x 4 bytes are used: one fp32 per block and query),
  *              16-byte aligned; its contents on entry do not matter.
  * Errors: VEDA_ERR_WORKSPACE if workspace_bytes is too small;
  * VEDA_ERR_INVALID_ARG if lse, heat and workspace are not three different
@@ -338,6 +340,51 @@ veda_status veda_dense_lse_heat(const veda_plan* plan, const void* q, int32_t q_
                                 const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
                                 float* lse, float* heat, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* The block-sparse attention of a selected mask and the dense LSE and
+ * teacher block heat, without computing any block's scores twice (Key
+ * Features > "Veda sparse attention": the block-sparse forward over the kept
+ * blocks, and the teacher block heat from the dense LSE, fused kernel).
+ * Computes what
+ *   veda_block_sparse_attn_fwd(plan, q, q_layout, k, v_t, row_ptr, col_idx,
+ *                              softmax_scale, o, o_layout, lse, NULL, stream)
+ *   veda_dense_lse_heat(dense_plan, q, q_layout, k, dense_row_ptr,
+ *                       dense_col_idx, softmax_scale, dense_lse, heat, ...)
+ * compute: the attention over the selected blocks also keeps each selected
+ * block's share of every query's probability; an LSE-only pass over the
+ * rest of each dense row (its blocks that are not selected) joins its sum
+ * with the selected row's LSE into the dense LSE,
+ *   dense_lse[r] = log(exp(lse[r]) + sum over the rest of exp(s)),
+ * and forms the heat of every block of the dense row.  o and lse are bitwise
+ * those of veda_block_sparse_attn_fwd; dense_lse and heat agree with
+ * veda_dense_lse_heat to fp32 rounding (other summation order).
+ *   plan:       the plan of the selected mask; dense_plan: budget mode
+ *               VEDA_BUDGET_ALL (else VEDA_ERR_UNSUPPORTED), same segments,
+ *               heads, head dimension and tile shapes as plan (else
+ *               VEDA_ERR_SHAPE)
+ *   q, k, v_t:  as for veda_block_sparse_attn_fwd (q in q_layout, k permuted
+ *               [R, D], v_t tile-transposed [T, D, 128]); padding rows of k
+ *               and columns of v_t hold zeros
+ *   row_ptr, col_idx: the selected CSR as veda_select_blocks writes it for
+ *               plan: rows ascending, free of repeats, non-empty, each a
+ *               subset of the same row of the dense CSR; a query tile whose
+ *               selected row is not gets NaN in its dense_lse rows and its
+ *               heat row (o and lse as veda_block_sparse_attn_fwd gives them)
+ *   dense_row_ptr, dense_col_idx: dense_plan's all-blocks CSR, ascending
+ *   o:          device bf16 in o_layout (required); lse, dense_lse: device
+ *               fp32 [R] natural log, or NULL (not stored)
+ *   heat:       device fp32 [sum_h n_h^2], every pair written
+ *   workspace:  at least dense_plan's heat_workspace_bytes, 16-byte
+ *               aligned; contents on entry do not matter
+ * Three launches on `stream`.  Errors: VEDA_ERR_WORKSPACE if
+ * workspace_bytes is too small; VEDA_ERR_INVALID_ARG if an output aliases an
+ * input or another output, or the workspace is misaligned. */
+veda_status veda_attn_fwd_lse_heat(const veda_plan* plan, const veda_plan* dense_plan, const void* q,
+                                   int32_t q_layout, const void* k, const void* v_t, const int32_t* row_ptr,
+                                   const int32_t* col_idx, const int32_t* dense_row_ptr,
+                                   const int32_t* dense_col_idx, float softmax_scale, void* o, int32_t o_layout,
+                                   float* lse, float* dense_lse, float* heat, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /* Attention mass a block mask keeps ("Deploying this checkpoint", section 4:
  * recall of a predicted mask against the oracle mask; section 6: the share

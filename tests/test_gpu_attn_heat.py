@@ -1,0 +1,218 @@
+"""GPU parity of veda_attn_fwd_lse_heat (the block-sparse attention of the
+predicted mask, then the dense LSE and block heat from the rest of each dense
+row, no block's scores computed twice) through the C ABI (ctypes binding), on
+seeded synthetic inputs.
+
+Against the oracle: O and LSE of the predicted mask (bars of the attention:
+max-abs 2e-2, relative L2 1e-2, LSE 1e-3), the dense LSE (1e-3) and the block
+heat (1e-4).  Against the separate calls it replaces: O and LSE bitwise those
+of veda_block_sparse_attn_fwd.  Covered: the small workloads (partial tiles,
+two tile shapes, a dense segment, a diagonal-only mask, keep ratios 0 and 1,
+the latter with an empty rest in every row), all Q / O layouts, the exact
+fallback of either pass (late logits, logits far below zero), and a selected
+row that is not a subset of its dense row.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import veda_workloads as wl
+from oracle import veda_oracle as vo
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gpu_path as gp  # noqa: E402
+import test_gpu_parity as tp  # noqa: E402
+from block_sparse_attention_10_amd import binding as vb  # noqa: E402
+
+
+def _nan(shape, dtype):
+    return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
+
+
+def fused_run(w, inp, q_natural=True, o_natural=True, edit_sel=None):
+    """The predicted-mask front (permute, scores, selection) on the GPU, then
+    the fused call and, for comparison, veda_dense_lse_heat over the same
+    all-blocks CSR.  edit_sel(col_idx) may change the selected CSR first."""
+    g = gp.gpu_path(w, inp)
+    plan = g["plan"]
+    dense = vb.Plan.from_workload(w, budget_mode=wl.ALL_BLOCKS)
+    d_row = torch.empty(plan.T + 1, dtype=torch.int32, device="cuda")
+    d_col = torch.empty(dense.info["nnz"], dtype=torch.int32, device="cuda")
+    dense.select(g["scores"], d_row, d_col)
+    col = g["col_idx"].clone()
+    if edit_sel is not None:
+        edit_sel(col)
+    q = inp["q"].to("cuda") if q_natural else g["q_perm"]
+    ql = vb.VEDA_LAYOUT_NATURAL if q_natural else vb.VEDA_LAYOUT_PERMUTED
+    if o_natural:
+        o = _nan((w.num_tokens, w.num_heads, w.head_dim), torch.bfloat16)
+        ol = vb.VEDA_LAYOUT_NATURAL
+    else:
+        o = _nan((plan.R, w.head_dim), torch.bfloat16)
+        ol = vb.VEDA_LAYOUT_PERMUTED
+    lse, d_lse = _nan((plan.R,), torch.float32), _nan((plan.R,), torch.float32)
+    heat = _nan((plan.info["total_pairs"],), torch.float32)
+    ws = _nan((dense.info["heat_workspace_bytes"] // 4,), torch.float32)
+    plan.attention_lse_heat(dense, q, g["k_perm"], g["v_t"], g["row_ptr"], col, d_row, d_col, w.softmax_scale, o,
+                            lse, d_lse, heat, ws, o_layout=ol, q_layout=ql)
+    o2, lse2 = torch.full_like(o, float("nan")), _nan((plan.R,), torch.float32)
+    plan.attention(q, g["k_perm"], g["v_t"], g["row_ptr"], col, w.softmax_scale, o2, lse2, o_layout=ol, q_layout=ql)
+    dl3, heat3 = _nan((plan.R,), torch.float32), _nan((plan.info["total_pairs"],), torch.float32)
+    ws3 = _nan((dense.info["heat_workspace_bytes"] // 4,), torch.float32)
+    dense.lse_heat(q, g["k_perm"], d_row, d_col, w.softmax_scale, dl3, heat3, ws3, q_layout=ql)
+    torch.cuda.synchronize()
+    return g, dict(o=o, o_natural=o_natural, lse=lse, d_lse=d_lse, heat=heat, o2=o2, lse2=lse2, dl3=dl3,
+                   heat3=heat3)
+
+
+def check_against_oracle(w, inp, g, f, label):
+    op, qp, kp, sel = tp.check_front(w, inp, g)
+    vp = vo.permute_forward(op, gp.f64(inp["v"]))
+    O, L = vo.block_sparse_attention(op, qp, kp, vp, sel, w.softmax_scale)
+    vr = gp.valid_rows(op)
+    o_gpu = vo.permute_forward(op, gp.f64(f["o"])) if f["o_natural"] else gp.f64(f["o"])
+    max_abs, rel = gp.attn_errors(o_gpu, O, vr)
+    lse = f["lse"].cpu().numpy().astype(np.float64)
+    lse_err = float(np.max(np.abs(lse[vr] - L[vr])))
+    _, Ld = vo.block_sparse_attention(op, qp, kp, kp, vo.all_blocks_selection(op), w.softmax_scale)
+    dl = f["d_lse"].cpu().numpy().astype(np.float64)
+    dlse_err = float(np.max(np.abs(dl[vr] - Ld[vr])))
+    heat_ref = vo.block_heat(op, qp, kp, Ld, w.softmax_scale)
+    hg = gp.split_scores(None, op, f["heat"].cpu().numpy())
+    heat_err = max(float(np.max(np.abs(hg[h] - heat_ref[h]))) for h in range(w.num_heads))
+    print("%s %s: O max_abs %.3e rel_l2 %.3e lse %.3e dense lse %.3e heat %.3e" % (
+        label, w.name, max_abs, rel, lse_err, dlse_err, heat_err), flush=True)
+    assert max_abs <= gp.MAX_ABS and rel <= gp.REL_L2 and lse_err <= gp.LSE_ABS
+    assert dlse_err <= gp.LSE_ABS and heat_err <= gp.HEAT_ABS
+    return op
+
+
+def assert_same_as_separate(f, label):
+    """O and LSE bitwise those of the attention call; the dense LSE and heat
+    printed against the one-pass dense call (another summation order)."""
+    assert torch.equal(f["o"].view(torch.int16), f["o2"].view(torch.int16)), label
+    assert torch.equal(f["lse"].view(torch.int32), f["lse2"].view(torch.int32)), label
+    dl = float((f["d_lse"] - f["dl3"]).abs().nan_to_num(0.0).max())
+    dh = float((f["heat"] - f["heat3"]).abs().max())
+    print("%s: against veda_dense_lse_heat: dense lse %.2e heat %.2e" % (label, dl, dh), flush=True)
+
+
+@pytest.mark.parametrize("w", tp.small_workloads(), ids=lambda w: w.name)
+def test_fused_small_workloads(w):
+    inp = wl.make_inputs(w, seed=w.index)
+    g, f = fused_run(w, inp)
+    check_against_oracle(w, inp, g, f, "fast")
+    assert_same_as_separate(f, w.name)
+
+
+@pytest.mark.parametrize("layouts", [(False, False), (False, True), (True, False)],
+                         ids=["q_perm-o_perm", "q_perm-o_nat", "q_nat-o_perm"])
+def test_fused_layouts(layouts):
+    """Both Q layouts and both O layouts give the same O (bitwise) and pass the
+    oracle checks."""
+    w = tp.small_workloads()[1]
+    inp = wl.make_inputs(w, seed=w.index)
+    g, f = fused_run(w, inp, q_natural=layouts[0], o_natural=layouts[1])
+    op = check_against_oracle(w, inp, g, f, "layouts")
+    assert_same_as_separate(f, w.name)
+    _, ref = fused_run(w, inp)
+    o_ref = vo.permute_forward(op, gp.f64(ref["o"]))
+    o = vo.permute_forward(op, gp.f64(f["o"])) if f["o_natural"] else gp.f64(f["o"])
+    vr = gp.valid_rows(op)
+    assert np.array_equal(o[vr], o_ref[vr])
+    assert torch.equal(f["lse"].view(torch.int32), ref["lse"].view(torch.int32))
+
+
+def _first_tile_far_above(w, inp):
+    """Every query gains +10 on channel 0 and the keys of every head's first key
+    tile +80 there: those logits lie about 100 log2 units above all others, so
+    in the join of the selected row and the rest one side's sum is 2^-100 of
+    the other's (whichever holds the first tile)."""
+    op = vo.Plan.from_workload(w)
+    q, k = inp["q"].float(), inp["k"].float()
+    q[..., 0] += 10.0
+    for h in range(w.num_heads):
+        first = op.heads[h].perm()[:128]
+        k[torch.from_numpy(first[first >= 0].astype(np.int64)), h, 0] += 80.0
+    inp["q"], inp["k"] = q.to(torch.bfloat16), k.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("kind", ["guard_late_logits", "guard_far_below_zero", "first_tile_far_above"])
+def test_fused_fallback(kind):
+    if kind == "first_tile_far_above":
+        w = tp.small_workloads()[1]
+        inp = wl.make_inputs(w, seed=w.index)
+        _first_tile_far_above(w, inp)
+    else:
+        w = wl.Workload(98, "guard_keep_ratio", (wl.Segment(wl.VIDEO3D, (4, 10, 12), 0),), 2, 64,
+                        ((2, 8, 8),) * 2, wl.KEEP_RATIO, 1, 3)
+        inp = wl.make_inputs(w, seed=w.index)
+        if kind == "guard_late_logits":
+            tp._late_logits(w, inp)
+        else:
+            tp._far_below_zero(inp, 9)
+    g, f = fused_run(w, inp)
+    check_against_oracle(w, inp, g, f, kind)
+    assert_same_as_separate(f, kind)
+
+
+def test_fused_selected_row_not_in_dense_row():
+    """A selected column outside the dense row (here out of range) makes that
+    query tile's dense LSE and heat row NaN; every other tile's dense LSE and
+    heat row, and the attention of every other tile, are bitwise those of the
+    unedited call."""
+    w = tp.small_workloads()[1]
+    inp = wl.make_inputs(w, seed=w.index)
+
+    def edit(col):
+        col[0] = 1 << 20
+
+    _, f = fused_run(w, inp, o_natural=False, edit_sel=edit)
+    _, ref = fused_run(w, inp, o_natural=False)
+    op = vo.Plan.from_workload(w)
+    n0 = op.heads[0].num_tiles
+    dl, dl_ref = f["d_lse"].cpu(), ref["d_lse"].cpu()
+    assert torch.isnan(dl[:128]).all()
+    assert torch.equal(dl[128:].view(torch.int32), dl_ref[128:].view(torch.int32))
+    heat, heat_ref = f["heat"].cpu(), ref["heat"].cpu()
+    assert torch.isnan(heat[:n0]).all()
+    assert torch.equal(heat[n0:].view(torch.int32), heat_ref[n0:].view(torch.int32))
+    assert torch.equal(f["o"][128:].view(torch.int16), ref["o"][128:].view(torch.int16))
+    assert torch.equal(f["lse"][128:].view(torch.int32), ref["lse"][128:].view(torch.int32))
+
+
+def test_fused_errors():
+    """Host checks before any launch: a dense plan that is not all-blocks
+    (UNSUPPORTED), plans of different tile shapes (SHAPE), a short workspace
+    (WORKSPACE), an output aliasing an input (INVALID_ARG)."""
+    w = tp.small_workloads()[1]
+    inp = wl.make_inputs(w, seed=w.index)
+    g = gp.gpu_path(w, inp)
+    plan = g["plan"]
+    dense = vb.Plan.from_workload(w, budget_mode=wl.ALL_BLOCKS)
+    d_row = torch.empty(plan.T + 1, dtype=torch.int32, device="cuda")
+    d_col = torch.empty(dense.info["nnz"], dtype=torch.int32, device="cuda")
+    dense.select(g["scores"], d_row, d_col)
+    o = torch.empty((plan.R, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(plan.R, dtype=torch.float32, device="cuda")
+    heat = torch.empty(plan.info["total_pairs"], dtype=torch.float32, device="cuda")
+    ws = torch.empty(dense.info["heat_workspace_bytes"] // 4, dtype=torch.float32, device="cuda")
+
+    def call(pl, dn, o_=o, ws_=ws):
+        vb.veda_attn_fwd_lse_heat(pl.handle, dn.handle, g["q_perm"], g["k_perm"], g["v_t"], g["row_ptr"],
+                                  g["col_idx"], d_row, d_col, w.softmax_scale, o_, lse, None, heat, ws_)
+
+    for args, status in (((plan, plan), 3),
+                         ((plan, vb.Plan(w.segments, w.num_heads, w.head_dim, ((4, 4, 8),) * w.num_heads,
+                                         wl.ALL_BLOCKS)), 2),
+                         ((plan, dense, o, ws[:-64]), 4),
+                         ((plan, dense, g["k_perm"]), 1)):
+        with pytest.raises(vb.VedaError) as e:
+            call(*args)
+        assert e.value.status == status, (status, str(e.value))
+    torch.cuda.synchronize()

@@ -37,7 +37,7 @@ def test_abi_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert vb.veda_abi_version() == 8 == vb.ABI_VERSION
+    assert vb.veda_abi_version() == 9 == vb.ABI_VERSION
 
 
 def test_available_reports_reason_without_gpu():
@@ -176,6 +176,8 @@ def test_compute_calls_check_on_host_before_any_launch():
         assert lib.veda_block_heat(h, fake, fake, fake, ctypes.c_float(0.125), fake, None) == 6
         assert lib.veda_dense_lse_heat(h, fake, 0, fake, fake, fake, ctypes.c_float(0.125), fake, fake, fake,
                                        1 << 30, None) == 6
+        assert lib.veda_attn_fwd_lse_heat(h, h, fake, 0, fake, fake, fake, fake, fake, fake, ctypes.c_float(0.125),
+                                          fake, 0, None, None, fake, fake, 1 << 30, None) == 6
         assert lib.veda_mask_mass(h, fake, fake, fake, fake, fake, 1 << 20, None) == 6
         assert lib.veda_output_error(h, fake, fake, fake, fake, 1 << 20, None) == 6
         assert lib.veda_mask_transpose(h, fake, fake, fake, fake, fake, 1 << 30, None) == 6
