@@ -822,8 +822,9 @@ veda_status veda_attn_fwd_lse_heat(const veda_plan* plan, const veda_plan* dense
   if (sel_nnz > dense_nnz)
     return fail(VEDA_ERR_SHAPE, "plan keeps %lld blocks, more than the dense plan's %lld", (long long)sel_nnz,
                 (long long)dense_nnz);
-  // layout: shares of the selected blocks | block sums of the rest | rest
-  // columns | per-tile flags | the selected rows' LSE (if lse is NULL)
+  // layout: sums of the selected blocks | block sums of the rest | rest
+  // columns | per-tile flags | per-row factors | the selected rows' LSE (if
+  // lse is NULL)
   uint8_t* base = static_cast<uint8_t*>(workspace);
   SplitWorkspace ws{};
   ws.rest_nnz = dense_nnz - sel_nnz;
@@ -836,6 +837,8 @@ veda_status veda_attn_fwd_lse_heat(const veda_plan* plan, const veda_plan* dense
   off += align256(dense_nnz * 4);
   ws.cflag = reinterpret_cast<int32_t*>(base + off);
   off += align256(dense_plan->info.total_tiles * 4);
+  ws.fac = reinterpret_cast<float2*>(base + off);
+  off += align256(dense_plan->info.total_rows * 8);
   float* lse_sel = lse ? lse : reinterpret_cast<float*>(base + off);
   off += align256(dense_plan->info.total_rows * 4);
   if (off > dense_plan->info.heat_workspace_bytes)

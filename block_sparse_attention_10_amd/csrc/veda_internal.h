@@ -34,9 +34,11 @@ inline int64_t bwd_workspace_bytes(int64_t total_rows, int64_t total_tiles, int6
 // veda_dense_lse_heat: nnz x 128 block sums.  veda_attn_fwd_lse_heat (with
 // this plan as the dense plan): the same floats split between the selected
 // and the rest blocks (one more alignment gap), the rest's columns, one flag
-// per tile and an LSE of the selected rows when the caller passes none.
+// per tile, two factors per row and an LSE of the selected rows when the
+// caller passes none.
 inline int64_t heat_workspace_bytes(int64_t nnz, int64_t tiles, int64_t rows) {
-  return align256(nnz * 128 * 4) + 256 + align256(nnz * 4) + align256(tiles * 4) + align256(rows * 4);
+  return align256(nnz * 128 * 4) + 256 + align256(nnz * 4) + align256(tiles * 4) + align256(rows * 8) +
+         align256(rows * 4);
 }
 // Per-head partial sums of the two-launch reductions (mask mass: one per 16
 // rows; output error: 32 token chunks), two fp64 each.
@@ -95,11 +97,13 @@ hipError_t launch_attn_fwd(const DevPlan& p, const void* q, int q_natural, const
 hipError_t launch_lse_heat(const DevPlan& p, const void* q, int q_natural, const void* k, const int32_t* row_ptr,
                            const int32_t* col_idx, float scale, float* lse, float* bsum, float* heat,
                            hipStream_t s);
-// veda_attn_fwd_lse_heat's scratch: the selected blocks' shares (mass,
-// sel nnz x 128 floats), the rest's block sums (rest_nnz x 128 floats), the
-// rest CSR's columns and the per-tile mismatch flags
+// veda_attn_fwd_lse_heat's scratch: the selected blocks' sums of p (mass,
+// sel nnz x 128 floats) and per query the factors that make them shares
+// (fac), the rest's block sums (rest_nnz x 128 floats), the rest CSR's
+// columns and the per-tile mismatch flags
 struct SplitWorkspace {
   float* mass;
+  float2* fac;
   float* rest_bsum;
   int32_t* rest_col;
   int32_t* cflag;

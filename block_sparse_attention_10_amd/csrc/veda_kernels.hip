@@ -1068,8 +1068,9 @@ __device__ __forceinline__ int half_pads(int nv, int hh) {
 // query tile in two (veda_attn_fwd_lse_heat): its selected blocks and the
 // rest.
 //  PV and HB (attn_mass_kernel): the attention over the selected row that
-//    also keeps, per selected block and query, the block's share of the
-//    query's attention probability (bsum, normalised at the end of the row).
+//    also keeps, per selected block and query, the block's sum of p (bsum)
+//    and, per query, the two factors that turn those sums into the block's
+//    share of the query's probability over the selected blocks (fac).
 //  HB and REST (rest_heat_kernel): the LSE-only pass over the rest of the
 //    dense row (the complement list); at the end of the row it joins its sum
 //    with the selected row's LSE into the dense LSE and writes the heat of
@@ -1080,7 +1081,8 @@ struct HeatSplit {
   const int32_t* scol;
   const int32_t* cflag;   // per query tile: the two lists do not match (REST)
   const float* lse_sel;   // the selected row's LSE, natural log (REST)
-  const float* mass;      // per selected block and query, the share of the probability (REST)
+  const float* mass;      // per selected block and query, the sum of p (REST)
+  float2* fac;            // per query: share = bsum * x - pads * y (MASS writes, REST reads)
 };
 
 template <int D, bool PV, bool HB, bool REST = false>
@@ -1106,7 +1108,8 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
   __shared__ int32_t redo;
   __shared__ float s_inv[HB ? kTile : 1];   // heat: per query, the factor of its block sums
   __shared__ float s_pe[HB ? kTile : 1];    // heat: per query, one padding key's share of its row
-  __shared__ float s_sel[REST ? kTile : 1]; // rest: per query, the factor of its selected blocks' shares
+  __shared__ float s_sel[REST ? kTile : 1]; // rest: per query, the factors of its selected blocks' sums
+  __shared__ float s_spe[REST ? kTile : 1];
   const int t = uni(p.attn_order[blockIdx.x]);
   if (t < 0) return;
   const int h = uni(p.row_head[t]);
@@ -1576,8 +1579,8 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
   // 2^(m + log2 l - L2), the rest's share of the dense row).  After the safe
   // pass those sums are not on one reference point, so every block is walked
   // again with the final LSE and its exact masked mass stored instead.
-  // MASS keeps the masses per query (normalised in place) instead of
-  // reducing them; REST adds the selected blocks from those.
+  // MASS keeps the sums per query and stores each query's two factors
+  // instead of reducing them; REST adds the selected blocks from those.
   if constexpr (HB) {
     const bool exact = uni(redo) != 0;
     if (exact) {
@@ -1603,32 +1606,31 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
         if (hl == 0) bsum[(int64_t)b * kTile + 32 * w + ln] = bq;
       }
     }
-    if (hl == 0) {
-      if constexpr (REST) {
-        s_inv[32 * w + ln] = qvalid ? (exact ? 1.0f : __builtin_amdgcn_exp2f(m_all - L2)) : 0.0f;
-        s_pe[32 * w + ln] = (qvalid && !exact && !empty) ? __builtin_amdgcn_exp2f(-L2) : 0.0f;
-        s_sel[32 * w + ln] = qvalid ? __builtin_amdgcn_exp2f(ls2 - L2) : 0.0f;
-      } else {
-        s_inv[32 * w + ln] = qvalid ? (exact ? 1.0f : 1.0f / l_all) : 0.0f;
-        s_pe[32 * w + ln] = (qvalid && !exact) ? __builtin_amdgcn_exp2f(-m_all) / l_all : 0.0f;
-      }
-    }
-    __syncthreads();                    // every wave's block sums and factors are visible
-    const int nv_i = sh.valid[i];
     if constexpr (MASS) {
-      // share of query qq's probability on block e: (bsum - pads * pe) / l,
-      // 0 for padding queries
-      for (int idx = threadIdx.x; idx < (end - beg) * kTile; idx += kThreads) {
-        const int e = idx >> 7, qq = idx & (kTile - 1);
-        const int j = min(max(col_idx[beg + e], 0), nt - 1);
-        float* bp = bsum + (int64_t)(beg + e) * kTile + qq;
-        *bp = qq < nv_i ? fmaf(-(float)(kTile - sh.valid[j]), s_pe[qq], *bp * s_inv[qq]) : 0.0f;
-      }
+      // share of query r's probability on a block: bsum * x - pads * y
+      if (hl == 0)
+        hs.fac[row0 + 32 * w + ln] =
+            make_float2(qvalid ? (exact ? 1.0f : 1.0f / l_all) : 0.0f,
+                        (qvalid && !exact) ? __builtin_amdgcn_exp2f(-m_all) / l_all : 0.0f);
     } else {
+      if (hl == 0) {
+        if constexpr (REST) {
+          s_inv[32 * w + ln] = qvalid ? (exact ? 1.0f : __builtin_amdgcn_exp2f(m_all - L2)) : 0.0f;
+          s_pe[32 * w + ln] = (qvalid && !exact && !empty) ? __builtin_amdgcn_exp2f(-L2) : 0.0f;
+          const float2 f = hs.fac[row0 + 32 * w + ln];
+          const float g = __builtin_amdgcn_exp2f(ls2 - L2);
+          s_sel[32 * w + ln] = qvalid ? f.x * g : 0.0f;
+          s_spe[32 * w + ln] = qvalid ? f.y * g : 0.0f;
+        } else {
+          s_inv[32 * w + ln] = qvalid ? (exact ? 1.0f : 1.0f / l_all) : 0.0f;
+          s_pe[32 * w + ln] = (qvalid && !exact) ? __builtin_amdgcn_exp2f(-m_all) / l_all : 0.0f;
+        }
+      }
+      __syncthreads();                  // every wave's block sums and factors are visible
       float pe = 0.0f;                  // one padding key's mass, summed over the queries
 #pragma unroll 4
       for (int qq = 0; qq < kTile; ++qq) pe += s_pe[qq];
-      const float inv_nq = 1.0f / (float)nv_i;
+      const float inv_nq = 1.0f / (float)sh.valid[i];
       float* hrow_out = heat + p.head_pair_off[h] + (int64_t)i * nt;
       if (rbad) {
         for (int j = threadIdx.x; j < nt; j += kThreads) hrow_out[j] = __builtin_nanf("");
@@ -1647,6 +1649,9 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
         }
         if constexpr (REST) {
           // the selected blocks: their shares of the selected row times 2^(ls2 - L2)
+          float pes = 0.0f;
+#pragma unroll 4
+          for (int qq = 0; qq < kTile; ++qq) pes += s_spe[qq];
           const int sb = uni(hs.srow[t]), se = uni(hs.srow[t + 1]);
           for (int e = threadIdx.x; e < se - sb; e += kThreads) {
             const int j = min(max(hs.scol[sb + e], 0), nt - 1);
@@ -1658,7 +1663,7 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
 #pragma unroll
               for (int u = 0; u < 4; ++u) acc = fmaf(__uint_as_float(mv[u]), s_sel[q4 + u], acc);
             }
-            hrow_out[j] = acc * inv_nq;
+            hrow_out[j] = fmaf(-(float)(kTile - sh.valid[j]), pes, acc) * inv_nq;
           }
         }
       }
@@ -1726,8 +1731,9 @@ __global__ void __launch_bounds__(kThreads, 2) lse_heat_kernel(DevPlan p, const 
 // The attention and the dense heat of one layer without computing any
 // block's QK^T twice (veda_attn_fwd_lse_heat), in three launches:
 //  attn_mass_kernel: the attention over the selected CSR; it also leaves in
-//    mass[position][query] each selected block's share of the query's
-//    attention probability (over the selected blocks);
+//    mass[position][query] each selected block's sum of p and in fac[query]
+//    the factors that make it the block's share of the query's attention
+//    probability (over the selected blocks);
 //  complement_kernel: the rest of every dense row (its blocks that are not
 //    selected) as a CSR of its own;
 //  rest_heat_kernel: the LSE-only heat pass over that rest, which joins the
@@ -1736,9 +1742,10 @@ template <int D>
 __global__ void __launch_bounds__(kThreads, 2) attn_mass_kernel(
     DevPlan p, const uint16_t* __restrict__ q, int q_natural, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    float scale_log2, uint16_t* __restrict__ o, int o_natural, float* __restrict__ lse, float* __restrict__ mass) {
+    float scale_log2, uint16_t* __restrict__ o, int o_natural, float* __restrict__ lse, float* __restrict__ mass,
+    float2* __restrict__ fac) {
   attn_fwd_body<D, true, true>(p, q, q_natural, k, vt, row_ptr, col_idx, scale_log2, o, o_natural, lse, nullptr, mass,
-                               nullptr, HeatSplit{});
+                               nullptr, HeatSplit{nullptr, nullptr, nullptr, nullptr, nullptr, fac});
 }
 
 template <int D>
@@ -2929,17 +2936,17 @@ hipError_t launch_attn_lse_heat(const DevPlan& sel, const DevPlan& dense, const 
   uint16_t* oo = static_cast<uint16_t*>(o);
   if (sel.head_dim == 128)
     hipLaunchKernelGGL(attn_mass_kernel<128>, dim3((unsigned)sel.attn_grid), dim3(kThreads), 0, s, sel, qq, q_natural,
-                       kk, vv, row_ptr, col_idx, scale_log2, oo, o_natural, lse_sel, ws.mass);
+                       kk, vv, row_ptr, col_idx, scale_log2, oo, o_natural, lse_sel, ws.mass, ws.fac);
   else
     hipLaunchKernelGGL(attn_mass_kernel<64>, dim3((unsigned)sel.attn_grid), dim3(kThreads), 0, s, sel, qq, q_natural,
-                       kk, vv, row_ptr, col_idx, scale_log2, oo, o_natural, lse_sel, ws.mass);
+                       kk, vv, row_ptr, col_idx, scale_log2, oo, o_natural, lse_sel, ws.mass, ws.fac);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(complement_kernel, dim3((unsigned)dense.total_tiles), dim3(kThreads), 0, s, dense_row_ptr,
                      dense_col_idx, row_ptr, col_idx, ws.rest_nnz, ws.rest_col, ws.cflag);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const HeatSplit hs{row_ptr, col_idx, ws.cflag, lse_sel, ws.mass};
+  const HeatSplit hs{row_ptr, col_idx, ws.cflag, lse_sel, ws.mass, ws.fac};
   if (dense.head_dim == 128)
     hipLaunchKernelGGL(rest_heat_kernel<128>, dim3((unsigned)dense.attn_grid), dim3(kThreads), 0, s, dense, qq,
                        q_natural, kk, dense_row_ptr, ws.rest_col, scale_log2, dense_lse, ws.rest_bsum, heat, hs);

@@ -126,7 +126,7 @@ typedef struct veda_plan_info {
   int32_t uploaded;           /* 1 after a successful veda_plan_upload        */
   int64_t heat_workspace_bytes; /* bytes veda_dense_lse_heat and (as the dense
                                    plan) veda_attn_fwd_lse_heat need: about
-                                   nnz*516 + 4*(T + R)                        */
+                                   nnz*516 + 4*T + 12*R                       */
   int64_t reduce_workspace_bytes; /* bytes veda_mask_mass / veda_output_error
                                      need (per-head partial sums)             */
 } veda_plan_info;

@@ -9,9 +9,11 @@ dense mask bit-exact; O and LSE on every query tile of one head of each tile
 shape (heads 0 and 12); the whole path twice, bitwise equal.
 
 Packed sequence, all 24 heads: scores, CSR and dense mask bit-exact; O and LSE
-on every query tile of two heads; the dense LSE and the block heat (the fused
-one-pass call and the heat from a given LSE) on every head against the
-oracle's dense LSE and heat; the whole path twice, bitwise equal.
+on every query tile of two heads; the dense LSE and the block heat (the
+one-pass call, the heat from a given LSE, and the split call the benchmark
+runs, whose O and LSE are also bitwise the attention call's) on every head
+against the oracle's dense LSE and heat; the whole path twice, bitwise
+equal.
 
 Both run the calls the benchmark times: the permutation writes K and V^T
 only (Q is pooled), and the attention and the dense LSE and heat read Q in
@@ -155,8 +157,9 @@ def test_config5_packed_full():
     print("config 5: repeat, bitwise", flush=True)
     _check_repeat_bitwise(g, w, inp)
 
-    # the dense LSE and the block heat: the fused one-pass call (what the bench
-    # runs) and the heat from the all-blocks attention's LSE
+    # the dense LSE and the block heat: the one-pass call, the heat from the
+    # all-blocks attention's LSE, and the split call the benchmark runs (the
+    # predicted mask's attention, then the rest of each dense row)
     d = gp.gpu_path(w, inp, budget_mode=wl.ALL_BLOCKS, dense_mask=False)
     dplan = d["plan"]
     lse1 = torch.full_like(d["lse"], float("nan"))
@@ -169,9 +172,19 @@ def test_config5_packed_full():
     dplan.heat(d["q_perm"], d["k_perm"], d["lse"], w.softmax_scale, heat2)
     torch.cuda.synchronize()
     assert torch.equal(lse1.view(torch.int32), d["lse"].view(torch.int32)), "one-pass LSE != attention LSE"
+    o3 = torch.full_like(dev["o_nat"], float("nan"))
+    lse3, dl3 = torch.full_like(dev["lse"], float("nan")), torch.full_like(d["lse"], float("nan"))
+    heat3 = torch.full_like(heat1, float("nan"))
+    plan.attention_lse_heat(dplan, inp["q"].to("cuda"), dev["k_perm"], dev["v_t"], dev["row_ptr"], dev["col_idx"],
+                            d["row_ptr"], d["col_idx"], w.softmax_scale, o3, lse3, dl3, heat3, ws,
+                            o_layout=vb.VEDA_LAYOUT_NATURAL, q_layout=vb.VEDA_LAYOUT_NATURAL)
+    torch.cuda.synchronize()
+    assert torch.equal(o3.view(torch.int16), dev["o_nat"].view(torch.int16)), "split call O != attention O"
+    assert torch.equal(lse3.view(torch.int32), dev["lse"].view(torch.int32)), "split call LSE != attention LSE"
     lse_dense = lse1.cpu().numpy().astype(np.float64)
-    h1, h2 = heat1.cpu().numpy(), heat2.cpu().numpy()
-    del d, ws
+    lse_split = dl3.cpu().numpy().astype(np.float64)
+    h1, h2, h3 = heat1.cpu().numpy(), heat2.cpu().numpy(), heat3.cpu().numpy()
+    del d, ws, o3, lse3, dl3, heat3
     torch.cuda.empty_cache()
 
     print("config 5: oracle front, %d heads on %d workers" % (w.num_heads, opool.workers()), flush=True)
@@ -190,12 +203,15 @@ def test_config5_packed_full():
         n, r0, t0, p0 = vb.veda_plan_head(dplan.handle, h)
         valid = ~np.isnan(L)
         lerr = float(np.max(np.abs(lse_dense[r0:r0 + L.size][valid] - L[valid])))
+        lerr3 = float(np.max(np.abs(lse_split[r0:r0 + L.size][valid] - L[valid])))
         e1 = float(np.max(np.abs(h1[p0:p0 + n * n].reshape(n, n) - heat_ref)))
         e2 = float(np.max(np.abs(h2[p0:p0 + n * n].reshape(n, n) - heat_ref)))
+        e3 = float(np.max(np.abs(h3[p0:p0 + n * n].reshape(n, n) - heat_ref)))
         rows = float(np.max(np.abs(h1[p0:p0 + n * n].reshape(n, n).sum(axis=1) - 1.0)))
-        worst_heat, worst_lse = max(worst_heat, e1, e2), max(worst_lse, lerr)
-        assert lerr <= gp.LSE_ABS, ("dense lse", h, lerr)
-        assert e1 <= gp.HEAT_ABS and e2 <= gp.HEAT_ABS, ("heat", h, e1, e2)
-        assert rows <= 1e-3, ("heat row sum", h, rows)
+        rows3 = float(np.max(np.abs(h3[p0:p0 + n * n].reshape(n, n).sum(axis=1) - 1.0)))
+        worst_heat, worst_lse = max(worst_heat, e1, e2, e3), max(worst_lse, lerr, lerr3)
+        assert lerr <= gp.LSE_ABS and lerr3 <= gp.LSE_ABS, ("dense lse", h, lerr, lerr3)
+        assert e1 <= gp.HEAT_ABS and e2 <= gp.HEAT_ABS and e3 <= gp.HEAT_ABS, ("heat", h, e1, e2, e3)
+        assert rows <= 1e-3 and rows3 <= 1e-3, ("heat row sum", h, rows, rows3)
     print("config 5: dense LSE max |d| %.3e, heat max |d| %.3e over %d heads" % (worst_lse, worst_heat,
           w.num_heads), flush=True)
