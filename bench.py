@@ -305,9 +305,9 @@ def main():
         with open(args.traffic_json) as f:
             tj = json.load(f)
         key = ("attn_lse_heat_config%d" if layer.fused_heat else "attn_fwd_config%d") % args.config
-        if key in tj and tj[key].get("kernel_source_sha") == _kernel_sha():
+        if key in tj and tj[key].get("kernel_code_sha") == kernel_code_sha(vb.loaded_library(), w.head_dim):
             traffic = tj[key]["bytes_per_launch"]
-    except (OSError, ValueError):
+    except (OSError, ValueError, RuntimeError):
         pass
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -319,6 +319,7 @@ def main():
         "attn_kernel": ("attn_lse_heat_kernel (the attention inside the dense LSE + heat pass; its work counts "
                         "the dense QK^T products too)" if layer.fused_heat else "attn_fwd_kernel"),
         "attn_kernel_ms": round(attn_avg, 4), "attn_kernel_tflops": round(attn_tflops, 2),
+        "attn_kernel_code_sha": _code_sha_or_none(vb.loaded_library(), w.head_dim),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "attn_kernel_calls": {"n": len(attn_ms), "median_ms": round(float(np.median(attn_ms)), 4),
@@ -511,23 +512,61 @@ def time_search():
             "heads_per_chosen_shape": counts}
 
 
-FWD_SOURCE_END = b"// block heat from the dense LSE"
+def _code_sha_or_none(lib_path, head_dim):
+    try:
+        return kernel_code_sha(lib_path, head_dim)
+    except (OSError, ValueError, RuntimeError):
+        return None
 
 
-def _kernel_sha():
-    """Hash of the source the attention kernel is built from: the kernel file
-    up to the first section after the attention forward (shared helpers, the
-    layer kernels and the attention kernel itself), so that edits to later
-    kernels (heat, backward, search) keep the recorded traffic valid."""
+ATTN_SYMBOL = "_ZN4veda12_GLOBAL__N_115attn_fwd_kernelILi%dELb1EEEvNS_7DevPlanEPKtiS4_S4_PKiS6_fPtiPfPj"
+
+
+def kernel_code_sha(lib_path, head_dim=128):
+    """Hash of the attention kernel's machine code in the library that runs:
+    the bytes of attn_fwd_kernel<D, true> in the gfx950 code object of the
+    library's offload bundle, plus its kernel descriptor with the entry
+    offset zeroed (the only field that depends on where the linker put the
+    kernel).  Recorded traffic stays valid while this hash is unchanged,
+    whatever else changes in the library."""
     import hashlib
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_sparse_attention_10_amd", "csrc",
-                        "veda_kernels.hip")
-    with open(path, "rb") as f:
-        src = f.read()
-    end = src.find(FWD_SOURCE_END)
-    if end < 0:
-        raise RuntimeError("kernel source layout changed: no heat section marker")
-    return hashlib.sha256(src[:end]).hexdigest()[:16]
+    import struct
+    with open(lib_path, "rb") as f:
+        data = f.read()
+    b0 = data.find(b"__CLANG_OFFLOAD_BUNDLE__")
+    if b0 < 0:
+        raise RuntimeError("no offload bundle in " + lib_path)
+    n = struct.unpack_from("<Q", data, b0 + 24)[0]
+    off, elf = b0 + 32, None
+    for _ in range(n):
+        o, size, tl = struct.unpack_from("<QQQ", data, off)
+        triple = data[off + 24: off + 24 + tl]
+        off += 24 + tl
+        if triple.endswith(b"gfx950"):
+            elf = data[b0 + o: b0 + o + size]
+    if elf is None or elf[:4] != b"\x7fELF":
+        raise RuntimeError("no gfx950 code object in " + lib_path)
+    shoff = struct.unpack_from("<Q", elf, 0x28)[0]
+    shentsize, shnum = struct.unpack_from("<HH", elf, 0x3A)
+    # section headers: name, type, flags, addr, offset, size, link, info, align, entsize
+    secs = [struct.unpack_from("<IIQQQQIIQQ", elf, shoff + k * shentsize) for k in range(shnum)]
+    symtab = [sh for sh in secs if sh[1] == 2][0]          # SHT_SYMTAB
+    strtab = secs[symtab[6]]
+    sym = (ATTN_SYMBOL % head_dim).encode()
+    parts = {}
+    for k in range(symtab[5] // 24):
+        st_name, _, _, st_shndx, st_value, st_size = struct.unpack_from("<IBBHQQ", elf, symtab[4] + 24 * k)
+        a = strtab[4] + st_name
+        name = elf[a: elf.index(b"\0", a)]
+        if name in (sym, sym + b".kd"):
+            sh = secs[st_shndx]
+            fo = sh[4] + (st_value - sh[3])
+            parts[name] = bytearray(elf[fo: fo + st_size])
+    if len(parts) != 2:
+        raise RuntimeError("attention kernel symbol not found in " + lib_path)
+    kd = parts[sym + b".kd"]
+    kd[16:24] = bytes(8)                                    # kernel_code_entry_byte_offset
+    return hashlib.sha256(bytes(parts[sym]) + bytes(kd)).hexdigest()[:16]
 
 
 if __name__ == "__main__":
