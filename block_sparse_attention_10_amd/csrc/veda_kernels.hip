@@ -1498,6 +1498,52 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
     interleave_step<8, 0>();
   };
 
+  // A wave whose 32 query slots all lie past the tile's valid count holds
+  // only padding queries.  It computes nothing: it issues its share of the
+  // tile copies and meets the barriers of run_fast_pv (with PV) or
+  // run_fast_lse, in the same order, and (HB) stores zero block sums for its
+  // queries where those passes store theirs.  About a tenth of the waves of
+  // the video workloads (edge tiles of the grid).
+  auto run_copies = [&]() {
+    reset_row();
+    fill_list(beg);
+    dma_sync<0>();
+    const int nb = end - beg;
+    int jc = uni(rowlist[0]) >> 14;
+    dma_k_half<D>(kh0, rk, jc * kTile * D * 2, koff, wave, 0);
+    dma_k_half<D>(kh1, rk, jc * kTile * D * 2, koff, wave, 1);
+    if constexpr (PV) dma_vt_half<D>(vh0, rv, jc * kTile * D * 2, voff, wave, 0);
+    dma_sync<0>();
+    auto zero_sum = [&](int bpos) {
+      if constexpr (HB) {
+        if (hl == 0) bsum[(int64_t)bpos * kTile + 32 * w + ln] = 0.0f;
+      }
+    };
+    for (int b = 0; b < nb; ++b) {
+      const bool more = b + 1 < nb;
+      dma_sync<0>();                  // barrier A
+      int jn = 0;
+      if (more) {
+        const int slot = (b + 1) % kRowList;
+        if (slot == 0) {
+          fill_list(beg + b + 1);
+          dma_sync<0>();
+        }
+        jn = uni(rowlist[slot]) >> 14;
+        dma_k_half<D>(kh0, rk, jn * kTile * D * 2, koff, wave, 0);
+      }
+      if constexpr (PV) dma_vt_half<D>(vh1, rv, jc * kTile * D * 2, voff, wave, 1);
+      dma_sync<0>();                  // barrier B
+      if (more) {
+        dma_k_half<D>(kh1, rk, jn * kTile * D * 2, koff, wave, 1);
+        if constexpr (PV) dma_vt_half<D>(vh0, rv, jn * kTile * D * 2, voff, wave, 0);
+        zero_sum(beg + b);
+        jc = jn;
+      }
+    }
+    zero_sum(end - 1);
+  };
+
   // Safe pass over the blocks b0 .. b1-1 of the list cols: per block a plain
   // synchronous tile copy, then the four groups one after another with
   // explicit masking and exact re-basing; with SPV also the PV products.
@@ -1546,11 +1592,13 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
   bool rbad = false;
   if constexpr (REST) rbad = uni(hs.cflag[t]) != 0;
   const bool empty = REST && (rbad || end <= beg);
+  const bool wdead = 32 * wave >= sh.valid[i];   // only padding queries
   if (empty) reset_row();
+  else if (wdead) run_copies();
   else if constexpr (PV) run_fast_pv();
   else run_fast_lse();
   float l_all = l_run + __shfl_xor(l_run, 32, 64);
-  const float pad_mass = empty ? 0.0f : (float)npad * __builtin_amdgcn_exp2f(-m_run);
+  const float pad_mass = (empty || wdead) ? 0.0f : (float)npad * __builtin_amdgcn_exp2f(-m_run);
   l_all -= pad_mass;
   const bool bad = !empty && qvalid && !(l_all <= kMaxRowSum && pad_mass <= kMaxPadRatio * l_all);
   if (__any(bad) && lane == 0) redo = 1;
@@ -1558,6 +1606,11 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
   if (uni(redo)) {
     run_safe(BoolC<PV>{}, col_idx, beg, end);
     l_all = l_run + __shfl_xor(l_run, 32, 64);
+  } else if (wdead) {
+    // a padding query's outputs: O = 0 and LSE = 0 (finite, so that a
+    // backward over these rows, whose Q and dO are zero, stays finite)
+    l_all = 1.0f;
+    m_run = 0.0f;
   }
   const float m_all = m_run;
 
