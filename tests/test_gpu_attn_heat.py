@@ -216,3 +216,64 @@ def test_fused_errors():
             call(*args)
         assert e.value.status == status, (status, str(e.value))
     torch.cuda.synchronize()
+
+
+def test_fused_rows_longer_than_the_staged_list():
+    """The split call on rows of 2,300 key blocks (a dense 1-D segment, one
+    head, D = 64, keep ratio 1/20): the rest of every dense row, about 2,185
+    blocks, is longer than the staged block list, which refills mid-row.
+    Sampled query tiles' O, LSE, dense LSE and heat rows against the oracle;
+    O and LSE bitwise those of the attention call; every heat row sums to 1."""
+    n_tok = 128 * 2299 + 37
+    w = wl.Workload(99, "long_rows_2300_tiles", (wl.Segment(wl.DENSE1D, (1, 1, n_tok), 0),), 1, 64,
+                    ((2, 8, 8),), wl.KEEP_RATIO, 1, 20)
+    inp = wl.make_inputs(w, seed=w.index)
+    g, f = fused_run(w, inp, o_natural=False)
+    assert_same_as_separate(f, w.name)
+    op, qp, kp, sel = tp.check_front(w, inp, g)
+    n = op.heads[0].num_tiles
+    assert n - max(len(r) for r in sel[0]) > 2048      # the rest exceeds the staged list
+    vp = vo.permute_forward(op, gp.f64(inp["v"]))
+    o, lse = gp.f64(f["o"]), f["lse"].cpu().numpy().astype(np.float64)
+    dl = f["d_lse"].cpu().numpy().astype(np.float64)
+    hg = f["heat"].cpu().numpy().reshape(n, n)
+    assert np.max(np.abs(hg.sum(axis=1) - 1.0)) <= 1e-3
+    sampled = (0, 1500, n - 1)
+    Ld = np.full(op.total_rows, np.nan)
+    for i in sampled:
+        nv = op.heads[0].tiles[i].valid
+        rows = slice(128 * i, 128 * i + nv)
+        Oi, Li = vo.attention_row_tile(op, 0, i, qp, kp, vp, sel[0][i], w.softmax_scale)
+        _, Ldi = vo.attention_row_tile(op, 0, i, qp, kp, vp, range(n), w.softmax_scale)
+        Ld[rows] = Ldi
+        assert np.max(np.abs(o[rows] - Oi)) <= gp.MAX_ABS
+        assert np.max(np.abs(lse[rows] - Li)) <= gp.LSE_ABS
+        assert np.max(np.abs(dl[rows] - Ldi)) <= gp.LSE_ABS
+    ref = vo.block_heat(op, qp, kp, Ld, w.softmax_scale, rows=sampled)[0]
+    for i in sampled:
+        err = float(np.max(np.abs(hg[i] - ref[i])))
+        print("long rows tile %d: heat max_abs %.3e" % (i, err), flush=True)
+        assert err <= gp.HEAT_ABS
+
+
+def test_fused_without_lse():
+    """lse = NULL: the selected rows' LSE goes to the workspace instead; O,
+    the dense LSE and the heat are bitwise those of the call with lse."""
+    w = tp.small_workloads()[1]
+    inp = wl.make_inputs(w, seed=w.index)
+    g, f = fused_run(w, inp, o_natural=False)
+    plan = g["plan"]
+    dense = vb.Plan.from_workload(w, budget_mode=wl.ALL_BLOCKS)
+    d_row = torch.empty(plan.T + 1, dtype=torch.int32, device="cuda")
+    d_col = torch.empty(dense.info["nnz"], dtype=torch.int32, device="cuda")
+    dense.select(g["scores"], d_row, d_col)
+    o = _nan((plan.R, w.head_dim), torch.bfloat16)
+    d_lse = _nan((plan.R,), torch.float32)
+    heat = _nan((plan.info["total_pairs"],), torch.float32)
+    ws = _nan((dense.info["heat_workspace_bytes"] // 4,), torch.float32)
+    plan.attention_lse_heat(dense, inp["q"].to("cuda"), g["k_perm"], g["v_t"], g["row_ptr"], g["col_idx"], d_row,
+                            d_col, w.softmax_scale, o, None, d_lse, heat, ws, q_layout=vb.VEDA_LAYOUT_NATURAL)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), f["o"].view(torch.int16))
+    assert torch.equal(d_lse.view(torch.int32), f["d_lse"].view(torch.int32))
+    assert torch.equal(heat.view(torch.int32), f["heat"].view(torch.int32))
