@@ -1622,6 +1622,7 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
     const float lr2 = m_all + __log2f(l_all);         // -inf for an empty rest
     const float mx = fmaxf(ls2, lr2);
     L2 = rbad ? __builtin_nanf("") : mx + __log2f(__builtin_amdgcn_exp2f(ls2 - mx) + __builtin_amdgcn_exp2f(lr2 - mx));
+    if (wdead && !uni(redo) && !rbad) L2 = 0.0f;   // padding queries: LSE 0, as the passes above give them
   }
 
   // Block heat of this query tile (HB): heat(i, j) is the mean over the

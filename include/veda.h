@@ -289,7 +289,8 @@ veda_status veda_select_blocks(const veda_plan* plan, const float* scores, int32
  *           products; v_t is not read), bitwise equal to the LSE of a call
  *           with o, e.g. the dense LSE that veda_block_heat takes.
  *   lse:    device fp32 [R] natural log, permuted row order, or NULL (not
- *           both o and lse NULL: VEDA_ERR_INVALID_ARG)
+ *           both o and lse NULL: VEDA_ERR_INVALID_ARG); rows of padding
+ *           slots unspecified (finite)
  *   blocks_visited: device uint32 counter the kernel adds the number of
  *           blocks it computed to (caller zeroes it), or NULL.
  * softmax_scale must be finite and > 0 (1/sqrt(D) for the usual scale). */
@@ -357,7 +358,8 @@ veda_status veda_dense_lse_heat(const veda_plan* plan, const void* q, int32_t q_
  *   dense_lse[r] = log(exp(lse[r]) + sum over the rest of exp(s)),
  * and forms the heat of every block of the dense row.  o and lse are bitwise
  * those of veda_block_sparse_attn_fwd; dense_lse and heat agree with
- * veda_dense_lse_heat to fp32 rounding (other summation order).
+ * veda_dense_lse_heat to fp32 rounding (other summation order; dense_lse
+ * rows of padding slots are unspecified but finite, as in both calls).
  *   plan:       the plan of the selected mask; dense_plan: budget mode
  *               VEDA_BUDGET_ALL (else VEDA_ERR_UNSUPPORTED), same segments,
  *               heads, head dimension and tile shapes as plan (else

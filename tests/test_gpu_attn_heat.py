@@ -219,13 +219,13 @@ def test_fused_errors():
 
 
 def test_fused_rows_longer_than_the_staged_list():
-    """The split call on rows of 2,300 key blocks (a dense 1-D segment, one
-    head, D = 64, keep ratio 1/20): the rest of every dense row, about 2,185
-    blocks, is longer than the staged block list, which refills mid-row.
-    Sampled query tiles' O, LSE, dense LSE and heat rows against the oracle;
-    O and LSE bitwise those of the attention call; every heat row sums to 1."""
-    n_tok = 128 * 2299 + 37
-    w = wl.Workload(99, "long_rows_2300_tiles", (wl.Segment(wl.DENSE1D, (1, 1, n_tok), 0),), 1, 64,
+    """The split call on rows of 2,300 key blocks (a 2 x 8 x 18,397 video
+    grid, one head, D = 64, keep ratio 1/20; the last tile partial): the rest
+    of every dense row, about 2,185 blocks, is longer than the staged block
+    list, which refills mid-row.  Sampled query tiles' O, LSE, dense LSE and
+    heat rows against the oracle; O and LSE bitwise those of the attention
+    call; every heat row sums to 1."""
+    w = wl.Workload(99, "long_rows_2300_tiles", (wl.Segment(wl.VIDEO3D, (2, 8, 18397), 0),), 1, 64,
                     ((2, 8, 8),), wl.KEEP_RATIO, 1, 20)
     inp = wl.make_inputs(w, seed=w.index)
     g, f = fused_run(w, inp, o_natural=False)
