@@ -63,9 +63,10 @@ class Layer:
 
     def __init__(self, w, inputs, vb, q_copy=False, separate_heat=False):
         self.w, self.vb = w, vb
-        # with the heat: the attention runs inside the dense LSE + heat pass
-        # (veda_attn_fwd_lse_heat) unless separate_heat
-        self.fused_heat = bool(w.with_heat) and not separate_heat
+        # with the heat: the attention and the dense LSE + heat in one call
+        # (veda_attn_fwd_lse_heat: no block's scores computed twice) unless
+        # separate_heat
+        self.split_heat = bool(w.with_heat) and not separate_heat
         # q_copy: the permutation also writes the permuted copy of Q and the
         # attention reads it; by default the attention gathers Q's rows from
         # the natural [N, H, D] layout and no copy of Q is written
@@ -117,13 +118,13 @@ class Layer:
         p.score_pooled(x["w_q"], x["w_k"], self.scores, self.ws)
         p.select(self.scores, self.row_ptr, self.col)
         q, ql = self.q_of(x)
-        if self.fused_heat:
+        if self.split_heat:
             d = self.dense
             d.select(self.scores, self.d_row_ptr, self.d_col)
         if time_attn:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-        if self.fused_heat:
+        if self.split_heat:
             # the attention of the predicted mask, the dense LSE and the block heat in one pass
             p.attention_lse_heat(d, q, self.kp, self.vt, self.row_ptr, self.col, self.d_row_ptr, self.d_col,
                                  w.softmax_scale, self.o_nat, self.lse, self.d_lse, self.heat, self.heat_ws,
@@ -136,7 +137,7 @@ class Layer:
             self.attn_events.append((e0, e1))
         if self.dense is not None:
             d = self.dense
-            if not self.fused_heat:
+            if not self.split_heat:
                 d.select(self.scores, self.d_row_ptr, self.d_col)
                 # the dense LSE and the block heat in one pass over all blocks
                 d.lse_heat(q, self.kp, self.d_row_ptr, self.d_col, w.softmax_scale, self.d_lse, self.heat,
@@ -267,10 +268,10 @@ def main():
     p = layer.plan
     nnz = p.info["nnz"]
     flops_attn = 4.0 * 128 * 128 * w.head_dim * nnz
-    # the timed kernel's work: the attention, plus with the fused heat pass the
+    # the timed kernels' work: the attention, plus with the split heat call the
     # dense QK^T products (2 * 128^2 * D per block of the all-blocks mask)
     flops_kernel = flops_attn
-    if layer.fused_heat:
+    if layer.split_heat:
         flops_kernel += 2.0 * 128 * 128 * w.head_dim * layer.dense.info["nnz"]
     print("bench: warmup %d, steps %d, nnz %d" % (args.warmup, args.steps, nnz), file=sys.stderr, flush=True)
     for s in range(args.warmup):
@@ -304,7 +305,7 @@ def main():
     try:
         with open(args.traffic_json) as f:
             tj = json.load(f)
-        key = ("attn_lse_heat_config%d" if layer.fused_heat else "attn_fwd_config%d") % args.config
+        key = ("attn_lse_heat_config%d" if layer.split_heat else "attn_fwd_config%d") % args.config
         if key in tj and tj[key].get("kernel_code_sha") == kernel_code_sha(vb.loaded_library(), w.head_dim):
             traffic = tj[key]["bytes_per_launch"]
     except (OSError, ValueError, RuntimeError):
@@ -316,8 +317,9 @@ def main():
         "config": {"workload": "config %d %s" % (args.config, w.describe()), "tokens": w.num_tokens,
                    "heads": w.num_heads, "head_dim": w.head_dim, "nnz_blocks": nnz,
                    "block_density": round(nnz / p.info["total_pairs"], 4), "parallelism": "single GPU"},
-        "attn_kernel": ("attn_lse_heat_kernel (the attention inside the dense LSE + heat pass; its work counts "
-                        "the dense QK^T products too)" if layer.fused_heat else "attn_fwd_kernel"),
+        "attn_kernel": ("veda_attn_fwd_lse_heat: attn_mass_kernel + complement_kernel + rest_heat_kernel (the "
+                        "attention and the dense LSE + heat; its work counts the dense QK^T products too)"
+                        if layer.split_heat else "attn_fwd_kernel"),
         "attn_kernel_ms": round(attn_avg, 4), "attn_kernel_tflops": round(attn_tflops, 2),
         "attn_kernel_code_sha": _code_sha_or_none(vb.loaded_library(), w.head_dim),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
@@ -325,7 +327,7 @@ def main():
         "attn_kernel_calls": {"n": len(attn_ms), "median_ms": round(float(np.median(attn_ms)), 4),
                               "min_ms": round(float(np.min(attn_ms)), 4),
                               "p90_ms": round(float(np.percentile(attn_ms, 90)), 4)},
-        "attn_valid_only_tflops": None if layer.fused_heat else round(valid_flops / (attn_avg * 1e-3) / 1e12, 2),
+        "attn_valid_only_tflops": None if layer.split_heat else round(valid_flops / (attn_avg * 1e-3) / 1e12, 2),
         "attn_cold_cache": cold,
         "permute_qkv": perm,
         "q_operand": "permuted copy written by the permutation" if args.q_copy else
@@ -439,7 +441,7 @@ def attention_cold(layer, n):
         ms.append(e0.elapsed_time(e1))
     del scrub
     note = "after a 1 GiB device write per call"
-    if layer.fused_heat:
+    if layer.split_heat:
         note += "; the separate attention call (veda_block_sparse_attn_fwd), not the fused heat pass"
     return {"n": n, "mean_ms": round(float(np.mean(ms)), 4), "note": note}
 
