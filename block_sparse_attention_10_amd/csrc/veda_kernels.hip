@@ -1209,8 +1209,10 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
   // the sum of p of one group, into l and (HB) the block's sum
   auto sum_group = [&](const f32x16& sg, bool first_of_block) {
     const float g = exp_sum(sg, c, m_run);
-    l_run += g;
-    pin_sum(l_run);
+    if constexpr (!REST) {   // REST: l gathers whole blocks' sums in store_block_sum
+      l_run += g;
+      pin_sum(l_run);
+    }
     if constexpr (HB) {
       bs = first_of_block ? g : bs + g;
       pin_sum(bs);
@@ -1320,6 +1322,7 @@ __device__ __forceinline__ void attn_fwd_body(const DevPlan& p, const uint16_t* 
     const f32x16 zero16 = {};
     f32x16 s0, s1;
     auto store_block_sum = [&](int bpos) {
+      if constexpr (REST) l_run += bs;
       if constexpr (HB) {
         const float tot = bs + __shfl_xor(bs, 32, 64);
         if (hl == 0) bsum[(int64_t)bpos * kTile + 32 * w + ln] = tot;
