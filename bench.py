@@ -223,15 +223,43 @@ def cpu_baseline(w, inp, budget_s, total_blocks):
     H = w.num_heads
     layer_s = {k: v * H / heads_front for k, v in t.items() if k != "attention"}
     layer_s["attention"] = t["attention"] * total_blocks / blocks_attn
+    heat_note = ""
+    if w.with_heat:
+        # the dense LSE (the oracle's attention over every key tile of the
+        # row; it also forms an O that is not used) and the block heat of
+        # query tiles 0, 1, ... of head 0, about a quarter of budget_s,
+        # extrapolated by query tiles (every head of the packed workload has
+        # the same tile count)
+        sub = vo.Plan(w.segments, 1, w.head_dim, [w.tile_shapes[0]], wl.ALL_BLOCKS, 1, 1, 0)
+        qp, kp = vo.permute_forward(sub, qn[:, :1]), vo.permute_forward(sub, kn[:, :1])
+        n = sub.heads[0].num_tiles
+        L = np.full(sub.total_rows, np.nan)
+        rows = []
+        d0 = clock()
+        for i in range(n):
+            _, Li = vo.attention_row_tile(sub, 0, i, qp, kp, kp, range(n), w.softmax_scale)
+            L[128 * i: 128 * i + sub.heads[0].tiles[i].valid] = Li
+            rows.append(i)
+            if clock() - d0 >= budget_s / 4:
+                break
+        d1 = clock()
+        vo.block_heat(sub, qp, kp, L, w.softmax_scale, rows=rows)
+        d2 = clock()
+        t["dense_lse"], t["heat"] = d1 - d0, d2 - d1
+        spent += d2 - d0
+        total_tiles = n * H
+        layer_s["dense_lse"] = t["dense_lse"] * total_tiles / len(rows)
+        layer_s["heat"] = t["heat"] * total_tiles / len(rows)
+        heat_note = "; the dense LSE and the heat of %d query tiles of head 0, extrapolated by query tiles" % len(rows)
     layer_ms = 1e3 * sum(layer_s.values())
     return {"value": total_blocks * per_block / (layer_ms * 1e-3) / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": "fp64 numpy oracle, %.1f s on the host: front stages (permute Q/K/V, pool, project+score, "
                       "select) and the inverse permutation of heads 0..%d of %d, attention of %d query tiles "
                       "(%d blocks of %d in the layer; %d whole heads); each stage extrapolated to the layer "
-                      "(front stages by heads, attention by blocks)" % (spent, heads_front - 1, H, tiles_attn,
-                                                                        blocks_attn, total_blocks,
-                                                                        heads_attn_whole),
+                      "(front stages by heads, attention by blocks)%s" % (spent, heads_front - 1, H, tiles_attn,
+                                                                          blocks_attn, total_blocks,
+                                                                          heads_attn_whole, heat_note),
             "ms_per_layer_extrapolated": round(layer_ms, 1),
             "stage_ms_sample": {k: round(1e3 * v, 1) for k, v in t.items()},
             "stage_ms_per_layer_extrapolated": {k: round(1e3 * v, 1) for k, v in layer_s.items()},
