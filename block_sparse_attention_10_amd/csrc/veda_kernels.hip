@@ -1074,7 +1074,8 @@ __device__ __forceinline__ int half_pads(int nv, int hh) {
 //  HB and REST (rest_heat_kernel): the LSE-only pass over the rest of the
 //    dense row (the complement list); at the end of the row it joins its sum
 //    with the selected row's LSE into the dense LSE and writes the heat of
-//    every block of the dense row, the selected ones from their shares.
+//    every block of the dense row, the selected ones from the attention's
+//    block sums and factors.
 // So no block's QK^T product is computed twice.
 struct HeatSplit {
   const int32_t* srow;    // the selected CSR (REST)
